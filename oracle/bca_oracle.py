@@ -1,0 +1,270 @@
+"""Plain, slow, float64 CPU oracle of block-causal attention (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may import
+this module.  It materialises the visibility mask from its definition and runs dense softmax
+attention in float64; nothing here is blocked, fused or reordered beyond computing one (batch,
+head) pair and one chunk of query rows at a time.
+
+Sources (web pages, cited by title and section):
+
+* [QI21-guide] "Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo" (flozi.net
+  guide, English; the German edition has the same sections).  Sections used: "One stream for
+  text, reference images, and the target", "Block-causal attention is the cache-enabling
+  boundary", "Timestep-zero conditioning makes the prefix invariant", "The prefix cache is a
+  compute-for-memory trade", "Two exact attention paths, with different operating requirements".
+* [QI21-article] the 10100.com article on Qwen-Image 2.1 inference (Chinese): its Block-Causal
+  mask part (the rule written as a boolean expression), its piecewise-attention part (the
+  bottom-right aligned causal mask for a text segment whose Q length is shorter than its K
+  length) and its prefix-KV-cache part (prefill on step 1, mask-free decode afterwards).
+
+Parity pins (tests/test_oracle_pins.py): every function below is pinned by a check that does not
+reuse its own formula -- brute force of the rule as stated in words, the per-segment
+construction, the pages' worked 3x8 example, closed forms (Q = 0), reductions to
+``torch.nn.functional.scaled_dot_product_attention`` (unmasked, causal, piecewise segment calls),
+prefix invariance, decode == prefill rows, and the pages' cache-size figures.  No function here
+is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+TEXT = -1
+ROW_CHUNK = 1024  # query rows per dense block; bounds memory at S = 32,912
+
+
+class OracleInputError(ValueError):
+    """Raised for block-id vectors the rule does not define."""
+
+
+# ----------------------------------------------------------------------------------------------
+# Block ids and runs
+# ----------------------------------------------------------------------------------------------
+def validate_block_ids(ids: Sequence[int]) -> np.ndarray:
+    """Check a block-id vector: -1 for text, k >= 0 for image block k.
+
+    [QI21-guide, "Block-causal attention is the cache-enabling boundary"]: every position gets an
+    identifier, -1 for text, a unique non-negative identifier per reference image and another
+    one for the target; adjacent images keep distinct identifiers.  Reading: an image id must
+    occupy exactly one contiguous run (a reused id would let an earlier run see a later one, which
+    the same section rules out), so reuse is rejected rather than honoured.
+    """
+    a = np.asarray(ids)
+    if a.ndim != 1 or a.size < 1:
+        raise OracleInputError("block ids must be a non-empty 1-D vector")
+    a = a.astype(np.int64)
+    if (a < TEXT).any():
+        raise OracleInputError("block ids must be >= -1")
+    seen = set()
+    for start, end, bid in runs(a, _validated=True):
+        if bid >= 0:
+            if bid in seen:
+                raise OracleInputError(f"image block id {bid} occupies more than one run")
+            seen.add(bid)
+    return a
+
+
+def runs(ids: Sequence[int], _validated: bool = False) -> List[Tuple[int, int, int]]:
+    """Maximal runs of equal id as (start, end, id), end exclusive."""
+    a = np.asarray(ids).astype(np.int64)
+    out: List[Tuple[int, int, int]] = []
+    start = 0
+    for i in range(1, a.size + 1):
+        if i == a.size or a[i] != a[start]:
+            out.append((start, i, int(a[start])))
+            start = i
+    return out
+
+
+def prefix_split(ids: Sequence[int]) -> Tuple[int, int, bool]:
+    """(P, N, decode_ok): the prefix is everything before the last block.
+
+    [QI21-guide, "Timestep-zero conditioning makes the prefix invariant"]: the cache holds the
+    text and reference positions, i.e. everything before the target, which is the final block;
+    N target queries score P + N keys.  Cached decode needs that final block to be an image block
+    ([QI21-article], prefix-KV-cache part: the target is the last complete image block, so its rows
+    need no mask).
+    """
+    a = validate_block_ids(ids)
+    last = runs(a)[-1]
+    P = last[0]
+    return P, a.size - P, last[2] >= 0
+
+
+# ----------------------------------------------------------------------------------------------
+# The mask, from its definition
+# ----------------------------------------------------------------------------------------------
+def visibility_mask(ids: Sequence[int], rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """M[i, j] = (i >= j) or (i and j are in the same image block).
+
+    [QI21-article], Block-Causal mask part: visible = (query_position >= key_position) or
+    same_image_block.  Text is -1 and is strictly causal ([QI21-guide], "Block-causal attention
+    is the cache-enabling boundary"), so "same image block" requires a non-negative id.
+    Returns bool [len(rows), S] (all rows when ``rows`` is None).
+    """
+    a = validate_block_ids(ids)
+    S = a.size
+    r = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    i = r[:, None]
+    j = np.arange(S)[None, :]
+    same_image = (a[r][:, None] >= 0) & (a[r][:, None] == a[None, :])
+    return (i >= j) | same_image
+
+
+# ----------------------------------------------------------------------------------------------
+# Attention
+# ----------------------------------------------------------------------------------------------
+def _softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                       mask: Optional[np.ndarray]) -> np.ndarray:
+    """softmax(scale * q k^T, masked) v for one head, float64 throughout."""
+    s = (q @ k.T) * scale
+    if mask is not None:
+        if not mask.any(axis=1).all():
+            raise AssertionError("a query row with no visible key")
+        s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def default_scale(head_dim: int) -> float:
+    """Softmax scale when none is given: 1/sqrt(D), the default of the exact attention calls the
+    pages' default processor issues ([QI21-guide], "Two exact attention paths ...").  Reading:
+    the pages never state the scale."""
+    return 1.0 / np.sqrt(head_dim)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, ids: Sequence[int],
+              scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
+              batches: Optional[Sequence[int]] = None,
+              heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Block-causal prefill attention, float64, for [B, S, H, D] inputs.
+
+    For every (b, h): s = scale * Q K^T, s[i, j] = -inf where M[i, j] is False, row softmax,
+    O = p V ([QI21-guide], "Block-causal attention is the cache-enabling boundary").  Returns
+    float64 [len(batches), len(rows), len(heads), D]; callers round to float32 if they want the
+    stored precision.  ``rows``/``batches``/``heads`` select a subset (default: all).
+    """
+    a = validate_block_ids(ids)
+    B, S, H, D = q.shape
+    if a.size != S or k.shape != q.shape or v.shape != q.shape:
+        raise OracleInputError("shape mismatch")
+    sc = default_scale(D) if not scale else float(scale)
+    rsel = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    bsel = range(B) if batches is None else list(batches)
+    hsel = range(H) if heads is None else list(heads)
+    out = np.empty((len(bsel), rsel.size, len(hsel), D), dtype=np.float64)
+    for c0 in range(0, rsel.size, ROW_CHUNK):
+        rr = rsel[c0:c0 + ROW_CHUNK]
+        m = visibility_mask(a, rr)
+        for bi, b in enumerate(bsel):
+            for hi_, h in enumerate(hsel):
+                qq = q[b, rr, h, :].astype(np.float64)
+                kk = k[b, :, h, :].astype(np.float64)
+                vv = v[b, :, h, :].astype(np.float64)
+                out[bi, c0:c0 + rr.size, hi_, :] = _softmax_attention(qq, kk, vv, sc, m)
+    return out
+
+
+def prefix_cache(k: np.ndarray, v: np.ndarray, ids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """The per-layer prefix K/V: copies (not views) of positions [0, P).
+
+    [QI21-guide], "Timestep-zero conditioning makes the prefix invariant": the extract step stores
+    the prefix K/V and the implementation clones the prefix slices.
+    """
+    P, _, _ = prefix_split(ids)
+    return k[:, :P].copy(), v[:, :P].copy()
+
+
+def decode(q_t: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, k_t: np.ndarray,
+           v_t: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """Cached step: target queries attend, with no mask, to [cached prefix K/V ; target K/V].
+
+    [QI21-article], prefix-KV-cache part: Query = current target latents, Key/Value = cached
+    prefix K/V + current target K/V, one full attention with no mask; [QI21-guide], "Two exact
+    attention paths ...": target rows have full access to [cached prefix, target].
+    Returns float64 [B, N, H, D].
+    """
+    B, N, H, D = q_t.shape
+    P = k_cache.shape[1]
+    if k_t.shape != q_t.shape or v_t.shape != q_t.shape or v_cache.shape != k_cache.shape:
+        raise OracleInputError("shape mismatch")
+    if k_cache.shape[0] != B or k_cache.shape[2] != H or k_cache.shape[3] != D:
+        raise OracleInputError("cache shape mismatch")
+    sc = default_scale(D) if not scale else float(scale)
+    out = np.empty((B, N, H, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kk = np.concatenate([k_cache[b, :, h, :], k_t[b, :, h, :]]).astype(np.float64)
+            vv = np.concatenate([v_cache[b, :, h, :], v_t[b, :, h, :]]).astype(np.float64)
+            for c0 in range(0, N, ROW_CHUNK):
+                qq = q_t[b, c0:c0 + ROW_CHUNK, h, :].astype(np.float64)
+                out[b, c0:c0 + qq.shape[0], h, :] = _softmax_attention(qq, kk, vv, sc, None)
+    assert kk.shape[0] == P + N
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Plan derived from the mask
+# ----------------------------------------------------------------------------------------------
+def row_key_limits(ids: Sequence[int]) -> np.ndarray:
+    """hi[i] = 1 + (last visible key of row i), read off the materialised mask.
+
+    Also checks that every mask row is a prefix: M[i, :hi[i]] all True and M[i, hi[i]:] all
+    False.  (Not stated on the pages; it follows from the rule, and the check makes the mask's
+    shape explicit rather than assumed.)
+    """
+    a = validate_block_ids(ids)
+    S = a.size
+    hi = np.empty(S, dtype=np.int64)
+    for c0 in range(0, S, ROW_CHUNK):
+        rr = np.arange(c0, min(S, c0 + ROW_CHUNK))
+        m = visibility_mask(a, rr)
+        last = S - 1 - np.argmax(m[:, ::-1], axis=1)
+        hi[rr] = last + 1
+        prefix = np.arange(S)[None, :] < hi[rr][:, None]
+        if not np.array_equal(m, prefix):
+            raise AssertionError("a mask row is not a prefix of the keys")
+    return hi
+
+
+def plan_from_mask(ids: Sequence[int], block_m: int) -> Dict[str, np.ndarray]:
+    """Per-query-tile key ranges derived from the mask, for bit-exact comparison with a planner.
+
+    For query tile t (rows [t*block_m, min(S, (t+1)*block_m))): kv_full[t] = min hi over its
+    rows (every key below it is visible to every row of the tile), kv_end[t] = max hi (no row
+    sees a key at or beyond it).  ``order`` lists the tiles by kv_end descending, ties by tile
+    index ascending.  ``segments`` are the maximal equal-id runs (start, end, id).
+    """
+    a = validate_block_ids(ids)
+    S = a.size
+    hi = row_key_limits(a)
+    nt = -(-S // block_m)
+    kv_full = np.empty(nt, dtype=np.int64)
+    kv_end = np.empty(nt, dtype=np.int64)
+    for t in range(nt):
+        seg = hi[t * block_m:min(S, (t + 1) * block_m)]
+        kv_full[t] = seg.min()
+        kv_end[t] = seg.max()
+    order = np.array(sorted(range(nt), key=lambda t: (-kv_end[t], t)), dtype=np.int64)
+    P, N, ok = prefix_split(a)
+    return {
+        "segments": np.array(runs(a), dtype=np.int64).reshape(-1, 3),
+        "row_limit": hi,
+        "kv_full": kv_full,
+        "kv_end": kv_end,
+        "order": order,
+        "prefix_len": np.int64(P),
+        "target_len": np.int64(N),
+        "decode_ok": np.int64(1 if ok else 0),
+        "useful_pairs": np.int64(hi.sum()),
+    }
+
+
+def prefix_cache_bytes(layers: int, batch: int, prefix_len: int, heads: int, head_dim: int,
+                       bytes_per_scalar: int) -> int:
+    """Logical prefix-K/V payload: two tensors (K and V) of [batch, prefix, heads, head_dim] per
+    layer ([QI21-guide], "The prefix cache is a compute-for-memory trade")."""
+    return 2 * layers * batch * prefix_len * heads * head_dim * bytes_per_scalar
