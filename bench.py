@@ -1,0 +1,204 @@
+"""Benchmark of the block-causal attention hot path on one MI355X.
+
+A step is one pass of the whole path on the 2-reference 1024^2 edit shape:
+  * block-causal prefill of [t48][ref 4096][t40][ref 4096][t24][target 4096] (S = 12,400, B = 1,
+    H = 32, D = 128, bf16 in, fp32 out) that also writes the prefix K/V cache (P = 8,304), then
+  * one prefix-cached decode step under CFG (B = 2, N = 4,096 target queries over
+    8,304 + 4,096 keys, no mask) with fresh target Q/K/V (pre-generated, cycled).
+The plan is built once before timing (it serves all layers and steps).  Inputs are resident in
+HBM before the timed region.  Useful work = 4 * D flops per visible (query, key) pair.
+
+Prints ONE JSON line on stdout.  Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "useful attention TFLOP/s + ms/call (prefill, decode), fraction of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published figure
+HEAD_DIM = 128
+N_DECODE_SETS = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def cpu_baseline(W, lay, ids, P, N, budget_rows):
+    """Times the float64 CPU oracle on a bounded sample of the same workload: every query row of
+    (batch 0, head 0) of the prefill, and every target row of (batch 0, head 0) of one decode."""
+    from oracle import bca_oracle as O
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    S = lay.seq_len
+    q, k, v = W.qkv(W.SEEDS["edit_2ref"], 1, S, 1, scaled=True)
+    qf, kf, vf = (W.bf16_bits_to_f32(x) for x in (q, k, v))
+    rows = np.arange(min(S, budget_rows))
+    t0 = time.perf_counter()
+    O.attention(qf, kf, vf, ids, rows=rows)
+    t_pre = time.perf_counter() - t0
+    hi = O.row_key_limits(ids)
+    flops_pre = 4.0 * HEAD_DIM * float(hi[rows].sum())
+    t0 = time.perf_counter()
+    O.decode(qf[:, P:], kf[:, :P], vf[:, :P], kf[:, P:], vf[:, P:])
+    t_dec = time.perf_counter() - t0
+    flops_dec = 4.0 * HEAD_DIM * N * (P + N)
+    value = (flops_pre + flops_dec) / (t_pre + t_dec) / 1e12
+    return {
+        "value": value, "unit": "TFLOP/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+        "sample": (f"float64 NumPy oracle, batch 0 / head 0 only: {rows.size} prefill rows of the "
+                   f"S={S} block-causal layout ({t_pre:.2f} s) + all {N} target rows of one "
+                   f"cached decode over {P + N} keys ({t_dec:.2f} s); value = useful flops / time"),
+        "prefill_ms_per_head": t_pre * 1e3 * S / rows.size,
+        "decode_ms_per_head": t_dec * 1e3,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=12400,
+                    help="prefill rows in the CPU-oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path "
+              "is built and measured on a single MI355X; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bca_workloads as W
+    import block_causal_attention_amd as bca
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pre = W.EDIT_2REF
+    cfg = W.EDIT_2REF_CFG
+    ids = pre.block_ids()
+    S, H = pre.seq_len, pre.heads
+    t0 = time.perf_counter()
+    plan = bca.Plan(ids)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info
+    P, N = info.prefix_len, info.target_len
+    pairs = info.useful_pairs
+
+    # prefill inputs (B = 1) and its cache
+    qb, kb, vb = W.qkv(W.SEEDS["edit_2ref"], 1, S, H)
+    q, k, v = (to_dev(torch, x, dev) for x in (qb, kb, vb))
+    o = torch.empty((1, S, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    kc1 = torch.empty((1, P, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    vc1 = torch.empty_like(kc1)
+    # CFG pair (B = 2): prefix cache from a B = 2 prefill, then fresh target Q/K/V per step
+    Bd = cfg.batch
+    q2, k2, v2 = (to_dev(torch, x, dev) for x in W.qkv(W.SEEDS["edit_2ref_cfg"], Bd, S, H))
+    kc2 = torch.empty((Bd, P, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    vc2 = torch.empty_like(kc2)
+    o2 = torch.empty((Bd, S, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    bca.prefill(plan, q2, k2, v2, out=o2, k_cache=kc2, v_cache=vc2)
+    del q2, k2, v2, o2
+    sets = [tuple(to_dev(torch, x, dev) for x in W.decode_step_qkv(s + 1, Bd, N, H))
+            for s in range(N_DECODE_SETS)]
+    od = torch.empty((Bd, N, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup done: S={S} P={P} N={N} useful pairs/head={pairs} plan {plan_ms:.2f} ms")
+
+    flops_pre = 4.0 * HEAD_DIM * H * pairs
+    flops_dec = 4.0 * HEAD_DIM * Bd * H * N * (P + N)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        bca.prefill(plan, q, k, v, out=o, k_cache=kc1, v_cache=vc1)
+        if ev is not None:
+            ev[1].record()
+        qt, kt, vt = sets[i % N_DECODE_SETS]
+        bca.decode(plan, qt, kc2, vc2, kt, vt, out=od)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    pre_tf = flops_pre / (pre_ms.mean() * 1e-3) / 1e12
+    dec_tf = flops_dec / (dec_ms.mean() * 1e-3) / 1e12
+    value = (flops_pre + flops_dec) / (ms_step * 1e-3) / 1e12
+    log(f"prefill {pre_ms.mean():.3f} ms (median {np.median(pre_ms):.3f}) = {pre_tf:.1f} TFLOP/s; "
+        f"decode {dec_ms.mean():.3f} ms (median {np.median(dec_ms):.3f}) = {dec_tf:.1f} TFLOP/s")
+
+    # the dominant kernel: the call with the larger share of the step
+    if dec_ms.mean() >= pre_ms.mean():
+        dom, achieved = "decode (attn_fwd<true>)", dec_tf
+    else:
+        dom, achieved = "prefill (attn_fwd<false> + prefix-K/V copy)", pre_tf
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": dom}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(W, pre, ids, P, N, args.cpu_rows)
+        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s ({cpu['sample']})")
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(128) bf16 Q/K/V)",
+        "config": {
+            "workload": ("2-ref 1024^2 edit: block-causal prefill S=12400 (P=8304, N=4096) B=1 "
+                         "H=32 D=128 writing the prefix K/V cache, + one prefix-cached CFG decode "
+                         "step B=2 N=4096 over 12400 keys"),
+            "seq_len": S, "prefix_len": P, "target_len": N, "heads": H, "head_dim": HEAD_DIM,
+            "prefill_batch": 1, "decode_batch": Bd, "useful_pairs_per_head": int(pairs),
+        },
+        "prefill": {"ms": round(float(pre_ms.mean()), 4), "ms_median": round(float(np.median(pre_ms)), 4),
+                    "useful_tflops": round(pre_tf, 2), "frac_peak": round(pre_tf / PEAK_BF16_TFLOPS, 4),
+                    "useful_gflop": round(flops_pre / 1e9, 1)},
+        "decode": {"ms": round(float(dec_ms.mean()), 4), "ms_median": round(float(np.median(dec_ms)), 4),
+                   "useful_tflops": round(dec_tf, 2), "frac_peak": round(dec_tf / PEAK_BF16_TFLOPS, 4),
+                   "useful_gflop": round(flops_dec / 1e9, 1)},
+        "plan_ms": round(plan_ms, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    plan.free()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+"""Block-causal attention for AMD MI355X: thin Python binding over libbca.so.
+
+The binding only marshals arguments: every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.
+
+    plan = Plan(block_ids)                        # -1 text, k >= 0 image block k
+    o = prefill(plan, q, k, v, k_cache=kc, v_cache=vc)  # bf16 [B,S,H,128] -> fp32, fills cache
+    o_t = decode(plan, q_t, kc, vc, k_t, v_t)     # bf16 target [B,N,H,128] -> fp32
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import BcaPlanInfo, BcaTensor
+
+__all__ = ["Plan", "prefill", "decode", "BcaError", "plan_info"]
+
+
+class BcaError(RuntimeError):
+    """A non-OK status from libbca, with the library's error text."""
+
+    def __init__(self, status: int, msg: str):
+        self.status = status
+        lib = _lib.load()
+        name = lib.bca_status_str(status).decode()
+        super().__init__(f"{name}: {msg}")
+
+
+def _check(status: int) -> None:
+    if status != _lib.BCA_OK:
+        raise BcaError(status, _lib.load().bca_last_error().decode())
+
+
+class Plan:
+    """Launch plan built from a per-position block-id vector (see include/bca.h, bca_plan)."""
+
+    def __init__(self, block_ids, host_only: bool = False):
+        lib = _lib.load()
+        if hasattr(block_ids, "detach"):
+            block_ids = block_ids.detach().cpu().numpy()
+        ids = np.ascontiguousarray(np.asarray(block_ids, dtype=np.int64))
+        if ids.ndim != 1:
+            raise ValueError("block ids must be 1-D")
+        if ids.size and (ids.min() < -(2**31) or ids.max() >= 2**31):
+            raise BcaError(_lib.BCA_ERR_BLOCK_IDS, "block id out of int32 range")
+        ids32 = ids.astype(np.int32)
+        self._h = ctypes.c_void_p()
+        flags = _lib.BCA_PLAN_HOST_ONLY if host_only else 0
+        ptr = ids32.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if ids32.size else None
+        _check(lib.bca_plan(ptr, ids32.size, flags, ctypes.byref(self._h)))
+        self.info = plan_info(self)
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise ValueError("plan already freed")
+        return self._h
+
+    def export(self) -> Dict[str, np.ndarray]:
+        i = self.info
+        seg = np.empty(3 * i.n_segments, np.int32)
+        rl = np.empty(i.seq_len, np.int32)
+        kf = np.empty(i.n_qtiles, np.int32)
+        ke = np.empty(i.n_qtiles, np.int32)
+        od = np.empty(i.n_qtiles, np.int32)
+        p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        _check(_lib.load().bca_plan_export(self.handle, p(seg), p(rl), p(kf), p(ke), p(od)))
+        return {"segments": seg.reshape(-1, 3), "row_limit": rl, "kv_full": kf, "kv_end": ke,
+                "order": od}
+
+    def free(self) -> None:
+        if self._h:
+            _lib.load().bca_plan_free(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def plan_info(plan: Plan) -> BcaPlanInfo:
+    info = BcaPlanInfo()
+    _check(_lib.load().bca_plan_get_info(plan.handle, ctypes.byref(info)))
+    return info
+
+
+def _desc(t, name: str, dtype) -> BcaTensor:
+    """bca_tensor of a 4-D [B, S, H, D] torch tensor with D contiguous."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, S, H, D]")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    sb, ss, sh, sd = t.stride()
+    if sd != 1 and t.shape[3] > 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return BcaTensor(t.data_ptr(), sb, ss, sh)
+
+
+def _scale(scale: Optional[float]) -> float:
+    return 0.0 if scale is None else float(scale)
+
+
+def prefill(plan: Plan, q, k, v, *, scale: Optional[float] = None, out=None, k_cache=None,
+            v_cache=None):
+    """Block-causal prefill (bca_prefill).  Returns the fp32 output [B, S, H, D]."""
+    import torch
+
+    B, S, H, D = q.shape
+    if tuple(k.shape) != (B, S, H, D) or tuple(v.shape) != (B, S, H, D):
+        raise ValueError("q, k, v must share the shape [B, S, H, D]")
+    if S != plan.info.seq_len:
+        raise ValueError(f"sequence length {S} != plan's {plan.info.seq_len}")
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, S, H, D):
+        raise ValueError("out has the wrong shape")
+    P = plan.info.prefix_len
+    kc = vc = None
+    if (k_cache is None) != (v_cache is None):
+        raise ValueError("k_cache and v_cache go together")
+    if k_cache is not None:
+        for c in (k_cache, v_cache):
+            if tuple(c.shape) != (B, P, H, D):
+                raise ValueError(f"cache must be [B, P={P}, H, D]")
+        kc = ctypes.byref(_desc(k_cache, "k_cache", torch.bfloat16))
+        vc = ctypes.byref(_desc(v_cache, "v_cache", torch.bfloat16))
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_prefill(
+            plan.handle, B, H, D, _scale(scale),
+            ctypes.byref(_desc(q, "q", torch.bfloat16)), ctypes.byref(_desc(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc(v, "v", torch.bfloat16)), ctypes.byref(_desc(out, "out", torch.float32)),
+            kc, vc, ctypes.c_void_p(stream)))
+    return out
+
+
+def decode(plan: Plan, q, k_cache, v_cache, k, v, *, scale: Optional[float] = None, out=None):
+    """Prefix-cached decode (bca_decode).  q/k/v are the target's [B, N, H, D]; returns fp32."""
+    import torch
+
+    B, N, H, D = q.shape
+    P = plan.info.prefix_len
+    if N != plan.info.target_len:
+        raise ValueError(f"target length {N} != plan's {plan.info.target_len}")
+    checks = [("k", k, N), ("v", v, N)]
+    if P > 0 or k_cache is not None or v_cache is not None:
+        checks += [("k_cache", k_cache, P), ("v_cache", v_cache, P)]
+    for name, t, n in checks:
+        if t is None or tuple(t.shape) != (B, n, H, D):
+            raise ValueError(f"{name} must be [B, {n}, H, D]")
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, N, H, D):
+        raise ValueError("out has the wrong shape")
+    kc = ctypes.byref(_desc(k_cache, "k_cache", torch.bfloat16)) if P > 0 else None
+    vc = ctypes.byref(_desc(v_cache, "v_cache", torch.bfloat16)) if P > 0 else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_decode(
+            plan.handle, B, H, D, _scale(scale), ctypes.byref(_desc(q, "q", torch.bfloat16)),
+            kc, vc, ctypes.byref(_desc(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc(v, "v", torch.bfloat16)),
+            ctypes.byref(_desc(out, "out", torch.float32)), ctypes.c_void_p(stream)))
+    return out

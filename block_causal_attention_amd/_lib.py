@@ -1,0 +1,68 @@
+"""ctypes view of libbca.so (include/bca.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbca.so")
+
+BCA_OK = 0
+BCA_ERR_ARG = 1
+BCA_ERR_BLOCK_IDS = 2
+BCA_ERR_UNSUPPORTED = 3
+BCA_ERR_NO_DECODE = 4
+BCA_ERR_ALLOC = 5
+BCA_ERR_HIP = 6
+BCA_PLAN_HOST_ONLY = 1
+
+# every symbol include/bca.h declares
+EXPORTED = ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export", "bca_prefill",
+            "bca_decode", "bca_status_str", "bca_last_error")
+
+
+class BcaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class BcaPlanInfo(ctypes.Structure):
+    _fields_ = [("seq_len", ctypes.c_int64), ("prefix_len", ctypes.c_int64),
+                ("target_len", ctypes.c_int64), ("useful_pairs", ctypes.c_int64),
+                ("n_segments", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("block_n", ctypes.c_int32), ("n_qtiles", ctypes.c_int32),
+                ("decode_ok", ctypes.c_int32), ("host_only", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libbca.so not found at {LIB_PATH}: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    T = ctypes.POINTER(BcaTensor)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.bca_plan.argtypes = [i32p, ctypes.c_int64, ctypes.c_uint32, ctypes.POINTER(P)]
+    lib.bca_plan_free.argtypes = [P]
+    lib.bca_plan_get_info.argtypes = [P, ctypes.POINTER(BcaPlanInfo)]
+    lib.bca_plan_export.argtypes = [P, i32p, i32p, i32p, i32p, i32p]
+    lib.bca_prefill.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                T, T, T, T, T, T, P]
+    lib.bca_decode.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                               T, T, T, T, T, T, P]
+    lib.bca_status_str.argtypes = [ctypes.c_int]
+    lib.bca_status_str.restype = ctypes.c_char_p
+    lib.bca_last_error.argtypes = []
+    lib.bca_last_error.restype = ctypes.c_char_p
+    for name in ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export",
+                 "bca_prefill", "bca_decode"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib

@@ -1,0 +1,316 @@
+// C ABI of libbca (include/bca.h): argument validation, plan ownership, launches.
+// Every check runs on the host before anything is enqueued.
+#include "bca.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "bca_internal.h"
+#include "bca_plan.h"
+
+struct bca_plan_s {
+  bca::HostPlan host;
+  int32_t host_only = 1;
+  int device = -1;
+  int32_t* d_row_limit = nullptr;
+  int32_t* d_kv_full = nullptr;
+  int32_t* d_kv_end = nullptr;
+  int32_t* d_order = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bca_status fail(bca_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bca_status hip_fail(hipError_t e, const char* what) {
+  return fail(BCA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void free_device(bca_plan_s* p) {
+  int32_t** arrs[] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end, &p->d_order};
+  for (int32_t** a : arrs) {
+    if (*a) (void)hipFree(*a);
+    *a = nullptr;
+  }
+}
+
+bca_status upload(const std::vector<int32_t>& src, int32_t** dst) {
+  const size_t bytes = src.size() * sizeof(int32_t);
+  hipError_t e = hipMalloc((void**)dst, bytes);
+  if (e != hipSuccess) {
+    *dst = nullptr;
+    return fail(BCA_ERR_ALLOC, std::string("hipMalloc of plan array: ") + hipGetErrorString(e));
+  }
+  e = hipMemcpy(*dst, src.data(), bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy of plan array");
+  return BCA_OK;
+}
+
+// A tensor descriptor must point at 16-byte aligned memory with strides that keep every row
+// 16-byte aligned (8 bf16 or 4 fp32 elements).
+bca_status check_tensor(const bca_tensor* t, const char* name, int elem_bytes) {
+  if (t == nullptr) return fail(BCA_ERR_ARG, std::string(name) + ": descriptor is NULL");
+  if (t->data == nullptr) return fail(BCA_ERR_ARG, std::string(name) + ": data is NULL");
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(BCA_ERR_ARG, std::string(name) + ": data is not 16-byte aligned");
+  const int64_t q = 16 / elem_bytes;
+  const int64_t st[3] = {t->stride_b, t->stride_s, t->stride_h};
+  for (int64_t s : st)
+    if (s < 0 || s % q != 0)
+      return fail(BCA_ERR_ARG, std::string(name) + ": strides must be non-negative multiples of " +
+                                   std::to_string(q) + " elements");
+  return BCA_OK;
+}
+
+// Size, head width and scale checks; they need no device, so they run first.
+bca_status check_common(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                        float* scale_log2) {
+  if (plan == nullptr) return fail(BCA_ERR_ARG, "plan is NULL");
+  if (B < 1 || H < 1) return fail(BCA_ERR_ARG, "B and H must be >= 1");
+  if (D != bca::kHeadDim)
+    return fail(BCA_ERR_UNSUPPORTED, "head width " + std::to_string(D) + " (only 128 is built)");
+  if (std::isnan(scale) || scale < 0.0f || std::isinf(scale))
+    return fail(BCA_ERR_ARG, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  const double sc = scale == 0.0f ? 1.0 / std::sqrt((double)D) : (double)scale;
+  *scale_log2 = (float)(sc * 1.4426950408889634);  // log2(e)
+  return BCA_OK;
+}
+
+// The plan must own device arrays on the current device.
+bca_status check_launchable(bca_plan_t plan) {
+  if (plan->host_only) return fail(BCA_ERR_ARG, "plan was built with BCA_PLAN_HOST_ONLY");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(BCA_ERR_ARG, "plan lives on device " + std::to_string(plan->device) +
+                                 " but device " + std::to_string(dev) + " is current");
+  return BCA_OK;
+}
+
+bool grid_fits(int64_t tiles, int32_t B, int32_t H) {
+  return tiles * (int64_t)B * (int64_t)H <= (int64_t)INT32_MAX;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bca_status_str(bca_status s) {
+  switch (s) {
+    case BCA_OK: return "BCA_OK";
+    case BCA_ERR_ARG: return "BCA_ERR_ARG";
+    case BCA_ERR_BLOCK_IDS: return "BCA_ERR_BLOCK_IDS";
+    case BCA_ERR_UNSUPPORTED: return "BCA_ERR_UNSUPPORTED";
+    case BCA_ERR_NO_DECODE: return "BCA_ERR_NO_DECODE";
+    case BCA_ERR_ALLOC: return "BCA_ERR_ALLOC";
+    case BCA_ERR_HIP: return "BCA_ERR_HIP";
+  }
+  return "unknown status";
+}
+
+const char* bca_last_error(void) { return g_last_error.c_str(); }
+
+bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, bca_plan_t* out) {
+  if (out == nullptr) return fail(BCA_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (flags & ~(uint32_t)BCA_PLAN_HOST_ONLY) return fail(BCA_ERR_ARG, "unknown plan flags");
+  bca_plan_s* p = new (std::nothrow) bca_plan_s();
+  if (p == nullptr) return fail(BCA_ERR_ALLOC, "host allocation of the plan failed");
+  std::string err;
+  int rc;
+  try {
+    rc = bca::build_host_plan(block_ids, seq_len, bca::kBlockM, &p->host, &err);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(BCA_ERR_ALLOC, "host allocation of the plan failed");
+  }
+  if (rc != bca::kPlanOk) {
+    delete p;
+    return fail(rc == bca::kPlanErrBlockIds ? BCA_ERR_BLOCK_IDS : BCA_ERR_ARG, err);
+  }
+  p->host_only = (flags & BCA_PLAN_HOST_ONLY) ? 1 : 0;
+  if (!p->host_only) {
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "hipGetDevice");
+    }
+    bca_status s = BCA_OK;
+    if (s == BCA_OK) s = upload(p->host.row_limit, &p->d_row_limit);
+    if (s == BCA_OK) s = upload(p->host.kv_full, &p->d_kv_full);
+    if (s == BCA_OK) s = upload(p->host.kv_end, &p->d_kv_end);
+    if (s == BCA_OK) s = upload(p->host.order, &p->d_order);
+    if (s != BCA_OK) {
+      free_device(p);
+      delete p;
+      return s;
+    }
+  }
+  *out = p;
+  return BCA_OK;
+}
+
+bca_status bca_plan_free(bca_plan_t plan) {
+  if (plan == nullptr) return BCA_OK;
+  free_device(plan);
+  delete plan;
+  return BCA_OK;
+}
+
+bca_status bca_plan_get_info(bca_plan_t plan, bca_plan_info* out) {
+  if (plan == nullptr || out == nullptr) return fail(BCA_ERR_ARG, "plan or out is NULL");
+  const bca::HostPlan& h = plan->host;
+  out->seq_len = h.seq_len;
+  out->prefix_len = h.prefix_len;
+  out->target_len = h.target_len;
+  out->useful_pairs = h.useful_pairs;
+  out->n_segments = (int32_t)(h.segments.size() / 3);
+  out->block_m = bca::kBlockM;
+  out->block_n = bca::kBlockN;
+  out->n_qtiles = (int32_t)h.kv_end.size();
+  out->decode_ok = h.decode_ok;
+  out->host_only = plan->host_only;
+  return BCA_OK;
+}
+
+bca_status bca_plan_export(bca_plan_t plan, int32_t* segments, int32_t* row_limit,
+                           int32_t* kv_full, int32_t* kv_end, int32_t* order) {
+  if (plan == nullptr) return fail(BCA_ERR_ARG, "plan is NULL");
+  const bca::HostPlan& h = plan->host;
+  auto put = [](int32_t* dst, const std::vector<int32_t>& v) {
+    if (dst) std::memcpy(dst, v.data(), v.size() * sizeof(int32_t));
+  };
+  put(segments, h.segments);
+  put(row_limit, h.row_limit);
+  put(kv_full, h.kv_full);
+  put(kv_end, h.kv_end);
+  put(order, h.order);
+  return BCA_OK;
+}
+
+bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                       const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
+                       const bca_tensor* o, const bca_tensor* k_cache, const bca_tensor* v_cache,
+                       void* stream) {
+  float scale_log2 = 0.0f;
+  bca_status s = check_common(plan, B, H, D, scale, &scale_log2);
+  if (s != BCA_OK) return s;
+  if ((s = check_tensor(q, "q", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(k, "k", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(v, "v", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(o, "o", 4)) != BCA_OK) return s;
+  const bool want_cache = k_cache != nullptr || v_cache != nullptr;
+  const bca::HostPlan& hp = plan->host;
+  if (want_cache) {
+    if (k_cache == nullptr || v_cache == nullptr)
+      return fail(BCA_ERR_ARG, "k_cache and v_cache must both be given or both be NULL");
+    if (hp.prefix_len > 0) {
+      if ((s = check_tensor(k_cache, "k_cache", 2)) != BCA_OK) return s;
+      if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
+    }
+  }
+  const int64_t nt = (int64_t)hp.kv_end.size();
+  if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles exceeds 2^31 - 1");
+  if ((s = check_launchable(plan)) != BCA_OK) return s;
+
+  bca::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.q_sb = q->stride_b; a.q_ss = q->stride_s; a.q_sh = q->stride_h;
+  a.k = static_cast<const uint16_t*>(k->data);
+  a.k_sb = k->stride_b; a.k_ss = k->stride_s; a.k_sh = k->stride_h;
+  a.v = static_cast<const uint16_t*>(v->data);
+  a.v_sb = v->stride_b; a.v_ss = v->stride_s; a.v_sh = v->stride_h;
+  a.k2 = a.k; a.k2_sb = a.k_sb; a.k2_ss = a.k_ss; a.k2_sh = a.k_sh;
+  a.v2 = a.v; a.v2_sb = a.v_sb; a.v2_ss = a.v_ss; a.v2_sh = a.v_sh;
+  a.o = static_cast<float*>(o->data);
+  a.o_sb = o->stride_b; a.o_ss = o->stride_s; a.o_sh = o->stride_h;
+  a.n_q = (int32_t)hp.seq_len;
+  a.kv_len = (int32_t)hp.seq_len;
+  a.split = (int32_t)hp.seq_len;
+  a.heads = H;
+  a.batch = B;
+  a.n_qtiles = (int32_t)nt;
+  a.scale_log2 = scale_log2;
+  a.row_limit = plan->d_row_limit;
+  a.kv_full = plan->d_kv_full;
+  a.kv_end = plan->d_kv_end;
+  a.order = plan->d_order;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = bca::launch_prefill(a, st);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  if (want_cache && hp.prefix_len > 0) {
+    bca::CopyArgs kc{a.k, k->stride_b, k->stride_s, k->stride_h,
+                     static_cast<uint16_t*>(k_cache->data), k_cache->stride_b, k_cache->stride_s,
+                     k_cache->stride_h, (int32_t)hp.prefix_len, H, B};
+    bca::CopyArgs vc{a.v, v->stride_b, v->stride_s, v->stride_h,
+                     static_cast<uint16_t*>(v_cache->data), v_cache->stride_b, v_cache->stride_s,
+                     v_cache->stride_h, (int32_t)hp.prefix_len, H, B};
+    e = bca::launch_prefix_copy(kc, vc, st);
+    if (e != hipSuccess) return hip_fail(e, "prefix copy launch");
+  }
+  return BCA_OK;
+}
+
+bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                      const bca_tensor* q_tgt, const bca_tensor* k_cache,
+                      const bca_tensor* v_cache, const bca_tensor* k_tgt,
+                      const bca_tensor* v_tgt, const bca_tensor* o, void* stream) {
+  float scale_log2 = 0.0f;
+  bca_status s = check_common(plan, B, H, D, scale, &scale_log2);
+  if (s != BCA_OK) return s;
+  const bca::HostPlan& hp = plan->host;
+  if (!hp.decode_ok)
+    return fail(BCA_ERR_NO_DECODE, "the layout's last block is text; cached decode needs the "
+                                   "target image block last");
+  if ((s = check_tensor(q_tgt, "q_tgt", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(k_tgt, "k_tgt", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(v_tgt, "v_tgt", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(o, "o", 4)) != BCA_OK) return s;
+  if (hp.prefix_len > 0) {
+    if ((s = check_tensor(k_cache, "k_cache", 2)) != BCA_OK) return s;
+    if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
+  }
+  const int64_t N = hp.target_len;
+  const int64_t nt = (N + bca::kBlockM - 1) / bca::kBlockM;
+  if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles exceeds 2^31 - 1");
+  if ((s = check_launchable(plan)) != BCA_OK) return s;
+
+  bca::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q_tgt->data);
+  a.q_sb = q_tgt->stride_b; a.q_ss = q_tgt->stride_s; a.q_sh = q_tgt->stride_h;
+  a.k2 = static_cast<const uint16_t*>(k_tgt->data);
+  a.k2_sb = k_tgt->stride_b; a.k2_ss = k_tgt->stride_s; a.k2_sh = k_tgt->stride_h;
+  a.v2 = static_cast<const uint16_t*>(v_tgt->data);
+  a.v2_sb = v_tgt->stride_b; a.v2_ss = v_tgt->stride_s; a.v2_sh = v_tgt->stride_h;
+  if (hp.prefix_len > 0) {
+    a.k = static_cast<const uint16_t*>(k_cache->data);
+    a.k_sb = k_cache->stride_b; a.k_ss = k_cache->stride_s; a.k_sh = k_cache->stride_h;
+    a.v = static_cast<const uint16_t*>(v_cache->data);
+    a.v_sb = v_cache->stride_b; a.v_ss = v_cache->stride_s; a.v_sh = v_cache->stride_h;
+  } else {  // no prefix: every key comes from the target
+    a.k = a.k2; a.k_sb = a.k2_sb; a.k_ss = a.k2_ss; a.k_sh = a.k2_sh;
+    a.v = a.v2; a.v_sb = a.v2_sb; a.v_ss = a.v2_ss; a.v_sh = a.v2_sh;
+  }
+  a.o = static_cast<float*>(o->data);
+  a.o_sb = o->stride_b; a.o_ss = o->stride_s; a.o_sh = o->stride_h;
+  a.n_q = (int32_t)N;
+  a.kv_len = (int32_t)(hp.prefix_len + N);
+  a.split = (int32_t)hp.prefix_len;
+  a.heads = H;
+  a.batch = B;
+  a.n_qtiles = (int32_t)nt;
+  a.scale_log2 = scale_log2;
+  hipError_t e = bca::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return BCA_OK;
+}
+
+}  // extern "C"

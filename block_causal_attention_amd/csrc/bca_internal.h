@@ -1,0 +1,58 @@
+// Internal interface between the host side of libbca (planner, validation) and the gfx950
+// kernels.  Not installed; the public ABI is include/bca.h.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace bca {
+
+constexpr int kHeadDim = 128;  // the only head width the kernels are built for
+constexpr int kBlockM = 128;   // query rows per workgroup (4 waves x 32 rows)
+constexpr int kBlockN = 64;    // keys per key tile
+
+// One attention launch.  Prefill and decode share the kernel: keys j < split come from (k, v),
+// keys j >= split from (k2, v2) at index j - split.  Prefill sets split = kv_len.
+struct AttnArgs {
+  const uint16_t* q;
+  int64_t q_sb, q_ss, q_sh;
+  const uint16_t* k;
+  int64_t k_sb, k_ss, k_sh;
+  const uint16_t* v;
+  int64_t v_sb, v_ss, v_sh;
+  const uint16_t* k2;
+  int64_t k2_sb, k2_ss, k2_sh;
+  const uint16_t* v2;
+  int64_t v2_sb, v2_ss, v2_sh;
+  float* o;
+  int64_t o_sb, o_ss, o_sh;
+  int32_t n_q;       // query rows per (batch, head): S for prefill, N for decode
+  int32_t kv_len;    // keys per (batch, head): S for prefill, P + N for decode
+  int32_t split;     // first key taken from the second source
+  int32_t heads;
+  int32_t batch;
+  int32_t n_qtiles;  // ceil(n_q / kBlockM)
+  float scale_log2;  // softmax scale * log2(e)
+  // Prefill only (NULL for decode): per-row key limit and per-tile ranges / order.
+  const int32_t* row_limit;
+  const int32_t* kv_full;
+  const int32_t* kv_end;
+  const int32_t* order;
+};
+
+struct CopyArgs {
+  const uint16_t* src;
+  int64_t s_sb, s_ss, s_sh;
+  uint16_t* dst;
+  int64_t d_sb, d_ss, d_sh;
+  int32_t rows;  // positions [0, rows) are copied
+  int32_t heads;
+  int32_t batch;
+};
+
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_prefix_copy(const CopyArgs& k, const CopyArgs& v, hipStream_t stream);
+
+}  // namespace bca

@@ -1,0 +1,89 @@
+// Segment planner: block ids -> per-row key limits and per-query-tile key ranges.
+// Pure C++ (no HIP), so it can also be built and sanitised on a machine without a GPU.
+//
+// The rule ("Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo", section
+// "Block-causal attention is the cache-enabling boundary") lets a text row see every key at or
+// before it and an image row see every key before its block plus its whole block.  So each mask
+// row is a prefix [0, hi(i)) of the keys: hi(i) = i + 1 on text (the bottom-right aligned causal
+// triangle of the 10100.com article's piecewise-attention part) and hi(i) = end of the block on
+// image rows.  hi never decreases along the sequence, so a tile's smallest limit is its first
+// row's and its largest is its last row's; the O(S^2) mask is never built.
+#include "bca_plan.h"
+
+#include <algorithm>
+#include <numeric>
+#include <unordered_set>
+
+namespace bca {
+
+int build_host_plan(const int32_t* ids, int64_t S, int block_m, HostPlan* out, std::string* err) {
+  if (ids == nullptr) {
+    *err = "block_ids is NULL";
+    return kPlanErrArg;
+  }
+  if (S < 1 || S > INT32_MAX) {
+    *err = "seq_len must be in [1, 2^31 - 1], got " + std::to_string(S);
+    return kPlanErrArg;
+  }
+  if (block_m < 1) {
+    *err = "block_m must be positive";
+    return kPlanErrArg;
+  }
+  HostPlan p;
+  p.seq_len = S;
+  // maximal runs of equal id
+  std::unordered_set<int32_t> seen;
+  int64_t start = 0;
+  for (int64_t i = 0; i <= S; ++i) {
+    if (i < S && ids[i] < -1) {
+      *err = "block id " + std::to_string(ids[i]) + " at position " + std::to_string(i) +
+             " is below -1";
+      return kPlanErrBlockIds;
+    }
+    if (i == S || ids[i] != ids[start]) {
+      const int32_t id = ids[start];
+      if (id >= 0 && !seen.insert(id).second) {
+        *err = "image block id " + std::to_string(id) + " occupies more than one run (again at " +
+               std::to_string(start) + ")";
+        return kPlanErrBlockIds;
+      }
+      p.segments.push_back((int32_t)start);
+      p.segments.push_back((int32_t)i);
+      p.segments.push_back(id);
+      start = i;
+    }
+  }
+  // per-row key limits
+  p.row_limit.resize((size_t)S);
+  const size_t nseg = p.segments.size() / 3;
+  for (size_t r = 0; r < nseg; ++r) {
+    const int32_t a = p.segments[3 * r], e = p.segments[3 * r + 1], id = p.segments[3 * r + 2];
+    for (int32_t i = a; i < e; ++i) p.row_limit[(size_t)i] = id < 0 ? i + 1 : e;
+  }
+  p.useful_pairs = 0;
+  for (int32_t x : p.row_limit) p.useful_pairs += x;
+  // per query tile: first row's limit is the minimum, last row's the maximum
+  const int64_t nt = (S + block_m - 1) / block_m;
+  p.kv_full.resize((size_t)nt);
+  p.kv_end.resize((size_t)nt);
+  for (int64_t t = 0; t < nt; ++t) {
+    const int64_t first = t * block_m;
+    const int64_t last = std::min<int64_t>(S, first + block_m) - 1;
+    p.kv_full[(size_t)t] = p.row_limit[(size_t)first];
+    p.kv_end[(size_t)t] = p.row_limit[(size_t)last];
+  }
+  // heavy-first: kv_end descending, ties by tile index ascending
+  p.order.resize((size_t)nt);
+  std::iota(p.order.begin(), p.order.end(), 0);
+  std::stable_sort(p.order.begin(), p.order.end(),
+                   [&](int32_t x, int32_t y) { return p.kv_end[(size_t)x] > p.kv_end[(size_t)y]; });
+  // prefix = everything before the last block; decode needs that block to be an image
+  p.prefix_len = p.segments[3 * (nseg - 1)];
+  p.target_len = S - p.prefix_len;
+  p.decode_ok = p.segments[3 * (nseg - 1) + 2] >= 0 ? 1 : 0;
+  p.block_m = block_m;
+  *out = std::move(p);
+  return kPlanOk;
+}
+
+}  // namespace bca

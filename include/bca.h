@@ -1,0 +1,157 @@
+/*
+ * bca.h -- C ABI of the block-causal attention library (libbca.so) for AMD MI355X (gfx950).
+ *
+ * What it computes.  One layer's attention of a single-stream diffusion transformer whose
+ * sequence is [text][reference-image latents]...[target latents].  Position i may attend to key
+ * j exactly when i >= j or when i and j lie in the same image block: text is strictly causal,
+ * every image block is bidirectional inside, and blocks are causal in sequence order
+ * ("Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo", section "Block-causal
+ * attention is the cache-enabling boundary"; the 10100.com Qwen-Image 2.1 article, Block-Causal
+ * mask part, which writes the rule as (query_position >= key_position) or same_image_block).
+ *
+ * Shapes.  Multi-head attention (not GQA) with H heads of width D = 128; Q, K and V are
+ * [B, S, H, D] bf16 with D contiguous (same guide, section "One stream for text, reference
+ * images, and the target").  Outputs are fp32.
+ *
+ * Conventions for every call below.
+ *  - All functions return a bca_status.  On failure nothing has been enqueued and
+ *    bca_last_error() returns a description (thread-local, valid until the next failing call on
+ *    the same thread).
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  bca_prefill and bca_decode never
+ *    allocate and never synchronise; they enqueue on `stream` (a hipStream_t; NULL = the
+ *    default stream) and return.
+ *  - bca_tensor strides are in elements; the D stride is 1.  data must be 16-byte aligned;
+ *    stride_b, stride_s and stride_h must be non-negative multiples of 8 (bf16) or 4 (fp32).
+ *  - scale is the softmax multiplier of q.k; 0 selects 1/sqrt(D).  Negative or NaN -> ARG.
+ */
+#ifndef BCA_H
+#define BCA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bca_status {
+  BCA_OK = 0,
+  BCA_ERR_ARG = 1,         /* bad size, pointer, stride, alignment, scale, or host-only plan */
+  BCA_ERR_BLOCK_IDS = 2,   /* an id < -1, or an image id that occupies more than one run */
+  BCA_ERR_UNSUPPORTED = 3, /* head width other than 128 */
+  BCA_ERR_NO_DECODE = 4,   /* decode asked for a layout whose last block is text */
+  BCA_ERR_ALLOC = 5,       /* host or device allocation failed (bca_plan only) */
+  BCA_ERR_HIP = 6          /* a HIP call or kernel launch failed; text has hipGetErrorString */
+} bca_status;
+
+/* Opaque, immutable once built.  Independent of B and H: one plan serves every layer, every
+ * denoising step, every stream and thread.  Free it only when no launch using it is in flight. */
+typedef struct bca_plan_s* bca_plan_t;
+
+typedef struct bca_tensor {
+  void* data;       /* device pointer to element [0, 0, 0, 0] */
+  int64_t stride_b; /* elements between consecutive batch entries */
+  int64_t stride_s; /* elements between consecutive sequence positions */
+  int64_t stride_h; /* elements between consecutive heads */
+} bca_tensor;
+
+typedef struct bca_plan_info {
+  int64_t seq_len;      /* S */
+  int64_t prefix_len;   /* P: start of the last block (text + reference positions before it) */
+  int64_t target_len;   /* N = S - P */
+  int64_t useful_pairs; /* number of visible (query, key) pairs per (batch, head) = sum of hi(i) */
+  int32_t n_segments;   /* maximal runs of equal block id */
+  int32_t block_m;      /* query rows per prefill tile */
+  int32_t block_n;      /* keys per key tile */
+  int32_t n_qtiles;     /* ceil(S / block_m) */
+  int32_t decode_ok;    /* 1 when the last block is an image block (the target) */
+  int32_t host_only;    /* 1 when built with BCA_PLAN_HOST_ONLY (no device arrays) */
+} bca_plan_info;
+
+enum { BCA_PLAN_HOST_ONLY = 1u };
+
+/*
+ * bca_plan -- turn a per-position block-id vector into the launch plan.
+ *
+ * block_ids: HOST array [seq_len]; -1 marks text, k >= 0 marks image block k (same guide,
+ * section "Block-causal attention is the cache-enabling boundary": -1 for text, a unique
+ * non-negative id per reference image and another for the target; adjacent images keep distinct
+ * ids).  Ids need not be increasing; an id >= 0 must form exactly one contiguous run (reuse is
+ * rejected: BCA_ERR_BLOCK_IDS).  seq_len >= 1 and < 2^31.
+ *
+ * The plan holds, for every row i, its key limit hi(i): row i sees exactly the keys [0, hi(i)),
+ * with hi(i) = i + 1 for text and the end of its block for image rows.  For text this is the
+ * bottom-right aligned causal triangle of a segment whose query count is below its key count
+ * (10100.com article, piecewise-attention part: mask = ones(q_len, kv_len).tril(kv_len - q_len)).
+ * Per query tile t of block_m rows it stores kv_full[t] (min hi: key tiles below it need no mask)
+ * and kv_end[t] (max hi: key tiles at or past it are skipped), and a heavy-first tile order.
+ *
+ * flags: 0, or BCA_PLAN_HOST_ONLY to skip the device upload (such a plan can be inspected but
+ * not launched).  Without it, the plan owns small int32 device arrays on the current device
+ * (hipMalloc + synchronous hipMemcpy, the only allocations in this library).
+ * *out receives the plan; release it with bca_plan_free.
+ */
+bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, bca_plan_t* out);
+
+/* Releases a plan (host and device arrays).  NULL is accepted and ignored. */
+bca_status bca_plan_free(bca_plan_t plan);
+
+/* Fills *out with the plan's scalars. */
+bca_status bca_plan_get_info(bca_plan_t plan, bca_plan_info* out);
+
+/*
+ * Copies the plan's arrays to HOST buffers (any pointer may be NULL to skip it):
+ *   segments [n_segments * 3]  (start, end exclusive, id) per maximal run
+ *   row_limit [seq_len]        hi(i)
+ *   kv_full, kv_end, order [n_qtiles]
+ */
+bca_status bca_plan_export(bca_plan_t plan, int32_t* segments, int32_t* row_limit,
+                           int32_t* kv_full, int32_t* kv_end, int32_t* order);
+
+/*
+ * bca_prefill -- block-causal attention over the whole joint sequence (the first denoising step,
+ * "extract" in the guide's section "Timestep-zero conditioning makes the prefix invariant"),
+ * optionally storing the per-layer prefix K/V cache.
+ *
+ *   o[b, i, h, :] = sum_{j < hi(i)} softmax_j(scale * q[b,i,h,:] . k[b,j,h,:]) v[b,j,h,:]
+ *
+ * q, k, v: bf16 [B, S, H, D] (S = the plan's seq_len).  o: fp32 [B, S, H, D], fully written.
+ * k_cache, v_cache: bf16 [B, P, H, D] with P = the plan's prefix_len, or both NULL.  When given,
+ * they receive copies of k[:, :P] and v[:, :P] (the guide clones the prefix slices rather than
+ * keeping views).  The cache holds K as handed in (post-RoPE when the caller applied RoPE).
+ * Output buffers must not overlap the inputs.  D must be 128 (else BCA_ERR_UNSUPPORTED).
+ */
+bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                       const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
+                       const bca_tensor* o, const bca_tensor* k_cache, const bca_tensor* v_cache,
+                       void* stream);
+
+/*
+ * bca_decode -- a cached denoising step: the N target queries attend with no mask to the
+ * concatenation [cached prefix K/V ; current target K/V] (10100.com article, prefix-KV-cache
+ * part: Query = current target latents, Key/Value = cached prefix K/V + current target K/V, one
+ * full attention; guide, section "Two exact attention paths, with different operating
+ * requirements").
+ *
+ *   o[b, n, h, :] = sum_{j < P + N} softmax_j(scale * q_tgt[b,n,h,:] . kk[b,j,h,:]) vv[b,j,h,:]
+ *   with kk[j] = k_cache[j] for j < P and k_tgt[j - P] otherwise (same for vv).
+ *
+ * q_tgt, k_tgt, v_tgt: bf16 [B, N, H, D]; k_cache, v_cache: bf16 [B, P, H, D] (P, N from the
+ * plan); o: fp32 [B, N, H, D].  The plan's last block must be an image block
+ * (else BCA_ERR_NO_DECODE).  D must be 128.
+ */
+bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                      const bca_tensor* q_tgt, const bca_tensor* k_cache,
+                      const bca_tensor* v_cache, const bca_tensor* k_tgt,
+                      const bca_tensor* v_tgt, const bca_tensor* o, void* stream);
+
+/* Static name of a status code ("BCA_OK", ...); "unknown status" for other values. */
+const char* bca_status_str(bca_status status);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* bca_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BCA_H */

@@ -179,13 +179,15 @@ def prefix_cache(k: np.ndarray, v: np.ndarray, ids: Sequence[int]) -> Tuple[np.n
 
 
 def decode(q_t: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, k_t: np.ndarray,
-           v_t: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+           v_t: np.ndarray, scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
+           batches: Optional[Sequence[int]] = None,
+           heads: Optional[Sequence[int]] = None) -> np.ndarray:
     """Cached step: target queries attend, with no mask, to [cached prefix K/V ; target K/V].
 
     [QI21-article], prefix-KV-cache part: Query = current target latents, Key/Value = cached
     prefix K/V + current target K/V, one full attention with no mask; [QI21-guide], "Two exact
     attention paths ...": target rows have full access to [cached prefix, target].
-    Returns float64 [B, N, H, D].
+    Returns float64 [len(batches), len(rows), len(heads), D] (default: all of them).
     """
     B, N, H, D = q_t.shape
     P = k_cache.shape[1]
@@ -194,15 +196,19 @@ def decode(q_t: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, k_t: np.nd
     if k_cache.shape[0] != B or k_cache.shape[2] != H or k_cache.shape[3] != D:
         raise OracleInputError("cache shape mismatch")
     sc = default_scale(D) if not scale else float(scale)
-    out = np.empty((B, N, H, D), dtype=np.float64)
-    for b in range(B):
-        for h in range(H):
+    rsel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    bsel = range(B) if batches is None else list(batches)
+    hsel = range(H) if heads is None else list(heads)
+    out = np.empty((len(bsel), rsel.size, len(hsel), D), dtype=np.float64)
+    for bi, b in enumerate(bsel):
+        for hi_, h in enumerate(hsel):
             kk = np.concatenate([k_cache[b, :, h, :], k_t[b, :, h, :]]).astype(np.float64)
             vv = np.concatenate([v_cache[b, :, h, :], v_t[b, :, h, :]]).astype(np.float64)
-            for c0 in range(0, N, ROW_CHUNK):
-                qq = q_t[b, c0:c0 + ROW_CHUNK, h, :].astype(np.float64)
-                out[b, c0:c0 + qq.shape[0], h, :] = _softmax_attention(qq, kk, vv, sc, None)
-    assert kk.shape[0] == P + N
+            assert kk.shape[0] == P + N
+            for c0 in range(0, rsel.size, ROW_CHUNK):
+                rr = rsel[c0:c0 + ROW_CHUNK]
+                qq = q_t[b, rr, h, :].astype(np.float64)
+                out[bi, c0:c0 + rr.size, hi_, :] = _softmax_attention(qq, kk, vv, sc, None)
     return out
 
 

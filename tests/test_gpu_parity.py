@@ -1,0 +1,299 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerance on fp32 outputs from bf16 inputs: max |err| <= 1e-2 and mean |err| <= 1e-3.  Because
+that tolerance alone does not separate a correct mask from an off-by-one at the scaled input
+distribution (logits ~ 1e-2 make attention nearly uniform), the suite adds:
+  * the "sharp" distribution (no 1/sqrt(128) factor) under the same tolerance;
+  * an exact counting probe (Q = 0, V = segment indicators and key-index bits), checked to 2 ulp
+    against a closed form at full sizes;
+  * a leak probe: keys a row cannot see are overwritten and the row must not change by one bit;
+  * decode vs prefill target rows, cache bit-equality, run-to-run bit-equality, strided inputs.
+"""
+import numpy as np
+import pytest
+
+import bca_workloads as W
+from oracle import bca_oracle as O
+
+torch = pytest.importorskip("torch")
+bca = pytest.importorskip("block_causal_attention_amd")
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL = 1e-2, 1e-3
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def f32(bits):
+    return W.bf16_bits_to_f32(bits)
+
+
+def check(got, ref, what):
+    err = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    say(f"  {what}: max|err|={err.max():.3e} mean|err|={err.mean():.3e} n={err.size}")
+    assert np.isfinite(got).all(), what
+    assert err.max() <= MAX_TOL and err.mean() <= MEAN_TOL, what
+
+
+def hi_closed_form(ids):
+    ids = np.asarray(ids)
+    out = np.arange(1, len(ids) + 1, dtype=np.int64)
+    for a, e, bid in O.runs(ids):
+        if bid >= 0:
+            out[a:e] = e
+    return out
+
+
+def run_prefill(ids, qb, kb, vb, cache=False):
+    plan = bca.Plan(ids)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    B, S, H, D = q.shape
+    P = plan.info.prefix_len
+    kc = vc = None
+    if cache:
+        kc = torch.full((B, P, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+        vc = torch.full_like(kc, float("nan"))
+    o = bca.prefill(plan, q, k, v, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    return plan, o, kc, vc
+
+
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("scaled", [True, False])
+def test_tiny_prefill_decode_cache(scaled):
+    lay = W.TINY
+    ids = lay.block_ids()
+    say(f"case: tiny prefill+decode scaled={scaled}")
+    qb, kb, vb = W.qkv(W.SEEDS["tiny"], lay.batch, lay.seq_len, lay.heads, scaled)
+    plan, o, kc, vc = run_prefill(ids, qb, kb, vb, cache=True)
+    ref = O.attention(f32(qb), f32(kb), f32(vb), ids)
+    check(o.cpu().numpy(), ref, "prefill")
+    P = plan.info.prefix_len
+    assert torch.equal(kc.cpu().view(torch.int16), torch.from_numpy(kb[:, :P].view(np.int16)))
+    assert torch.equal(vc.cpu().view(torch.int16), torch.from_numpy(vb[:, :P].view(np.int16)))
+    od = bca.decode(plan, to_dev(qb[:, P:]), kc, vc, to_dev(kb[:, P:]), to_dev(vb[:, P:]))
+    torch.cuda.synchronize()
+    check(od.cpu().numpy(), ref[:, P:], "decode vs oracle prefill rows")
+    refd = O.decode(f32(qb[:, P:]), f32(kb[:, :P]), f32(vb[:, :P]), f32(kb[:, P:]), f32(vb[:, P:]))
+    check(od.cpu().numpy(), refd, "decode vs oracle decode")
+
+
+RANDOM_CASES = [(31, 1, 1, 2), (32, 7, 2, 2), (33, 64, 2, 2), (34, 65, 1, 3), (35, 127, 2, 2),
+                (36, 129, 2, 2), (37, 300, 2, 2), (38, 777, 1, 2), (39, 1500, 1, 2),
+                (40, 2100, 1, 1)]
+
+
+@pytest.mark.parametrize("seed,S,B,H", RANDOM_CASES)
+def test_random_layouts_full(seed, S, B, H):
+    rng = np.random.default_rng(seed)
+    ids = W.random_layout(rng, S, p_text=0.5, max_seg=max(1, S // 3))
+    say(f"case: random layout seed={seed} S={S} B={B} H={H} runs={len(O.runs(ids))}")
+    qb, kb, vb = W.qkv(seed, B, S, H, scaled=False)
+    plan, o, kc, vc = run_prefill(ids, qb, kb, vb, cache=True)
+    ref = O.attention(f32(qb), f32(kb), f32(vb), ids)
+    check(o.cpu().numpy(), ref, "prefill (sharp)")
+    P = plan.info.prefix_len
+    if P > 0:
+        assert torch.equal(kc.cpu().view(torch.int16), torch.from_numpy(kb[:, :P].view(np.int16)))
+    if plan.info.decode_ok:
+        od = bca.decode(plan, to_dev(qb[:, P:]), kc if P else None, vc if P else None,
+                        to_dev(kb[:, P:]), to_dev(vb[:, P:]))
+        torch.cuda.synchronize()
+        check(od.cpu().numpy(), ref[:, P:], "decode")
+
+
+def test_single_image_block_decode_without_prefix():
+    S, B, H = 200, 2, 2
+    ids = np.zeros(S, np.int32)
+    say("case: single image block, P = 0")
+    qb, kb, vb = W.qkv(77, B, S, H, scaled=False)
+    plan, o, _, _ = run_prefill(ids, qb, kb, vb)
+    assert plan.info.prefix_len == 0
+    ref = O.attention(f32(qb), f32(kb), f32(vb), ids)
+    check(o.cpu().numpy(), ref, "prefill")
+    empty = torch.empty((B, 0, H, 128), dtype=torch.bfloat16, device=DEV)
+    od = bca.decode(plan, to_dev(qb), empty, empty, to_dev(kb), to_dev(vb))
+    torch.cuda.synchronize()
+    check(od.cpu().numpy(), ref, "decode")
+
+
+# ---------------------------------------------------------------------------------------------
+def count_probe_inputs(ids, B, H):
+    """Q = 0; V[j, c] = 1 if key j lies in run c; V[j, 64 + b] = bit b of j."""
+    S = len(ids)
+    segs = O.runs(ids)
+    assert len(segs) <= 64 and S < 2 ** 16
+    v = np.zeros((S, 128), np.float32)
+    for c, (a, e, _) in enumerate(segs):
+        v[a:e, c] = 1.0
+    j = np.arange(S)
+    for bit in range(16):
+        v[:, 64 + bit] = (j >> bit) & 1
+    vb = np.broadcast_to(W.f32_to_bf16_bits(v)[None, :, None, :], (B, S, H, 128)).copy()
+    qb = np.zeros((B, S, H, 128), np.uint16)
+    kb = W.qkv(5, B, S, H, scaled=False)[1]
+    return qb, kb, vb, v
+
+
+def count_probe_expected(ids, v):
+    """Closed form: each output column is (number of visible keys with V = 1) / hi(i)."""
+    hi = hi_closed_form(ids)
+    cum = np.concatenate([np.zeros((1, 128)), np.cumsum(v.astype(np.float64), axis=0)])
+    return cum[hi] / hi[:, None]
+
+
+@pytest.mark.parametrize("name,H", [("tiny", 2), ("t2i_1024", 4), ("edit_2ref", 32),
+                                    ("long_4ref", 2)])
+def test_count_probe_exact(name, H):
+    lay = W.WORKLOADS[name]
+    ids = lay.block_ids()
+    say(f"case: count probe {name} S={lay.seq_len} H={H}")
+    qb, kb, vb, v = count_probe_inputs(ids, 1, H)
+    plan, o, _, _ = run_prefill(ids, qb, kb, vb)
+    want = count_probe_expected(ids, v)
+    got = o.cpu().numpy()[0]  # [S, H, D]
+    tol = 2 * np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    for h in range(H):
+        bad = np.abs(got[:, h, :] - want) > tol
+        assert not bad.any(), (name, h, np.argwhere(bad)[:5])
+    if plan.info.decode_ok:
+        P = plan.info.prefix_len
+        to = lambda a: to_dev(np.ascontiguousarray(a))
+        od = bca.decode(plan, to(qb[:, P:]), to(kb[:, :P]), to(vb[:, :P]), to(kb[:, P:]),
+                        to(vb[:, P:]))
+        torch.cuda.synchronize()
+        wd = v.astype(np.float64).mean(axis=0)
+        gd = od.cpu().numpy()[0]
+        assert (np.abs(gd - wd) <= 2 * np.spacing(np.abs(wd).astype(np.float32))).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "edit_2ref"])
+def test_leak_probe_bitwise(name):
+    """Overwrite every key/value a row range cannot see; those rows must not change at all."""
+    lay = W.WORKLOADS[name]
+    ids = lay.block_ids()
+    H = min(lay.heads, 8)
+    S = lay.seq_len
+    say(f"case: leak probe {name} S={S} H={H}")
+    qb, kb, vb = W.qkv(W.SEEDS[name] + 100, 1, S, H, scaled=False)
+    _, o1, _, _ = run_prefill(ids, qb, kb, vb)
+    hi = hi_closed_form(ids)
+    for a, e, bid in O.runs(ids)[:-1]:
+        bound = int(hi[e - 1])  # no row of [0, e) sees a key at or past this
+        k2, v2 = kb.copy(), vb.copy()
+        rng = np.random.default_rng(a)
+        k2[:, bound:] = W.f32_to_bf16_bits(30 * rng.standard_normal(k2[:, bound:].shape,
+                                                                     dtype=np.float32))
+        v2[:, bound:] = W.f32_to_bf16_bits(30 * rng.standard_normal(v2[:, bound:].shape,
+                                                                     dtype=np.float32))
+        _, o2, _, _ = run_prefill(ids, qb, k2, v2)
+        assert torch.equal(o1[:, :e], o2[:, :e]), (name, a, e)
+        assert not torch.equal(o1[:, e:], o2[:, e:])
+        if name == "edit_2ref" and e > 5000:
+            break
+
+
+# ---------------------------------------------------------------------------------------------
+def sample_rows(ids, every=97):
+    S = len(ids)
+    rows = set(range(0, S, every))
+    for a, e, _ in O.runs(ids):
+        for r in (a - 2, a - 1, a, a + 1, e - 2, e - 1):
+            if 0 <= r < S:
+                rows.add(r)
+    rows.add(S - 1)
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["t2i_1024", "edit_2ref", "long_4ref"])
+@pytest.mark.parametrize("scaled", [True, False])
+def test_full_size_sampled_rows(name, scaled):
+    lay = W.WORKLOADS[name]
+    ids = lay.block_ids()
+    B, S, H = lay.batch, lay.seq_len, lay.heads
+    say(f"case: full-size prefill {name} S={S} H={H} scaled={scaled}")
+    qb, kb, vb = W.qkv(W.SEEDS[name], B, S, H, scaled)
+    plan, o, kc, vc = run_prefill(ids, qb, kb, vb, cache=True)
+    P = plan.info.prefix_len
+    assert torch.equal(kc.view(torch.int16).cpu(), torch.from_numpy(kb[:, :P].view(np.int16)))
+    assert torch.equal(vc.view(torch.int16).cpu(), torch.from_numpy(vb[:, :P].view(np.int16)))
+    rows = sample_rows(ids, every=211 if S > 20000 else 97)
+    heads = [0, 13, H - 1]
+    got = o[:, torch.from_numpy(rows).to(DEV)][:, :, heads].cpu().numpy()
+    ref = O.attention(f32(qb[:, :, heads]), f32(kb[:, :, heads]), f32(vb[:, :, heads]), ids,
+                      rows=rows)
+    check(got, ref, f"{len(rows)} rows x {len(heads)} heads")
+
+
+@pytest.mark.parametrize("scaled", [True, False])
+def test_cfg_decode_full_size(scaled):
+    """B = 2 (cond/uncond) prefill writes both caches; a cached step with fresh target Q/K/V
+    is checked against the oracle's decode, and against the GPU prefill's target rows."""
+    lay = W.EDIT_2REF_CFG
+    ids = lay.block_ids()
+    B, S, H = lay.batch, lay.seq_len, lay.heads
+    say(f"case: CFG decode B={B} S={S} scaled={scaled}")
+    qb, kb, vb = W.qkv(W.SEEDS["edit_2ref_cfg"], B, S, H, scaled)
+    plan, o, kc, vc = run_prefill(ids, qb, kb, vb, cache=True)
+    P, N = plan.info.prefix_len, plan.info.target_len
+    assert (P, N) == (8304, 4096)
+    assert torch.equal(kc.view(torch.int16).cpu(), torch.from_numpy(kb[:, :P].view(np.int16)))
+    # decode over the prefill's own target rows == prefill's target rows (within tolerance)
+    od0 = bca.decode(plan, to_dev(qb[:, P:]), kc, vc, to_dev(kb[:, P:]), to_dev(vb[:, P:]))
+    torch.cuda.synchronize()
+    check(od0.cpu().numpy(), o[:, P:].cpu().numpy(), "decode vs GPU prefill target rows")
+    # a fresh cached step
+    qt, kt, vt = W.decode_step_qkv(1, B, N, H, scaled=scaled)
+    od = bca.decode(plan, to_dev(qt), kc, vc, to_dev(kt), to_dev(vt))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, N, 61), [N - 1]]))
+    heads = [1, 30]
+    got = od[:, torch.from_numpy(rows).to(DEV)][:, :, heads].cpu().numpy()
+    ref = O.decode(f32(qt[:, :, heads]), f32(kb[:, :P][:, :, heads]), f32(vb[:, :P][:, :, heads]),
+                   f32(kt[:, :, heads]), f32(vt[:, :, heads]), rows=rows)
+    check(got, ref, "fresh-step decode vs oracle")
+
+
+def test_run_to_run_bitwise():
+    lay = W.EDIT_2REF
+    ids = lay.block_ids()
+    say("case: determinism edit_2ref")
+    qb, kb, vb = W.qkv(9, 1, lay.seq_len, lay.heads, scaled=False)
+    plan, o1, kc, vc = run_prefill(ids, qb, kb, vb, cache=True)
+    _, o2, _, _ = run_prefill(ids, qb, kb, vb)
+    assert torch.equal(o1, o2)
+    P = plan.info.prefix_len
+    args = (plan, to_dev(qb[:, P:]), kc, vc, to_dev(kb[:, P:]), to_dev(vb[:, P:]))
+    d1 = bca.decode(*args)
+    d2 = bca.decode(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2)
+
+
+def test_strided_inputs_and_side_stream():
+    """Q/K/V as views of one packed [B, S, 3, H, D] tensor, output into a strided view, on a
+    non-default stream: bit-identical to contiguous inputs on the default stream."""
+    rng = np.random.default_rng(3)
+    S, B, H = 333, 2, 3
+    ids = W.random_layout(rng, S, max_seg=80)
+    qb, kb, vb = W.qkv(3, B, S, H, scaled=False)
+    say("case: strided inputs")
+    plan, o_ref, _, _ = run_prefill(ids, qb, kb, vb)
+    packed = torch.stack([to_dev(qb), to_dev(kb), to_dev(vb)], dim=2)  # [B, S, 3, H, D]
+    q, k, v = packed[:, :, 0], packed[:, :, 1], packed[:, :, 2]
+    big = torch.zeros((B, S, H + 1, 128), dtype=torch.float32, device=DEV)
+    out = big[:, :, 1:]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        bca.prefill(plan, q, k, v, out=out)
+    s.synchronize()
+    assert torch.equal(out, o_ref)
+    assert torch.count_nonzero(big[:, :, 0]) == 0

@@ -1,0 +1,158 @@
+"""CPU tests of the C-ABI library: symbols, planner parity with the oracle, argument validation.
+
+No compute call runs here: plans are host-only and every launch is expected to be rejected by a
+host-side check before anything touches a GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bca_workloads as W
+from oracle import bca_oracle as O
+
+bca = pytest.importorskip("block_causal_attention_amd")
+from block_causal_attention_amd import _lib  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "bca.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bca_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def plan_host(ids):
+    return bca.Plan(np.asarray(ids), host_only=True)
+
+
+def assert_plan_matches_oracle(ids):
+    p = plan_host(ids)
+    info = p.info
+    got = p.export()
+    want = O.plan_from_mask(ids, info.block_m)
+    for key in ("segments", "row_limit", "kv_full", "kv_end", "order"):
+        assert np.array_equal(got[key].astype(np.int64), want[key]), key
+    assert info.prefix_len == want["prefix_len"]
+    assert info.target_len == want["target_len"]
+    assert info.decode_ok == want["decode_ok"]
+    assert info.useful_pairs == want["useful_pairs"]
+    assert info.seq_len == len(ids) and info.host_only == 1
+    assert info.n_qtiles == -(-len(ids) // info.block_m)
+    p.free()
+
+
+@pytest.mark.parametrize("name", ["tiny", "t2i_1024", "edit_2ref", "long_4ref"])
+def test_plan_bit_exact_on_workloads(name):
+    assert_plan_matches_oracle(W.WORKLOADS[name].block_ids())
+
+
+def test_plan_bit_exact_fuzz():
+    rng = np.random.default_rng(21)
+    cases = [np.array([-1]), np.array([0]), np.full(300, -1), np.zeros(300, np.int32),
+             W.block_ids_from_segments([("image", 128), ("image", 1), ("text", 127)]),
+             W.block_ids_from_segments([("text", 1), ("image", 255), ("text", 1), ("image", 2)])]
+    for _ in range(40):
+        S = int(rng.integers(1, 700))
+        cases.append(W.random_layout(rng, S, p_text=float(rng.random()),
+                                     max_seg=int(rng.integers(1, 300))))
+    for ids in cases:
+        assert_plan_matches_oracle(ids)
+
+
+def test_plan_sizes_of_workloads():
+    """Sequence lengths, prefix lengths and visible pairs of the five workloads."""
+    expect = {"tiny": (146, 82, 14763), "t2i_1024": (4352, 256, 17858688),
+              "edit_2ref": (12400, 8304, 102045880), "long_4ref": (32912, 16528, 709372104)}
+    for name, (S, P, pairs) in expect.items():
+        info = plan_host(W.WORKLOADS[name].block_ids()).info
+        assert (info.seq_len, info.prefix_len, info.useful_pairs) == (S, P, pairs)
+        assert info.decode_ok == 1
+
+
+def status_of(fn):
+    with pytest.raises(bca.BcaError) as e:
+        fn()
+    return e.value.status
+
+
+def test_plan_rejects_bad_ids():
+    assert status_of(lambda: plan_host([-1, -2, 0])) == _lib.BCA_ERR_BLOCK_IDS
+    assert status_of(lambda: plan_host([0, 0, -1, 0])) == _lib.BCA_ERR_BLOCK_IDS
+    assert status_of(lambda: plan_host([1, 1, 1, 2, 1])) == _lib.BCA_ERR_BLOCK_IDS
+    assert status_of(lambda: plan_host([])) == _lib.BCA_ERR_ARG
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    assert lib.bca_plan(None, 4, 1, ctypes.byref(h)) == _lib.BCA_ERR_ARG
+    ids = (ctypes.c_int32 * 2)(-1, 0)
+    assert lib.bca_plan(ids, 2, 0x10, ctypes.byref(h)) == _lib.BCA_ERR_ARG
+    assert lib.bca_plan(ids, 2, 1, None) == _lib.BCA_ERR_ARG
+    assert b"out" in lib.bca_last_error()
+    assert lib.bca_plan_free(None) == _lib.BCA_OK
+
+
+def _t(ptr=0x10000, sb=8 * 4096, ss=4096, sh=128):
+    return _lib.BcaTensor(ptr, sb, ss, sh)
+
+
+def call_prefill(plan, B=1, H=2, D=128, scale=0.0, q=None, k=None, v=None, o=None, kc=None,
+                 vc=None):
+    lib = _lib.load()
+    r = lambda t: None if t is None else ctypes.byref(t)
+    return lib.bca_prefill(plan, B, H, D, scale, r(q or _t()), r(k or _t()), r(v or _t()),
+                           r(o or _t()), r(kc), r(vc), None)
+
+
+def call_decode(plan, B=1, H=2, D=128, scale=0.0, q=None, kc=None, vc=None, k=None, v=None, o=None):
+    lib = _lib.load()
+    r = lambda t: None if t is None else ctypes.byref(t)
+    return lib.bca_decode(plan, B, H, D, scale, r(q or _t()), r(kc or _t()), r(vc or _t()),
+                          r(k or _t()), r(v or _t()), r(o or _t()), None)
+
+
+def test_launch_validation_before_any_device_work():
+    p = plan_host(W.TINY.block_ids())
+    h = p.handle
+    lib = _lib.load()
+    assert call_prefill(None) == _lib.BCA_ERR_ARG
+    assert call_prefill(h, B=0) == _lib.BCA_ERR_ARG
+    assert call_prefill(h, H=0) == _lib.BCA_ERR_ARG
+    assert call_prefill(h, D=64) == _lib.BCA_ERR_UNSUPPORTED
+    assert call_prefill(h, scale=float("nan")) == _lib.BCA_ERR_ARG
+    assert call_prefill(h, scale=-1.0) == _lib.BCA_ERR_ARG
+    assert call_prefill(h, q=_t(ptr=0x10008)) == _lib.BCA_ERR_ARG          # misaligned
+    assert call_prefill(h, k=_t(ss=4100)) == _lib.BCA_ERR_ARG              # stride not x8
+    assert call_prefill(h, o=_t(sh=130)) == _lib.BCA_ERR_ARG               # fp32 stride not x4
+    assert call_prefill(h, o=_t(sh=132)) == _lib.BCA_ERR_ARG               # host-only plan
+    assert b"HOST_ONLY" in lib.bca_last_error()
+    assert call_prefill(h, v=_t(ptr=0)) == _lib.BCA_ERR_ARG                # NULL data
+    assert call_prefill(h, kc=_t()) == _lib.BCA_ERR_ARG                    # half a cache
+    assert call_prefill(h) == _lib.BCA_ERR_ARG                             # host-only plan
+    assert call_decode(h, D=256) == _lib.BCA_ERR_UNSUPPORTED
+    assert call_decode(h, o=_t(ptr=0x10004)) == _lib.BCA_ERR_ARG
+    assert call_decode(h) == _lib.BCA_ERR_ARG                              # host-only plan
+    text_last = plan_host([-1, 0, 0, -1])
+    assert text_last.info.decode_ok == 0
+    assert call_decode(text_last.handle) == _lib.BCA_ERR_NO_DECODE
+    assert lib.bca_status_str(4) == b"BCA_ERR_NO_DECODE"
+    assert lib.bca_status_str(99) == b"unknown status"
+
+
+def test_python_shim_rejects_bad_shapes_without_gpu():
+    torch = pytest.importorskip("torch")
+    p = plan_host(W.TINY.block_ids())
+    x = torch.zeros((1, 10, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bca.prefill(p, x, x, x)  # S != plan's S
