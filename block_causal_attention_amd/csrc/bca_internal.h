@@ -8,9 +8,18 @@
 
 namespace bca {
 
+// Tile shape.  A wave owns kQueryBlocks blocks of 32 query rows; a workgroup has kWaves waves.
+#ifndef BCA_QUERY_BLOCKS
+#define BCA_QUERY_BLOCKS 1
+#endif
+#ifndef BCA_WAVES
+#define BCA_WAVES 4
+#endif
 constexpr int kHeadDim = 128;  // the only head width the kernels are built for
-constexpr int kBlockM = 128;   // query rows per workgroup (4 waves x 32 rows)
-constexpr int kBlockN = 64;    // keys per key tile
+constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
+constexpr int kWaves = BCA_WAVES;
+constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup (= plan tile)
+constexpr int kBlockN = 64;                          // keys per key tile
 
 // One attention launch.  Prefill and decode share the kernel: keys j < split come from (k, v),
 // keys j >= split from (k2, v2) at index j - split.  Prefill sets split = kv_len.
