@@ -79,7 +79,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=12400,
                     help="prefill rows in the CPU-oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "read_bytes": n, "write_bytes": n}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path "
               "is built and measured on a single MI355X; see the sharding notes in DESIGN.md)",

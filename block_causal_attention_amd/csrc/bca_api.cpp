@@ -243,19 +243,15 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   a.kv_full = plan->d_kv_full;
   a.kv_end = plan->d_kv_end;
   a.order = plan->d_order;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = bca::launch_prefill(a, st);
-  if (e != hipSuccess) return hip_fail(e, "prefill launch");
   if (want_cache && hp.prefix_len > 0) {
-    bca::CopyArgs kc{a.k, k->stride_b, k->stride_s, k->stride_h,
-                     static_cast<uint16_t*>(k_cache->data), k_cache->stride_b, k_cache->stride_s,
-                     k_cache->stride_h, (int32_t)hp.prefix_len, H, B};
-    bca::CopyArgs vc{a.v, v->stride_b, v->stride_s, v->stride_h,
-                     static_cast<uint16_t*>(v_cache->data), v_cache->stride_b, v_cache->stride_s,
-                     v_cache->stride_h, (int32_t)hp.prefix_len, H, B};
-    e = bca::launch_prefix_copy(kc, vc, st);
-    if (e != hipSuccess) return hip_fail(e, "prefix copy launch");
+    a.kc = static_cast<uint16_t*>(k_cache->data);
+    a.kc_sb = k_cache->stride_b; a.kc_ss = k_cache->stride_s; a.kc_sh = k_cache->stride_h;
+    a.vc = static_cast<uint16_t*>(v_cache->data);
+    a.vc_sb = v_cache->stride_b; a.vc_ss = v_cache->stride_s; a.vc_sh = v_cache->stride_h;
+    a.cache_len = (int32_t)hp.prefix_len;
   }
+  hipError_t e = bca::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return BCA_OK;
 }
 

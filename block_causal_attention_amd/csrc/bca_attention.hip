@@ -1,5 +1,5 @@
 // Block-causal flash attention for gfx950 (MI355X): prefill (plan-driven) and prefix-cached
-// decode (mask-free over [cache ; target]), plus the prefix-K/V copy.
+// decode (mask-free over [cache ; target]); the prefill also writes the prefix-K/V cache.
 //
 // The rule ("Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo", section
 // "Block-causal attention is the cache-enabling boundary") makes every mask row a prefix of the
@@ -9,7 +9,7 @@
 // row limit, and never loads the rest.  Decode is the same kernel with no mask except the tail.
 //
 // Work decomposition.  One workgroup = kWaves waves = one tile of kBlockM query rows of one
-// (batch, head); a wave owns kQueryBlocks blocks of 32 rows.  Per key tile of 64 keys:
+// (batch, head); a wave owns kQueryBlocks blocks of 32 rows.  Per key tile of kBlockN keys:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q rows held in VGPRs.
 //                 The accumulator gives each lane ONE query (lane % 32) and 16 keys, so the row
 //                 max is an in-lane reduction plus one swap of the two 32-lane halves.
@@ -45,7 +45,10 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kOccupancy = BCA_WAVES_PER_SIMD;
 constexpr int kKStride = kHeadDim + 8;   // bf16 per LDS K row: 272 B, rows 4 banks apart
-constexpr int kVStride = kHeadDim + 16;  // bf16 per LDS V row: 288 B, rows 8 banks apart
+#ifndef BCA_V_PAD
+#define BCA_V_PAD 16
+#endif
+constexpr int kVStride = kHeadDim + BCA_V_PAD;  // bf16 per LDS V row
 constexpr int kChunks = kBlockN * kHeadDim / 8;  // 16-byte chunks per K (or V) tile
 constexpr int kChunksPerThread = kChunks / kThreads;
 constexpr int kRowsPerPass = kThreads / 16;      // tile rows covered by one pass of the group
@@ -53,11 +56,15 @@ constexpr float kRescaleThreshold = 8.0f;        // log2 units
 // With one 32-row block per wave, the next tile's scores are computed while this tile's softmax
 // runs (K one tile ahead of V).  With two blocks there are not enough registers for a second
 // score tile, and the tiles run one after the other through a plain double buffer.
+#ifndef BCA_SCHED_INTERLEAVE
+#define BCA_SCHED_INTERLEAVE 0
+#endif
 #ifndef BCA_SCORES_AHEAD
 #define BCA_SCORES_AHEAD (kQueryBlocks == 1)
 #endif
 constexpr bool kScoresAhead = BCA_SCORES_AHEAD;
-static_assert(kBlockN == 64, "two 32-key MFMA blocks per key tile");
+constexpr int kKeyBlocks = kBlockN / 32;  // 32-key MFMA blocks per key tile
+static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
 static_assert(kChunks % kThreads == 0, "whole 16-byte chunks per thread");
 
 // Reduce across the two 32-lane halves of the wave: after v_permlane32_swap(x, x) every lane
@@ -173,23 +180,41 @@ void attn_fwd(const AttnArgs a) {
   auto load_v = [&](int n0, u32x4 (&st)[kChunksPerThread]) {
     load_tile(n0, st, v_base, a.v_ss, v_row_off, v2_base, a.v2_ss, v2_row_off);
   };
-  auto store_k = [&](int buf, const u32x4 (&st)[kChunksPerThread]) {
+  // Prefix-K/V cache (prefill only): this workgroup owns cache rows [cache_lo, cache_hi), which
+  // lie inside its own diagonal key tiles, so they are stored from the staging registers as
+  // those tiles pass through; no K/V row is read twice for the cache.
+  const int cache_lo = tile * kBlockM;
+  const int cache_hi = kDecode || a.kc == nullptr ? 0 : min(cache_lo + kBlockM, a.cache_len);
+  auto store_cache = [&](int n0, const u32x4 (&st)[kChunksPerThread], uint16_t* base,
+                         int64_t sb, int64_t ss, int64_t sh) {
+    if (kDecode || n0 >= cache_hi || n0 + kBlockN <= cache_lo) return;
+    uint16_t* p = base + b * sb + h * sh + ld_col;
+#pragma unroll
+    for (int r = 0; r < kChunksPerThread; ++r) {
+      const int key = n0 + ld_row + kRowsPerPass * r;
+      if (key >= cache_lo && key < cache_hi)
+        *reinterpret_cast<u32x4*>(p + (int64_t)key * ss) = st[r];
+    }
+  };
+  auto store_k = [&](int buf, int n0, const u32x4 (&st)[kChunksPerThread]) {
 #pragma unroll
     for (int r = 0; r < kChunksPerThread; ++r)
       *reinterpret_cast<u32x4*>(&k_lds[buf][(ld_row + kRowsPerPass * r) * kKStride + ld_col]) =
           st[r];
+    store_cache(n0, st, a.kc, a.kc_sb, a.kc_ss, a.kc_sh);
   };
-  auto store_v = [&](int buf, const u32x4 (&st)[kChunksPerThread]) {
+  auto store_v = [&](int buf, int n0, const u32x4 (&st)[kChunksPerThread]) {
 #pragma unroll
     for (int r = 0; r < kChunksPerThread; ++r)
       *reinterpret_cast<u32x4*>(&v_lds[buf][(ld_row + kRowsPerPass * r) * kVStride + ld_col]) =
           st[r];
+    store_cache(n0, st, a.vc, a.vc_sb, a.vc_ss, a.vc_sh);
   };
 
-  // ---- S^T = K Q^T for the two 32-key blocks of the K tile in buffer buf ------------------
-  auto scores = [&](int buf, f32x16 (&s)[kQueryBlocks][2]) {
+  // ---- S^T = K Q^T for the 32-key blocks of the K tile in buffer buf ------------------
+  auto scores = [&](int buf, f32x16 (&s)[kQueryBlocks][kKeyBlocks]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kKeyBlocks; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < kQueryBlocks; ++qb) s[qb][kb] = f32x16{};
 #pragma unroll
@@ -225,16 +250,16 @@ void attn_fwd(const AttnArgs a) {
 
   // ---- prologue --------------------------------------------------------------------------
   u32x4 kst[kChunksPerThread], vst[kChunksPerThread];
-  f32x16 s_cur[kQueryBlocks][2];
+  f32x16 s_cur[kQueryBlocks][kKeyBlocks];
   if constexpr (kScoresAhead) {
     // K(0), V(0), K(1) into LDS; K(2) and V(1) in flight; scores of tile 0
     load_k(0, kst);
     load_v(0, vst);
-    store_k(0, kst);
-    store_v(0, vst);
+    store_k(0, 0, kst);
+    store_v(0, 0, vst);
     if (ntiles > 1) {
       load_k(kBlockN, kst);
-      store_k(1, kst);
+      store_k(1, kBlockN, kst);
     }
     if (ntiles > 2) load_k(2 * kBlockN, kst);
     if (ntiles > 1) load_v(kBlockN, vst);
@@ -245,8 +270,8 @@ void attn_fwd(const AttnArgs a) {
     // tile 0 into LDS buffer 0; tile 1 in flight
     load_k(0, kst);
     load_v(0, vst);
-    store_k(0, kst);
-    store_v(0, vst);
+    store_k(0, 0, kst);
+    store_v(0, 0, vst);
     if (ntiles > 1) {
       load_k(kBlockN, kst);
       load_v(kBlockN, vst);
@@ -265,7 +290,7 @@ void attn_fwd(const AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < kQueryBlocks; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -280,7 +305,7 @@ void attn_fwd(const AttnArgs a) {
     for (int qb = 0; qb < kQueryBlocks; ++qb) {
       float mx = s_cur[qb][0][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[qb][kb][i]);
       mx = halves_max(mx);
@@ -297,17 +322,17 @@ void attn_fwd(const AttnArgs a) {
 
     // scores of the next tile (its K is already in LDS); independent of the softmax below.
     // On the last tile this reads a stale buffer and the result is discarded.
-    f32x16 s_nxt[kQueryBlocks][2];
+    f32x16 s_nxt[kQueryBlocks][kKeyBlocks];
     if constexpr (kScoresAhead) scores((j + 1) & 1, s_nxt);
 
-    // p = 2^(s c2 - m) as bf16 P^T operands (4 chunks of 16 keys), row sums
-    bf16x8 pb[kQueryBlocks][4];
+    // p = 2^(s c2 - m) as bf16 P^T operands (chunks of 16 keys), row sums
+    bf16x8 pb[kQueryBlocks][2 * kKeyBlocks];
 #pragma unroll
     for (int qb = 0; qb < kQueryBlocks; ++qb) {
       const float mneg = -m_run[qb];
       float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][kb][i], c2, mneg));
@@ -326,7 +351,7 @@ void attn_fwd(const AttnArgs a) {
     // O^T += V^T P^T with V(j) from buffer j & 1
     const int vb = j & 1;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < 2 * kKeyBlocks; ++kc) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const __bf16* base = &v_lds[vb][(16 * kc + tr_row) * kVStride + 32 * d + tr_col];
@@ -340,17 +365,48 @@ void attn_fwd(const AttnArgs a) {
       }
     }
 
+#if BCA_SCHED_INTERLEAVE
+    if constexpr (kScoresAhead && kQueryBlocks == 1 && kBlockN == 64) {
+      // Interleave, within this wave, the next tile's K reads and QK^T MFMAs with this tile's
+      // softmax arithmetic, then the V reads with the PV MFMAs (masks: 0x100 LDS read,
+      // 0x008 MFMA, 0x002 VALU).
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
+    }
+#endif
     if constexpr (kScoresAhead) {
       // refill: K(j+2) replaces K(j), V(j+1) replaces V(j-1); then start the next loads
-      if (j + 2 < ntiles) store_k(j & 1, kst);
-      if (j + 1 < ntiles) store_v((j + 1) & 1, vst);
+      if (j + 2 < ntiles) store_k(j & 1, (j + 2) * kBlockN, kst);
+      if (j + 1 < ntiles) store_v((j + 1) & 1, (j + 1) * kBlockN, vst);
       if (j + 3 < ntiles) load_k((j + 3) * kBlockN, kst);
       if (j + 2 < ntiles) load_v((j + 2) * kBlockN, vst);
     } else {
       // refill: tile j+1 replaces tile j-1; then start loading tile j+2
       if (j + 1 < ntiles) {
-        store_k((j + 1) & 1, kst);
-        store_v((j + 1) & 1, vst);
+        store_k((j + 1) & 1, (j + 1) * kBlockN, kst);
+        store_v((j + 1) & 1, (j + 1) * kBlockN, vst);
       }
       if (j + 2 < ntiles) {
         load_k((j + 2) * kBlockN, kst);
@@ -360,10 +416,9 @@ void attn_fwd(const AttnArgs a) {
     __syncthreads();
     if constexpr (kScoresAhead) {
 #pragma unroll
-      for (int qb = 0; qb < kQueryBlocks; ++qb) {
-        s_cur[qb][0] = s_nxt[qb][0];
-        s_cur[qb][1] = s_nxt[qb][1];
-      }
+      for (int qb = 0; qb < kQueryBlocks; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb) s_cur[qb][kb] = s_nxt[qb][kb];
     }
   }
 
@@ -386,27 +441,6 @@ void attn_fwd(const AttnArgs a) {
   }
 }
 
-// Prefix-K/V store: dst[b, j, h, :] = src[b, j, h, :] for j < rows, both K and V, 16 B per thread.
-__global__ __launch_bounds__(256) void prefix_copy(const CopyArgs k, const CopyArgs v) {
-  const int64_t per_row = (int64_t)k.heads * (kHeadDim / 8);
-  const int64_t total = (int64_t)k.batch * k.rows * per_row;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int col = (int)(i % (kHeadDim / 8)) * 8;
-    const int64_t r = i / (kHeadDim / 8);
-    const int hh = (int)(r % k.heads);
-    const int64_t bj = r / k.heads;
-    const int64_t j = bj % k.rows;
-    const int64_t bb = bj / k.rows;
-    const u32x4 kx =
-        *reinterpret_cast<const u32x4*>(k.src + bb * k.s_sb + j * k.s_ss + hh * k.s_sh + col);
-    const u32x4 vx =
-        *reinterpret_cast<const u32x4*>(v.src + bb * v.s_sb + j * v.s_ss + hh * v.s_sh + col);
-    *reinterpret_cast<u32x4*>(k.dst + bb * k.d_sb + j * k.d_ss + hh * k.d_sh + col) = kx;
-    *reinterpret_cast<u32x4*>(v.dst + bb * v.d_sb + j * v.d_ss + hh * v.d_sh + col) = vx;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
@@ -418,15 +452,6 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
   hipLaunchKernelGGL(attn_fwd<true>, grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefix_copy(const CopyArgs& k, const CopyArgs& v, hipStream_t stream) {
-  const int64_t total = (int64_t)k.batch * k.rows * k.heads * (kHeadDim / 8);
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(prefix_copy, dim3((unsigned)blocks), dim3(256), 0, stream, k, v);
   return hipGetLastError();
 }
 

@@ -19,7 +19,10 @@ constexpr int kHeadDim = 128;  // the only head width the kernels are built for
 constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
 constexpr int kWaves = BCA_WAVES;
 constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup (= plan tile)
-constexpr int kBlockN = 64;                          // keys per key tile
+#ifndef BCA_BLOCK_N
+#define BCA_BLOCK_N 64
+#endif
+constexpr int kBlockN = BCA_BLOCK_N;                 // keys per key tile (32 or 64)
 
 // One attention launch.  Prefill and decode share the kernel: keys j < split come from (k, v),
 // keys j >= split from (k2, v2) at index j - split.  Prefill sets split = kv_len.
@@ -36,6 +39,13 @@ struct AttnArgs {
   int64_t v2_sb, v2_ss, v2_sh;
   float* o;
   int64_t o_sb, o_ss, o_sh;
+  // Prefill only: prefix-K/V cache [B, cache_len, H, D] receiving K/V rows [0, cache_len), or
+  // NULL.  The workgroup of query tile t writes rows [t kBlockM, (t + 1) kBlockM) of it.
+  uint16_t* kc;
+  int64_t kc_sb, kc_ss, kc_sh;
+  uint16_t* vc;
+  int64_t vc_sb, vc_ss, vc_sh;
+  int32_t cache_len;
   int32_t n_q;       // query rows per (batch, head): S for prefill, N for decode
   int32_t kv_len;    // keys per (batch, head): S for prefill, P + N for decode
   int32_t split;     // first key taken from the second source
@@ -50,18 +60,7 @@ struct AttnArgs {
   const int32_t* order;
 };
 
-struct CopyArgs {
-  const uint16_t* src;
-  int64_t s_sb, s_ss, s_sh;
-  uint16_t* dst;
-  int64_t d_sb, d_ss, d_sh;
-  int32_t rows;  // positions [0, rows) are copied
-  int32_t heads;
-  int32_t batch;
-};
-
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_prefix_copy(const CopyArgs& k, const CopyArgs& v, hipStream_t stream);
 
 }  // namespace bca

@@ -1,0 +1,67 @@
+// Host-side fuzz driver for the segment planner, built with AddressSanitizer and UBSan on the CPU
+// (tests/test_planner_sanitized.py).  Random block-id layouts, including invalid ones, go
+// through build_host_plan; valid plans are checked against the rule's consequences: limits are
+// non-decreasing and at least i + 1, each tile's range brackets its rows, the order is a
+// heavy-first permutation, and the prefix ends where the last run starts.
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "bca_plan.h"
+
+static int fail(const char* what, int64_t S) {
+  std::fprintf(stderr, "FAIL %s (S=%lld)\n", what, (long long)S);
+  return 1;
+}
+
+int main(int argc, char** argv) {
+  const int iters = argc > 1 ? std::atoi(argv[1]) : 2000;
+  std::mt19937_64 rng(12345);
+  int valid = 0, rejected = 0;
+  for (int it = 0; it < iters; ++it) {
+    const int64_t S = 1 + (int64_t)(rng() % 1500);
+    std::vector<int32_t> ids((size_t)S);
+    int32_t next = 0;
+    for (int64_t i = 0; i < S;) {
+      const int64_t n = 1 + (int64_t)(rng() % 200);
+      const bool text = rng() % 2;
+      const int32_t id = text ? -1 : next++;
+      for (int64_t k = 0; k < n && i < S; ++k, ++i) ids[(size_t)i] = id;
+    }
+    if (it % 7 == 3) ids[(size_t)(rng() % S)] = -2 - (int32_t)(rng() % 5);      // invalid id
+    if (it % 11 == 5 && next > 0) ids[(size_t)(rng() % S)] = 0;                 // possible reuse
+    const int block_m = (it % 3 == 0) ? 128 : (it % 3 == 1 ? 256 : 64);
+    bca::HostPlan p;
+    std::string err;
+    const int rc = bca::build_host_plan(ids.data(), S, block_m, &p, &err);
+    if (rc != bca::kPlanOk) {
+      if (err.empty()) return fail("error without text", S);
+      ++rejected;
+      continue;
+    }
+    ++valid;
+    if ((int64_t)p.row_limit.size() != S) return fail("row_limit size", S);
+    for (int64_t i = 0; i < S; ++i) {
+      if (p.row_limit[(size_t)i] < i + 1 || p.row_limit[(size_t)i] > S) return fail("limit range", S);
+      if (i && p.row_limit[(size_t)i] < p.row_limit[(size_t)i - 1]) return fail("monotone", S);
+    }
+    const int64_t nt = (S + block_m - 1) / block_m;
+    if ((int64_t)p.kv_full.size() != nt || (int64_t)p.order.size() != nt) return fail("tiles", S);
+    std::vector<int> seen((size_t)nt, 0);
+    for (int64_t t = 0; t < nt; ++t) {
+      const int32_t o = p.order[(size_t)t];
+      if (o < 0 || o >= nt || seen[(size_t)o]++) return fail("order permutation", S);
+      if (t && p.kv_end[(size_t)p.order[(size_t)t - 1]] < p.kv_end[(size_t)o]) return fail("heavy first", S);
+      for (int64_t r = t * block_m; r < S && r < (t + 1) * block_m; ++r)
+        if (p.row_limit[(size_t)r] < p.kv_full[(size_t)t] || p.row_limit[(size_t)r] > p.kv_end[(size_t)t])
+          return fail("tile range", S);
+    }
+    const size_t nseg = p.segments.size() / 3;
+    if (p.prefix_len != p.segments[3 * (nseg - 1)] || p.prefix_len + p.target_len != S)
+      return fail("prefix", S);
+  }
+  std::printf("planner fuzz ok: %d valid, %d rejected\n", valid, rejected);
+  return 0;
+}
