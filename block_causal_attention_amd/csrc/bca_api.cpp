@@ -22,6 +22,7 @@ struct bca_plan_s {
 
 namespace {
 
+constexpr int64_t kHeadDimElems = bca::kHeadDim;
 thread_local std::string g_last_error;
 
 bca_status fail(bca_status s, const std::string& msg) {
@@ -92,6 +93,16 @@ bca_status check_launchable(bca_plan_t plan) {
   if (dev != plan->device)
     return fail(BCA_ERR_ARG, "plan lives on device " + std::to_string(plan->device) +
                                  " but device " + std::to_string(dev) + " is current");
+  return BCA_OK;
+}
+
+// K and V rows are addressed with 32-bit element offsets inside one (batch, head) slice: the row
+// stride must stay below 2^24 elements and rows * stride below 2^31.
+bca_status check_extent(const bca_tensor* t, const char* name, int64_t rows) {
+  if (t->stride_s >= (int64_t(1) << 24))
+    return fail(BCA_ERR_ARG, std::string(name) + ": stride_s must be below 2^24 elements");
+  if (rows * t->stride_s + kHeadDimElems >= (int64_t(1) << 31))
+    return fail(BCA_ERR_ARG, std::string(name) + ": rows * stride_s must be below 2^31 elements");
   return BCA_OK;
 }
 
@@ -217,6 +228,8 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
       if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
     }
   }
+  if ((s = check_extent(k, "k", hp.seq_len)) != BCA_OK) return s;
+  if ((s = check_extent(v, "v", hp.seq_len)) != BCA_OK) return s;
   const int64_t nt = (int64_t)hp.kv_end.size();
   if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles exceeds 2^31 - 1");
   if ((s = check_launchable(plan)) != BCA_OK) return s;
@@ -275,6 +288,12 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
     if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
   }
   const int64_t N = hp.target_len;
+  if ((s = check_extent(k_tgt, "k_tgt", N)) != BCA_OK) return s;
+  if ((s = check_extent(v_tgt, "v_tgt", N)) != BCA_OK) return s;
+  if (hp.prefix_len > 0) {
+    if ((s = check_extent(k_cache, "k_cache", hp.prefix_len)) != BCA_OK) return s;
+    if ((s = check_extent(v_cache, "v_cache", hp.prefix_len)) != BCA_OK) return s;
+  }
   const int64_t nt = (N + bca::kBlockM - 1) / bca::kBlockM;
   if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles exceeds 2^31 - 1");
   if ((s = check_launchable(plan)) != BCA_OK) return s;

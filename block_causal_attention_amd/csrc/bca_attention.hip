@@ -13,11 +13,12 @@
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q rows held in VGPRs.
 //                 The accumulator gives each lane ONE query (lane % 32) and 16 keys, so the row
 //                 max is an in-lane reduction plus one swap of the two 32-lane halves.
-//   online softmax in base 2 with scale*log2(e) folded into one FMA per score; a row's running
-//                 max is raised (and its O and l rescaled) only when it grew by more than 8
-//                 (p <= 2^8 is exact in fp32 and within bf16's range), so most tiles skip it.
-//                 The row sum accumulates the bf16-rounded p (the values PV uses) two at a time
-//                 with v_dot2_f32_bf16 against (1, 1).
+//   online softmax in base 2 with scale*log2(e) folded into one FMA per score.  p is computed
+//                 against the running max of earlier tiles; a row's max is raised (and its O, l
+//                 rescaled) only when its scores grew by more than 16, which shows up as a lane's
+//                 tile sum above 2^16 and sends the wave through an exact recompute.  So the
+//                 common tile needs no max reduction at all.  The row sum accumulates the
+//                 bf16-rounded p (the values PV uses) two at a time with v_dot2_f32_bf16.
 //   O^T += V^T P^T  on the same MFMA: B = P^T straight from the score registers (bf16, RNE), A =
 //                 V^T read from the row-major LDS tile with ds_read_b64_tr_b16, which hands each
 //                 lane four consecutive keys of one column.  The key order inside one MFMA step
@@ -58,7 +59,11 @@ constexpr int kChunksPerThread = kBlockN * kHeadDim / 8 / kThreads;  // staging:
 constexpr int kRowsPerPass = kThreads / 16;                          // staging: rows per pass
 constexpr int kDmaRowsPerWave = kBlockN / kWaves;                    // direct: rows per wave
 constexpr int kDmaInstr = kDmaRowsPerWave / 4;                       // direct: 4 rows per instr
-constexpr float kRescaleThreshold = 8.0f;                            // log2 units
+// A row's running max is raised only when its scores grew by more than kRescaleThreshold (log2
+// units), so p <= 2^16: exact in fp32, within bf16's exponent range, and l, O stay far below
+// fp32 overflow.  A lane's tile sum above kRescaleBound is what sends a wave to the exact path.
+constexpr float kRescaleThreshold = 16.0f;
+constexpr float kRescaleBound = 65536.0f;
 static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
 static_assert(kBlockN * kHeadDim / 8 % kThreads == 0, "whole 16-byte chunks per thread");
 static_assert(kDmaRowsPerWave % 16 == 0, "direct loads: each wave fills whole 16-row swizzle periods");
@@ -207,7 +212,13 @@ void attn_fwd(const AttnArgs a) {
       const int col = dma_col(i);
       const uint16_t* kp;
       const uint16_t* vp;
-      if (in_end && src1) {
+      if (!kDecode) {
+        // One source: clamp the key (a no-op except on the last tile) and address it with a
+        // 32-bit element offset; the host keeps seq_len * stride below 2^31 and stride below 2^24.
+        const uint32_t key = (uint32_t)min(n0 + row, kv_end - 1);
+        kp = k_base + (key * (uint32_t)a.k_ss + (uint32_t)col);
+        vp = v_base + (key * (uint32_t)a.v_ss + (uint32_t)col);
+      } else if (in_end && src1) {
         kp = k_base + (int64_t)(n0 + row) * a.k_ss + col;
         vp = v_base + (int64_t)(n0 + row) * a.v_ss + col;
       } else if (in_end && src2) {
@@ -337,32 +348,15 @@ void attn_fwd(const AttnArgs a) {
           }
     }
 
-    // ---- row max; each row raises its own running max only when it grew by more than the
-    // threshold, so a row's arithmetic depends on its own visible scores alone.  The branch is
-    // wave-uniform and merely skips the O rescale when no row of the wave needs one.
-#pragma unroll
-    for (int qb = 0; qb < kQueryBlocks; ++qb) {
-      float mx = s[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-      mx = halves_max(mx);
-      const float m_cand = fmaxf(m_run[qb], mx * c2);
-      const bool raise = m_cand > m_run[qb] + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[qb] - m_cand) : 1.0f;  // 0 at first
-        m_run[qb] = raise ? m_cand : m_run[qb];
-        l_part[qb] *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) o[qb][d] *= alpha;
-      }
-    }
-
-    // ---- p = 2^(s c2 - m) as bf16 P^T operands (chunks of 16 keys), row sums
+    // ---- p = 2^(s c2 - m) against the running max m of earlier tiles, as bf16 P^T operands
+    // (chunks of 16 keys), plus this tile's row-sum share.  A row whose scores grew past
+    // m + kRescaleThreshold (or any row on its first tile, where m = -inf) shows a lane sum
+    // above 2^threshold (or inf); only then does the wave take the exact path: per-row max, raise
+    // and rescale for rows that grew by more than the threshold, and p recomputed.  Rows that do
+    // not raise recompute the same values, so each row still depends on its own scores alone.
     bf16x8 pb[kQueryBlocks][2 * kKeyBlocks];
-#pragma unroll
-    for (int qb = 0; qb < kQueryBlocks; ++qb) {
+    float tsum[kQueryBlocks];
+    auto exp_tile = [&](int qb) {
       const float mneg = -m_run[qb];
       float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
@@ -379,8 +373,35 @@ void attn_fwd(const AttnArgs a) {
           else
             acc0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc0, false);
         }
-      l_part[qb] += acc0 + acc1;
+      tsum[qb] = acc0 + acc1;
+    };
+    bool redo = false;
+#pragma unroll
+    for (int qb = 0; qb < kQueryBlocks; ++qb) {
+      exp_tile(qb);
+      redo = redo || !(tsum[qb] <= kRescaleBound);
     }
+    if (__builtin_amdgcn_ballot_w64(redo)) {
+#pragma unroll
+      for (int qb = 0; qb < kQueryBlocks; ++qb) {
+        float mx = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+        mx = halves_max(mx);
+        const float m_cand = fmaxf(m_run[qb], mx * c2);
+        const bool raise = m_cand > m_run[qb] + kRescaleThreshold;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[qb] - m_cand) : 1.0f;  // 0 at first
+        m_run[qb] = raise ? m_cand : m_run[qb];
+        l_part[qb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[qb][d] *= alpha;
+        exp_tile(qb);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQueryBlocks; ++qb) l_part[qb] += tsum[qb];
 
     // ---- O^T += V^T P^T
 #if BCA_SETPRIO

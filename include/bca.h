@@ -22,6 +22,8 @@
  *    default stream) and return.
  *  - bca_tensor strides are in elements; the D stride is 1.  data must be 16-byte aligned;
  *    stride_b, stride_s and stride_h must be non-negative multiples of 8 (bf16) or 4 (fp32).
+ *    For K, V and the caches, stride_s must be below 2^24 and rows * stride_s below 2^31 (rows
+ *    within one (batch, head) slice are addressed with 32-bit offsets); else BCA_ERR_ARG.
  *  - scale is the softmax multiplier of q.k; 0 selects 1/sqrt(D).  Negative or NaN -> ARG.
  */
 #ifndef BCA_H

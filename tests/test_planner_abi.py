@@ -139,6 +139,11 @@ def test_launch_validation_before_any_device_work():
     assert b"HOST_ONLY" in lib.bca_last_error()
     assert call_prefill(h, v=_t(ptr=0)) == _lib.BCA_ERR_ARG                # NULL data
     assert call_prefill(h, kc=_t()) == _lib.BCA_ERR_ARG                    # half a cache
+    assert call_prefill(h, k=_t(ss=1 << 24)) == _lib.BCA_ERR_ARG           # stride_s >= 2^24
+    assert b"2^24" in lib.bca_last_error()
+    big = plan_host(np.zeros(300000, np.int32))
+    assert call_prefill(big.handle, v=_t(ss=8192)) == _lib.BCA_ERR_ARG      # rows*stride >= 2^31
+    assert b"2^31" in lib.bca_last_error()
     assert call_prefill(h) == _lib.BCA_ERR_ARG                             # host-only plan
     assert call_decode(h, D=256) == _lib.BCA_ERR_UNSUPPORTED
     assert call_decode(h, o=_t(ptr=0x10004)) == _lib.BCA_ERR_ARG
