@@ -25,13 +25,13 @@
 //                 is permuted identically in A and B, which leaves the sum unchanged.
 // K/V tiles go through a two-buffer LDS ring with one barrier per tile: tile j+1 is in flight
 // while tile j is computed.  Two ways to fill the ring (template parameter kDirect):
-//   register staging (decode): 16-byte global loads into VGPRs, written to padded LDS rows one
-//                 tile later; the per-row cache/target source choice stays in registers;
-//   direct (prefill): global_load_lds_dwordx4 writes each wave's 1 KB straight into LDS, rows
-//                 unpadded with an XOR swizzle of their 16-byte chunks (below) that keeps both
-//                 the K reads and the transposed V reads free of bank conflicts.  Measured on
-//                 the two-reference edit shape this is ~6% faster for prefill and ~8% slower
-//                 for decode than staging, hence the split.
+//   register staging (decode): 16-byte global loads into VGPRs, written to LDS one tile later;
+//                 the per-row cache/target source choice stays in registers;
+//   direct (prefill): global_load_lds_dwordx4 writes each wave's 1 KB straight into LDS.
+// Either way LDS rows are unpadded with an XOR swizzle of their 16-byte chunks (below) that keeps
+// the K reads and the transposed V reads free of bank conflicts.
+#include <type_traits>
+
 #include "bca_internal.h"
 
 namespace bca {
@@ -46,12 +46,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef BCA_SETPRIO
-#define BCA_SETPRIO 0
-#endif
 #ifndef BCA_WAVES_PER_SIMD
 #define BCA_WAVES_PER_SIMD (kQueryBlocks == 1 ? 2 : 1)
 #endif
+#ifndef BCA_STAGE_SWIZZLE
+#define BCA_STAGE_SWIZZLE 0
+#endif
+constexpr bool kStageSwizzle = BCA_STAGE_SWIZZLE;  // swizzled rows for the staging path too
 constexpr int kThreads = 64 * kWaves;
 constexpr int kOccupancy = BCA_WAVES_PER_SIMD;
 constexpr int kKeyBlocks = kBlockN / 32;  // 32-key MFMA blocks per key tile
@@ -90,10 +91,10 @@ __device__ inline float halves_sum(float x) {
 template <bool kDecode, bool kDirect>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOccupancy, kOccupancy)))
 void attn_fwd(const AttnArgs a) {
-  // LDS row strides in bf16: padded (272 B / 288 B) for register staging, unpadded and swizzled
-  // for direct loads.
-  constexpr int kKStride = kDirect ? kHeadDim : kHeadDim + 8;
-  constexpr int kVStride = kDirect ? kHeadDim : kHeadDim + 16;
+  // LDS rows: unpadded (256 B) with their 16-byte chunks swizzled, or padded (272 B / 288 B).
+  constexpr bool kSwizzle = kDirect || kStageSwizzle;
+  constexpr int kKStride = kSwizzle ? kHeadDim : kHeadDim + 8;
+  constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + 16;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBlockN * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBlockN * kVStride];
 
@@ -183,10 +184,14 @@ void attn_fwd(const AttnArgs a) {
   };
   auto stage_k = [&](int n0) { stage_tile(n0, kst, k_base, a.k_ss, k2_base, a.k2_ss); };
   auto stage_v = [&](int n0) { stage_tile(n0, vst, v_base, a.v_ss, v2_base, a.v2_ss); };
+  // 16 consecutive threads write one whole 256-byte row, so the swizzle costs no conflicts here.
+  // Rows ld_row + kRowsPerPass r share ld_row's swizzle (kRowsPerPass is a multiple of 16).
+  const int st_col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(ld_row)) : ld_col;
+  static_assert(kRowsPerPass % 16 == 0, "staging passes keep the swizzle phase");
   auto stage_write = [&](__bf16* lds, int stride, const u32x4* st) {
 #pragma unroll
     for (int r = 0; r < kChunksPerThread; ++r)
-      *reinterpret_cast<u32x4*>(&lds[(ld_row + kRowsPerPass * r) * stride + ld_col]) = st[r];
+      *reinterpret_cast<u32x4*>(&lds[(ld_row + kRowsPerPass * r) * stride + st_col]) = st[r];
   };
 
   // ---- filling the ring: direct loads ----------------------------------------------------------
@@ -251,9 +256,8 @@ void attn_fwd(const AttnArgs a) {
       const int row = ld_row + kRowsPerPass * r;
       const int key = n0 + row;
       if (key < cache_lo || key >= cache_hi) continue;
-      const int kcol = kDirect ? 8 * ((ld_col >> 3) ^ swz(row)) : ld_col;
-      const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds[buf][row * kKStride + kcol]);
-      const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds[buf][row * kVStride + kcol]);
+      const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds[buf][row * kKStride + st_col]);
+      const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds[buf][row * kVStride + st_col]);
       *reinterpret_cast<u32x4*>(a.kc + b * a.kc_sb + (int64_t)key * a.kc_ss + h * a.kc_sh + ld_col) = kx;
       *reinterpret_cast<u32x4*>(a.vc + b * a.vc_sb + (int64_t)key * a.vc_ss + h * a.vc_sh + ld_col) = vx;
     }
@@ -270,12 +274,12 @@ void attn_fwd(const AttnArgs a) {
   auto k_addr = [&](int kb, int c) {
     const int row = 32 * kb + qn;
     const int chunk = 2 * c + half;
-    return row * kKStride + 8 * (kDirect ? (chunk ^ swz(row)) : chunk);
+    return row * kKStride + 8 * (kSwizzle ? (chunk ^ swz(row)) : chunk);
   };
   auto v_addr = [&](int kc, int d, int hi) {
     const int row = 16 * kc + tr_row + 8 * hi;
     const int col = 32 * d + tr_col;
-    return row * kVStride + (kDirect ? 8 * ((col >> 3) ^ swz(row)) + (col & 7) : col);
+    return row * kVStride + (kSwizzle ? 8 * ((col >> 3) ^ swz(row)) + (col & 7) : col);
   };
 
   f32x16 o[kQueryBlocks][4];
@@ -308,14 +312,15 @@ void attn_fwd(const AttnArgs a) {
   }
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
+  // One key tile j from buffer j & 1.  kMasked: the tile crosses some row's key limit.  Full
+  // tiles run in a loop of their own, with no mask code between the score MFMAs and the
+  // softmax, so the compiler can overlap the two inside one wave.
+  auto tile_step = [&](auto masked_c, int j) {
+    constexpr bool kMasked = decltype(masked_c)::value;
     const int n0 = j * kBlockN;
     const int cur = j & 1;
     store_cache(n0, cur);
 
-#if BCA_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
     // ---- S^T = K Q^T
     f32x16 s[kQueryBlocks][kKeyBlocks];
 #pragma unroll
@@ -331,12 +336,9 @@ void attn_fwd(const AttnArgs a) {
       }
     }
 
-#if BCA_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
     // ---- mask: only tiles that cross some row's limit.  Accumulator element i of key block kb
     // holds key n0 + 32 kb + 8 (i / 4) + 4 half + i % 4.
-    if (n0 + kBlockN > kv_full) {
+    if (kMasked) {
 #pragma unroll
       for (int qb = 0; qb < kQueryBlocks; ++qb)
 #pragma unroll
@@ -404,9 +406,6 @@ void attn_fwd(const AttnArgs a) {
     for (int qb = 0; qb < kQueryBlocks; ++qb) l_part[qb] += tsum[qb];
 
     // ---- O^T += V^T P^T
-#if BCA_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
     for (int kc = 0; kc < 2 * kKeyBlocks; ++kc) {
 #pragma unroll
@@ -422,9 +421,6 @@ void attn_fwd(const AttnArgs a) {
       }
     }
 
-#if BCA_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
     // ---- refill.  Staging: write tile j+1 into the other buffer (its tile j-1 was consumed
     // before the last barrier) and start fetching tile j+2.  Direct: tile j+1 was issued one
     // iteration ago; wait for it, then after the barrier reuse this buffer for tile j+2.
@@ -443,7 +439,11 @@ void attn_fwd(const AttnArgs a) {
       }
       __syncthreads();
     }
-  }
+  };
+  // tiles [0, n_full) lie entirely below every row's limit; the rest need the mask
+  const int n_full = min(ntiles, kv_full / kBlockN);
+  for (int j = 0; j < n_full; ++j) tile_step(std::false_type{}, j);
+  for (int j = n_full; j < ntiles; ++j) tile_step(std::true_type{}, j);
 
   // ---- epilogue: O = O_acc / l; lane holds dims 32 d + 8 jj + 4 half + (0..3) of its query
 #pragma unroll
