@@ -274,3 +274,109 @@ def prefix_cache_bytes(layers: int, batch: int, prefix_len: int, heads: int, hea
     """Logical prefix-K/V payload: two tensors (K and V) of [batch, prefix, heads, head_dim] per
     layer ([QI21-guide], "The prefix cache is a compute-for-memory trade")."""
     return 2 * layers * batch * prefix_len * heads * head_dim * bytes_per_scalar
+
+
+# ----------------------------------------------------------------------------------------------
+# FP8 prefix cache
+# ----------------------------------------------------------------------------------------------
+# [QI21-article], FP8 part: the prefix K/V cache can be stored as FP8 E4M3 with one FP32 scale per
+# token and per attention head; quantising only V saves about 25% of the cache and is the safer
+# trade (K carries RoPE and drives the attention weights).  Readings: E4M3 is the OCP "E4M3FN"
+# encoding (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
+# S.1111.111 = NaN, largest finite 448); the scale of a (token, head) row is amax(|x|) / 448
+# computed in fp32 (1 for an all-zero row); a row is quantised as x * (1 / scale) in fp32 and
+# rounded to the nearest E4M3 value, ties to the even code, saturating at +-448.
+
+E4M3_MAX = 448.0
+CACHE_BF16, CACHE_FP8_V, CACHE_FP8_KV = 0, 1, 2
+
+
+def e4m3_value_table() -> np.ndarray:
+    """float64 value of each of the 256 E4M3 codes (NaN for the two NaN codes)."""
+    vals = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            vals[code] = np.nan
+        elif e == 0:
+            vals[code] = sign * (m / 8.0) * 2.0 ** (1 - 7)
+        else:
+            vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_E4M3 = e4m3_value_table()
+_E4M3_POS = _E4M3[:0x7F]  # codes 0x00..0x7E: 0 and the 126 positive finite values, ascending
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest finite E4M3 code, ties to the even code; |x| above 448 saturates; NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    dlo = np.abs(a - _E4M3_POS[lo])
+    dhi = np.abs(_E4M3_POS[hi] - a)
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a > E4M3_MAX, np.uint8(0x7E), code)
+    code = np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_fp8_rows(x: np.ndarray):
+    """Per-row (last axis) FP8 quantisation in the precision the method fixes (fp32 scales).
+
+    Returns (codes uint8 like x, scales float32 of x.shape[:-1])."""
+    xf = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(xf), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    inv = (np.float32(1.0) / scale).astype(np.float32)
+    q = (xf * inv[..., None]).astype(np.float32)
+    return e4m3_encode(q), scale
+
+
+def dequantize_fp8_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """code value * scale, exact in float64."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def prefix_cache_fp8(k: np.ndarray, v: np.ndarray, ids: Sequence[int], fmt: int) -> Dict:
+    """The prefix cache in a given format: V quantised for CACHE_FP8_V, K and V for
+    CACHE_FP8_KV, nothing for CACHE_BF16.  Quantised tensors are (codes, scales)."""
+    kc, vc = prefix_cache(k, v, ids)
+    out = {"format": fmt, "k": kc, "v": vc}
+    if fmt in (CACHE_FP8_V, CACHE_FP8_KV):
+        out["v"] = quantize_fp8_rows(vc)
+    if fmt == CACHE_FP8_KV:
+        out["k"] = quantize_fp8_rows(kc)
+    return out
+
+
+def cache_values(cache: Dict):
+    """float64 K and V of a prefix cache as the decode sees them."""
+    def val(t):
+        return dequantize_fp8_rows(*t) if isinstance(t, tuple) else np.asarray(t, np.float64)
+    return val(cache["k"]), val(cache["v"])
+
+
+def decode_cached(q_t, cache: Dict, k_t, v_t, scale: Optional[float] = None, **sel) -> np.ndarray:
+    """Cached step over a prefix cache in any format: dequantise, then the plain decode."""
+    kc, vc = cache_values(cache)
+    return decode(q_t, kc, vc, k_t, v_t, scale=scale, **sel)
+
+
+def prefix_cache_bytes_fp8(layers: int, batch: int, prefix_len: int, heads: int, head_dim: int,
+                           fmt: int) -> int:
+    """Payload of the prefix cache in a format: 2 bytes per bf16 scalar, 1 per FP8 code and 4
+    per (token, head) scale of each quantised tensor."""
+    per_tensor_bf16 = prefix_len * heads * head_dim * 2
+    per_tensor_fp8 = prefix_len * heads * head_dim + prefix_len * heads * 4
+    n_fp8 = {CACHE_BF16: 0, CACHE_FP8_V: 1, CACHE_FP8_KV: 2}[fmt]
+    return layers * batch * ((2 - n_fp8) * per_tensor_bf16 + n_fp8 * per_tensor_fp8)
