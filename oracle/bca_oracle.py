@@ -21,8 +21,11 @@ Parity pins (tests/test_oracle_pins.py): every function below is pinned by a che
 reuse its own formula -- brute force of the rule as stated in words, the per-segment
 construction, the pages' worked 3x8 example, closed forms (Q = 0), reductions to
 ``torch.nn.functional.scaled_dot_product_attention`` (unmasked, causal, piecewise segment calls),
-prefix invariance, decode == prefill rows, and the pages' cache-size figures.  No function here
-is "parity unpinned".
+prefix invariance, decode == prefill rows, and the pages' cache-size figures.  The FP8 cache
+functions (tests/test_oracle_fp8_pins.py) are pinned to the E4M3 definition (closed-form codes,
+brute-force nearest value over all 256 codes, tie midpoints), the half-ulp error bound, exact
+round trips and the pages' "V-only saves about a quarter".  No function here is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -284,10 +287,13 @@ def prefix_cache_bytes(layers: int, batch: int, prefix_len: int, heads: int, hea
 # trade (K carries RoPE and drives the attention weights).  Readings: E4M3 is the OCP "E4M3FN"
 # encoding (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
 # S.1111.111 = NaN, largest finite 448); the scale of a (token, head) row is amax(|x|) / 448
-# computed in fp32 (1 for an all-zero row); a row is quantised as x * (1 / scale) in fp32 and
-# rounded to the nearest E4M3 value, ties to the even code, saturating at +-448.
+# computed in fp32, floored at the smallest normal fp32 number (1 for an all-zero row); a row is
+# quantised as x * (1 / scale) in fp32 and rounded to the nearest E4M3 value, ties to the even
+# code, saturating at +-448 (never reached: |x * (1 / scale)| exceeds 448 by a few fp32 ulps at
+# most).
 
 E4M3_MAX = 448.0
+SCALE_FLOOR = 2.0 ** -126  # smallest normal fp32 number
 CACHE_BF16, CACHE_FP8_V, CACHE_FP8_KV = 0, 1, 2
 
 
@@ -336,7 +342,11 @@ def quantize_fp8_rows(x: np.ndarray):
     Returns (codes uint8 like x, scales float32 of x.shape[:-1])."""
     xf = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(xf), axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    # Reading: the scale is amax / 448 kept at or above the smallest normal fp32 number, so that
+    # its reciprocal stays finite for rows of tiny values (it only bites below amax ~ 2^-117);
+    # an all-zero row takes scale 1.
+    scale = np.maximum(amax / np.float32(E4M3_MAX), np.float32(SCALE_FLOOR))
+    scale = np.where(amax > 0, scale, np.float32(1.0)).astype(np.float32)
     inv = (np.float32(1.0) / scale).astype(np.float32)
     q = (xf * inv[..., None]).astype(np.float32)
     return e4m3_encode(q), scale

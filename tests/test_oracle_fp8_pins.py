@@ -168,3 +168,23 @@ def test_planted_table_mistakes_are_caught(bad_table):
 def test_planted_rounding_mistake_is_caught():
     with pytest.raises(AssertionError):
         check_encoder(_encode_ties_away, O.e4m3_value_table())
+
+
+def test_quantize_tiny_rows_keep_a_normal_scale():
+    """Rows of tiny values: the scale stays a normal fp32 number, its reciprocal finite, no
+    code is NaN, and every value comes back within half a step of the coarsest grid."""
+    x = np.zeros((4, 128), np.float32)
+    x[0, :3] = [2.0 ** -130, -2.0 ** -128, 2.0 ** -133]      # bf16 subnormals
+    x[1, 5] = 2.0 ** -118                                    # amax / 448 just below 2^-126
+    x[2, 7] = 448 * 2.0 ** -126                              # exactly at the floor
+    x[3, :] = 2.0 ** -100                                    # well above it
+    codes, scales = O.quantize_fp8_rows(x)
+    assert (scales >= np.float32(2.0 ** -126)).all()
+    assert np.isfinite(np.float32(1) / scales).all()
+    assert not np.isnan(O.e4m3_decode(codes)).any()
+    assert scales[2] == np.float32(2.0 ** -126) and scales[3] == np.float32(2.0 ** -100 / 448)
+    back = O.dequantize_fp8_rows(codes, scales)
+    step = 2.0 ** -9 * scales[:, None].astype(np.float64)    # finest E4M3 step times the scale
+    assert (np.abs(back - x) <= np.maximum(np.abs(x) / 16, step / 2)).all()
+    nz = back != 0
+    assert (np.sign(back[nz]) == np.sign(x[nz])).all()
