@@ -93,6 +93,46 @@ def cpu_baseline(W, lay, ids, P, N, budget_rows, heads):
     }
 
 
+def fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od, flops_pre, flops_dec, Bd, S, H, P,
+                dev, iters=10):
+    """The same prefill and decode calls with the prefix cache stored as FP8 E4M3 (V only, then
+    K and V): ms per call, useful TFLOP/s and the cache bytes per layer of the CFG pair."""
+    out = {}
+    for name, fmt in (("fp8_v", bca.KVCache.FP8_V), ("fp8_kv", bca.KVCache.FP8_KV)):
+        c1 = bca.KVCache.empty(plan, 1, H, fmt, device=dev)
+        c2 = bca.KVCache.empty(plan, Bd, H, fmt, device=dev)
+        q2, k2, v2 = (to_dev(torch, x, dev) for x in W.qkv(W.SEEDS["edit_2ref_cfg"], Bd, S, H))
+        bca.prefill_ex(plan, q2, k2, v2, c2)
+        del q2, k2, v2
+        for i in range(3):
+            qt, kt, vt = sets[i % len(sets)]
+            bca.prefill_ex(plan, q, k, v, c1, out=o)
+            bca.decode_ex(plan, qt, c2, kt, vt, out=od)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        for i in range(iters):
+            bca.prefill_ex(plan, q, k, v, c1, out=o)
+        ev[1].record()
+        for i in range(iters):
+            qt, kt, vt = sets[i % len(sets)]
+            bca.decode_ex(plan, qt, c2, kt, vt, out=od)
+        ev[2].record()
+        torch.cuda.synchronize()
+        pre_ms = ev[0].elapsed_time(ev[1]) / iters
+        dec_ms = ev[1].elapsed_time(ev[2]) / iters
+        out[name] = {"prefill_ms": round(pre_ms, 4),
+                     "prefill_useful_tflops": round(flops_pre / (pre_ms * 1e-3) / 1e12, 2),
+                     "decode_ms": round(dec_ms, 4),
+                     "decode_useful_tflops": round(flops_dec / (dec_ms * 1e-3) / 1e12, 2),
+                     "cache_mb_per_layer_b2": round(c2.nbytes() / 1e6, 2)}
+        log(f"{name}: prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms, cache "
+            f"{c2.nbytes() / 1e6:.1f} MB per layer (B={Bd})")
+        del c1, c2
+    out["bf16_cache_mb_per_layer_b2"] = round(2 * Bd * P * H * HEAD_DIM * 2 / 1e6, 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +143,8 @@ def main():
                     help="prefill rows in the CPU-oracle sample")
     ap.add_argument("--cpu-heads", type=int, default=10,
                     help="heads in the CPU-oracle sample")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 prefix-cache timings (reported beside the bf16 step)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -197,13 +239,16 @@ def main():
 
     # the dominant kernel: the call with the larger share of the step
     if dec_ms.mean() >= pre_ms.mean():
-        dom, key, achieved = "decode: attn_fwd<true, false>, B=2", "decode_cfg_b2", dec_tf
+        dom, key, achieved = "decode: attn_fwd<true, false, 0>, B=2", "decode_cfg_b2", dec_tf
     else:
-        dom, key, achieved = "prefill: attn_fwd<false, true> (writes the prefix cache), B=1", \
-            "prefill_b1", pre_tf
+        dom, key, achieved = ("prefill: attn_fwd<false, true, 0> (writes the prefix cache), B=1",
+                              "prefill_b1", pre_tf)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(key), "kernel": dom}
+
+    fp8 = None if args.no_fp8 else fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od,
+                                               flops_pre, flops_dec, Bd, S, H, P, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -230,6 +275,7 @@ def main():
                    "useful_tflops": round(dec_tf, 2), "frac_peak": round(dec_tf / PEAK_BF16_TFLOPS, 4),
                    "useful_gflop": round(flops_dec / 1e9, 1)},
         "plan_ms": round(plan_ms, 3),
+        "fp8_cache": fp8,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

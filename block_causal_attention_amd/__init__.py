@@ -6,6 +6,10 @@ kernels.  PyTorch supplies device memory and the current stream.
     plan = Plan(block_ids)                        # -1 text, k >= 0 image block k
     o = prefill(plan, q, k, v, k_cache=kc, v_cache=vc)  # bf16 [B,S,H,128] -> fp32, fills cache
     o_t = decode(plan, q_t, kc, vc, k_t, v_t)     # bf16 target [B,N,H,128] -> fp32
+
+    cache = KVCache.empty(plan, B, H, KVCache.FP8_V)    # FP8 prefix cache (bca_kv_cache)
+    o = prefill_ex(plan, q, k, v, cache)
+    o_t = decode_ex(plan, q_t, cache, k_t, v_t)
 """
 from __future__ import annotations
 
@@ -15,9 +19,10 @@ from typing import Dict, Optional
 import numpy as np
 
 from . import _lib
-from ._lib import BcaPlanInfo, BcaTensor
+from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 
-__all__ = ["Plan", "prefill", "decode", "BcaError", "plan_info"]
+__all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
+           "plan_info"]
 
 
 class BcaError(RuntimeError):
@@ -104,6 +109,75 @@ def _desc(t, name: str, dtype) -> BcaTensor:
     return BcaTensor(t.data_ptr(), sb, ss, sh)
 
 
+def _scale_desc(t, name: str) -> BcaTensor:
+    """bca_tensor of a 3-D fp32 [B, P, H] scale tensor."""
+    import torch
+
+    if t.dtype != torch.float32 or t.dim() != 3 or not t.is_cuda:
+        raise ValueError(f"{name} must be a float32 device tensor [B, P, H]")
+    sb, ss, sh = t.stride()
+    return BcaTensor(t.data_ptr(), sb, ss, sh)
+
+
+class KVCache:
+    """A prefix K/V cache in one of the storage formats of bca.h (bca_kv_cache).
+
+    BF16: k, v bf16 [B, P, H, D].  FP8_V: k bf16, v uint8 E4M3 codes [B, P, H, D] and v_scale
+    fp32 [B, P, H].  FP8_KV: k and v codes with k_scale and v_scale."""
+
+    BF16 = _lib.BCA_CACHE_BF16
+    FP8_V = _lib.BCA_CACHE_FP8_V
+    FP8_KV = _lib.BCA_CACHE_FP8_KV
+
+    def __init__(self, fmt: int, k, v, k_scale=None, v_scale=None):
+        if fmt not in (self.BF16, self.FP8_V, self.FP8_KV):
+            raise ValueError(f"unknown cache format {fmt}")
+        self.format, self.k, self.v, self.k_scale, self.v_scale = fmt, k, v, k_scale, v_scale
+
+    @property
+    def k_quantized(self) -> bool:
+        return self.format == self.FP8_KV
+
+    @property
+    def v_quantized(self) -> bool:
+        return self.format != self.BF16
+
+    @classmethod
+    def empty(cls, plan: "Plan", batch: int, heads: int, fmt: int = 0, head_dim: int = 128,
+              device="cuda") -> "KVCache":
+        import torch
+
+        P = plan.info.prefix_len
+        shape = (batch, P, heads, head_dim)
+        kq, vq = fmt == cls.FP8_KV, fmt != cls.BF16
+        k = torch.empty(shape, dtype=torch.uint8 if kq else torch.bfloat16, device=device)
+        v = torch.empty(shape, dtype=torch.uint8 if vq else torch.bfloat16, device=device)
+        ks = torch.empty((batch, P, heads), dtype=torch.float32, device=device) if kq else None
+        vs = torch.empty((batch, P, heads), dtype=torch.float32, device=device) if vq else None
+        return cls(fmt, k, v, ks, vs)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None)
+
+    def _struct(self, B: int, P: int, H: int, D: int) -> BcaKvCache:
+        import torch
+
+        c = BcaKvCache()
+        c.format = self.format
+        for name, t, q in (("k", self.k, self.k_quantized), ("v", self.v, self.v_quantized)):
+            if t is None or tuple(t.shape) != (B, P, H, D):
+                raise ValueError(f"cache.{name} must be [B, P={P}, H, D]")
+            setattr(c, name, _desc(t, f"cache.{name}", torch.uint8 if q else torch.bfloat16))
+        for name, t, q in (("k_scale", self.k_scale, self.k_quantized),
+                           ("v_scale", self.v_scale, self.v_quantized)):
+            if q:
+                if t is None or tuple(t.shape) != (B, P, H):
+                    raise ValueError(f"cache.{name} must be [B, P={P}, H]")
+                setattr(c, name, _scale_desc(t, f"cache.{name}"))
+        return c
+
+
 def _scale(scale: Optional[float]) -> float:
     return 0.0 if scale is None else float(scale)
 
@@ -167,6 +241,63 @@ def decode(plan: Plan, q, k_cache, v_cache, k, v, *, scale: Optional[float] = No
         _check(_lib.load().bca_decode(
             plan.handle, B, H, D, _scale(scale), ctypes.byref(_desc(q, "q", torch.bfloat16)),
             kc, vc, ctypes.byref(_desc(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc(v, "v", torch.bfloat16)),
+            ctypes.byref(_desc(out, "out", torch.float32)), ctypes.c_void_p(stream)))
+    return out
+
+
+def prefill_ex(plan: Plan, q, k, v, cache: Optional[KVCache] = None, *,
+               scale: Optional[float] = None, out=None):
+    """Block-causal prefill storing the prefix cache in any format (bca_prefill_ex)."""
+    import torch
+
+    B, S, H, D = q.shape
+    if tuple(k.shape) != (B, S, H, D) or tuple(v.shape) != (B, S, H, D):
+        raise ValueError("q, k, v must share the shape [B, S, H, D]")
+    if S != plan.info.seq_len:
+        raise ValueError(f"sequence length {S} != plan's {plan.info.seq_len}")
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, S, H, D):
+        raise ValueError("out has the wrong shape")
+    P = plan.info.prefix_len
+    c = None
+    if cache is not None and P > 0:
+        c = ctypes.byref(cache._struct(B, P, H, D))
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_prefill_ex(
+            plan.handle, B, H, D, _scale(scale),
+            ctypes.byref(_desc(q, "q", torch.bfloat16)), ctypes.byref(_desc(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc(v, "v", torch.bfloat16)),
+            ctypes.byref(_desc(out, "out", torch.float32)), c, ctypes.c_void_p(stream)))
+    return out
+
+
+def decode_ex(plan: Plan, q, cache: Optional[KVCache], k, v, *, scale: Optional[float] = None,
+              out=None):
+    """Prefix-cached decode over a cache of any format (bca_decode_ex); returns fp32."""
+    import torch
+
+    B, N, H, D = q.shape
+    P = plan.info.prefix_len
+    if N != plan.info.target_len:
+        raise ValueError(f"target length {N} != plan's {plan.info.target_len}")
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (B, N, H, D):
+            raise ValueError(f"{name} must be [B, {N}, H, D]")
+    if P > 0 and cache is None:
+        raise ValueError("the prefix is not empty: a cache is required")
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, N, H, D):
+        raise ValueError("out has the wrong shape")
+    c = ctypes.byref(cache._struct(B, P, H, D)) if P > 0 else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_decode_ex(
+            plan.handle, B, H, D, _scale(scale), ctypes.byref(_desc(q, "q", torch.bfloat16)), c,
+            ctypes.byref(_desc(k, "k", torch.bfloat16)),
             ctypes.byref(_desc(v, "v", torch.bfloat16)),
             ctypes.byref(_desc(out, "out", torch.float32)), ctypes.c_void_p(stream)))
     return out

@@ -15,15 +15,23 @@ BCA_ERR_NO_DECODE = 4
 BCA_ERR_ALLOC = 5
 BCA_ERR_HIP = 6
 BCA_PLAN_HOST_ONLY = 1
+BCA_CACHE_BF16 = 0
+BCA_CACHE_FP8_V = 1
+BCA_CACHE_FP8_KV = 2
 
 # every symbol include/bca.h declares
 EXPORTED = ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export", "bca_prefill",
-            "bca_decode", "bca_status_str", "bca_last_error")
+            "bca_decode", "bca_prefill_ex", "bca_decode_ex", "bca_status_str", "bca_last_error")
 
 
 class BcaTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
                 ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class BcaKvCache(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("k", BcaTensor), ("v", BcaTensor),
+                ("k_scale", BcaTensor), ("v_scale", BcaTensor)]
 
 
 class BcaPlanInfo(ctypes.Structure):
@@ -57,12 +65,17 @@ def load() -> ctypes.CDLL:
                                 T, T, T, T, T, T, P]
     lib.bca_decode.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                T, T, T, T, T, T, P]
+    C = ctypes.POINTER(BcaKvCache)
+    lib.bca_prefill_ex.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_float, T, T, T, T, C, P]
+    lib.bca_decode_ex.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_float, T, C, T, T, T, P]
     lib.bca_status_str.argtypes = [ctypes.c_int]
     lib.bca_status_str.restype = ctypes.c_char_p
     lib.bca_last_error.argtypes = []
     lib.bca_last_error.restype = ctypes.c_char_p
     for name in ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export",
-                 "bca_prefill", "bca_decode"):
+                 "bca_prefill", "bca_decode", "bca_prefill_ex", "bca_decode_ex"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -106,6 +106,59 @@ bca_status check_extent(const bca_tensor* t, const char* name, int64_t rows) {
   return BCA_OK;
 }
 
+// A scale tensor: fp32, 4-byte aligned, non-negative strides.
+bca_status check_scale_tensor(const bca_tensor* t, const char* name) {
+  if (t->data == nullptr) return fail(BCA_ERR_ARG, std::string(name) + ": data is NULL");
+  if (reinterpret_cast<uintptr_t>(t->data) % 4 != 0)
+    return fail(BCA_ERR_ARG, std::string(name) + ": data is not 4-byte aligned");
+  if (t->stride_b < 0 || t->stride_s < 0 || t->stride_h < 0)
+    return fail(BCA_ERR_ARG, std::string(name) + ": strides must be non-negative");
+  return BCA_OK;
+}
+
+// A prefix cache of `rows` positions: format, then each tensor by its storage type.
+bca_status check_format(const bca_kv_cache* c) {
+  if (c->format != BCA_CACHE_BF16 && c->format != BCA_CACHE_FP8_V &&
+      c->format != BCA_CACHE_FP8_KV)
+    return fail(BCA_ERR_ARG, "cache: unknown format " + std::to_string(c->format));
+  return BCA_OK;
+}
+
+bca_status check_cache(const bca_kv_cache* c, int64_t rows) {
+  bca_status s = check_format(c);
+  if (s != BCA_OK) return s;
+  const bool kq = c->format == BCA_CACHE_FP8_KV;
+  const bool vq = c->format != BCA_CACHE_BF16;
+  if ((s = check_tensor(&c->k, kq ? "cache.k (codes)" : "cache.k", kq ? 1 : 2)) != BCA_OK) return s;
+  if ((s = check_tensor(&c->v, vq ? "cache.v (codes)" : "cache.v", vq ? 1 : 2)) != BCA_OK) return s;
+  if ((s = check_extent(&c->k, "cache.k", rows)) != BCA_OK) return s;
+  if ((s = check_extent(&c->v, "cache.v", rows)) != BCA_OK) return s;
+  if (kq && (s = check_scale_tensor(&c->k_scale, "cache.k_scale")) != BCA_OK) return s;
+  if (vq && (s = check_scale_tensor(&c->v_scale, "cache.v_scale")) != BCA_OK) return s;
+  return BCA_OK;
+}
+
+void set_cache_args(const bca_kv_cache* c, bca::AttnArgs* a) {
+  a->cache_fmt = c->format;
+  if (c->format == BCA_CACHE_FP8_KV) {
+    a->kcs = static_cast<float*>(c->k_scale.data);
+    a->kcs_sb = c->k_scale.stride_b; a->kcs_ss = c->k_scale.stride_s; a->kcs_sh = c->k_scale.stride_h;
+  }
+  if (c->format != BCA_CACHE_BF16) {
+    a->vcs = static_cast<float*>(c->v_scale.data);
+    a->vcs_sb = c->v_scale.stride_b; a->vcs_ss = c->v_scale.stride_s; a->vcs_sh = c->v_scale.stride_h;
+  }
+}
+
+// A bf16 cache descriptor from the plain entry points' pair of tensors.
+bca_kv_cache bf16_cache(const bca_tensor* k_cache, const bca_tensor* v_cache) {
+  bca_kv_cache c{};
+  c.format = BCA_CACHE_BF16;
+  c.k = *k_cache;
+  c.v = *v_cache;
+  return c;
+}
+
 bool grid_fits(int64_t tiles, int32_t B, int32_t H) {
   return tiles * (int64_t)B * (int64_t)H <= (int64_t)INT32_MAX;
 }
@@ -207,10 +260,9 @@ bca_status bca_plan_export(bca_plan_t plan, int32_t* segments, int32_t* row_limi
   return BCA_OK;
 }
 
-bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
-                       const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
-                       const bca_tensor* o, const bca_tensor* k_cache, const bca_tensor* v_cache,
-                       void* stream) {
+bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                          const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
+                          const bca_tensor* o, const bca_kv_cache* cache, void* stream) {
   float scale_log2 = 0.0f;
   bca_status s = check_common(plan, B, H, D, scale, &scale_log2);
   if (s != BCA_OK) return s;
@@ -218,16 +270,10 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   if ((s = check_tensor(k, "k", 2)) != BCA_OK) return s;
   if ((s = check_tensor(v, "v", 2)) != BCA_OK) return s;
   if ((s = check_tensor(o, "o", 4)) != BCA_OK) return s;
-  const bool want_cache = k_cache != nullptr || v_cache != nullptr;
   const bca::HostPlan& hp = plan->host;
-  if (want_cache) {
-    if (k_cache == nullptr || v_cache == nullptr)
-      return fail(BCA_ERR_ARG, "k_cache and v_cache must both be given or both be NULL");
-    if (hp.prefix_len > 0) {
-      if ((s = check_tensor(k_cache, "k_cache", 2)) != BCA_OK) return s;
-      if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
-    }
-  }
+  const bool store = cache != nullptr && hp.prefix_len > 0;  // P = 0: nothing to store
+  if (cache != nullptr && (s = check_format(cache)) != BCA_OK) return s;
+  if (store && (s = check_cache(cache, hp.prefix_len)) != BCA_OK) return s;
   if ((s = check_extent(k, "k", hp.seq_len)) != BCA_OK) return s;
   if ((s = check_extent(v, "v", hp.seq_len)) != BCA_OK) return s;
   const int64_t nt = (int64_t)hp.kv_end.size();
@@ -237,12 +283,14 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   bca::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q->data);
   a.q_sb = q->stride_b; a.q_ss = q->stride_s; a.q_sh = q->stride_h;
-  a.k = static_cast<const uint16_t*>(k->data);
+  a.k = k->data;
   a.k_sb = k->stride_b; a.k_ss = k->stride_s; a.k_sh = k->stride_h;
-  a.v = static_cast<const uint16_t*>(v->data);
+  a.v = v->data;
   a.v_sb = v->stride_b; a.v_ss = v->stride_s; a.v_sh = v->stride_h;
-  a.k2 = a.k; a.k2_sb = a.k_sb; a.k2_ss = a.k_ss; a.k2_sh = a.k_sh;
-  a.v2 = a.v; a.v2_sb = a.v_sb; a.v2_ss = a.v_ss; a.v2_sh = a.v_sh;
+  a.k2 = static_cast<const uint16_t*>(k->data);
+  a.k2_sb = a.k_sb; a.k2_ss = a.k_ss; a.k2_sh = a.k_sh;
+  a.v2 = static_cast<const uint16_t*>(v->data);
+  a.v2_sb = a.v_sb; a.v2_ss = a.v_ss; a.v2_sh = a.v_sh;
   a.o = static_cast<float*>(o->data);
   a.o_sb = o->stride_b; a.o_ss = o->stride_s; a.o_sh = o->stride_h;
   a.n_q = (int32_t)hp.seq_len;
@@ -256,22 +304,35 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   a.kv_full = plan->d_kv_full;
   a.kv_end = plan->d_kv_end;
   a.order = plan->d_order;
-  if (want_cache && hp.prefix_len > 0) {
-    a.kc = static_cast<uint16_t*>(k_cache->data);
-    a.kc_sb = k_cache->stride_b; a.kc_ss = k_cache->stride_s; a.kc_sh = k_cache->stride_h;
-    a.vc = static_cast<uint16_t*>(v_cache->data);
-    a.vc_sb = v_cache->stride_b; a.vc_ss = v_cache->stride_s; a.vc_sh = v_cache->stride_h;
+  a.cache_fmt = BCA_CACHE_BF16;
+  if (store) {
+    a.kc = cache->k.data;
+    a.kc_sb = cache->k.stride_b; a.kc_ss = cache->k.stride_s; a.kc_sh = cache->k.stride_h;
+    a.vc = cache->v.data;
+    a.vc_sb = cache->v.stride_b; a.vc_ss = cache->v.stride_s; a.vc_sh = cache->v.stride_h;
     a.cache_len = (int32_t)hp.prefix_len;
+    set_cache_args(cache, &a);
   }
   hipError_t e = bca::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return BCA_OK;
 }
 
-bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
-                      const bca_tensor* q_tgt, const bca_tensor* k_cache,
-                      const bca_tensor* v_cache, const bca_tensor* k_tgt,
-                      const bca_tensor* v_tgt, const bca_tensor* o, void* stream) {
+bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                       const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
+                       const bca_tensor* o, const bca_tensor* k_cache, const bca_tensor* v_cache,
+                       void* stream) {
+  if ((k_cache == nullptr) != (v_cache == nullptr))
+    return fail(BCA_ERR_ARG, "k_cache and v_cache must both be given or both be NULL");
+  if (k_cache == nullptr) return bca_prefill_ex(plan, B, H, D, scale, q, k, v, o, nullptr, stream);
+  const bca_kv_cache c = bf16_cache(k_cache, v_cache);
+  return bca_prefill_ex(plan, B, H, D, scale, q, k, v, o, &c, stream);
+}
+
+bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                         const bca_tensor* q_tgt, const bca_kv_cache* cache,
+                         const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
+                         void* stream) {
   float scale_log2 = 0.0f;
   bca_status s = check_common(plan, B, H, D, scale, &scale_log2);
   if (s != BCA_OK) return s;
@@ -283,17 +344,15 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
   if ((s = check_tensor(k_tgt, "k_tgt", 2)) != BCA_OK) return s;
   if ((s = check_tensor(v_tgt, "v_tgt", 2)) != BCA_OK) return s;
   if ((s = check_tensor(o, "o", 4)) != BCA_OK) return s;
-  if (hp.prefix_len > 0) {
-    if ((s = check_tensor(k_cache, "k_cache", 2)) != BCA_OK) return s;
-    if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
+  const bool use_cache = hp.prefix_len > 0;
+  if (use_cache) {
+    if (cache == nullptr)
+      return fail(BCA_ERR_ARG, "the prefix is not empty: the cache (K and V) is required");
+    if ((s = check_cache(cache, hp.prefix_len)) != BCA_OK) return s;
   }
   const int64_t N = hp.target_len;
   if ((s = check_extent(k_tgt, "k_tgt", N)) != BCA_OK) return s;
   if ((s = check_extent(v_tgt, "v_tgt", N)) != BCA_OK) return s;
-  if (hp.prefix_len > 0) {
-    if ((s = check_extent(k_cache, "k_cache", hp.prefix_len)) != BCA_OK) return s;
-    if ((s = check_extent(v_cache, "v_cache", hp.prefix_len)) != BCA_OK) return s;
-  }
   const int64_t nt = (N + bca::kBlockM - 1) / bca::kBlockM;
   if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles exceeds 2^31 - 1");
   if ((s = check_launchable(plan)) != BCA_OK) return s;
@@ -305,11 +364,13 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
   a.k2_sb = k_tgt->stride_b; a.k2_ss = k_tgt->stride_s; a.k2_sh = k_tgt->stride_h;
   a.v2 = static_cast<const uint16_t*>(v_tgt->data);
   a.v2_sb = v_tgt->stride_b; a.v2_ss = v_tgt->stride_s; a.v2_sh = v_tgt->stride_h;
-  if (hp.prefix_len > 0) {
-    a.k = static_cast<const uint16_t*>(k_cache->data);
-    a.k_sb = k_cache->stride_b; a.k_ss = k_cache->stride_s; a.k_sh = k_cache->stride_h;
-    a.v = static_cast<const uint16_t*>(v_cache->data);
-    a.v_sb = v_cache->stride_b; a.v_ss = v_cache->stride_s; a.v_sh = v_cache->stride_h;
+  a.cache_fmt = BCA_CACHE_BF16;
+  if (use_cache) {
+    a.k = cache->k.data;
+    a.k_sb = cache->k.stride_b; a.k_ss = cache->k.stride_s; a.k_sh = cache->k.stride_h;
+    a.v = cache->v.data;
+    a.v_sb = cache->v.stride_b; a.v_ss = cache->v.stride_s; a.v_sh = cache->v.stride_h;
+    set_cache_args(cache, &a);
   } else {  // no prefix: every key comes from the target
     a.k = a.k2; a.k_sb = a.k2_sb; a.k_ss = a.k2_ss; a.k_sh = a.k2_sh;
     a.v = a.v2; a.v_sb = a.v2_sb; a.v_ss = a.v2_ss; a.v_sh = a.v2_sh;
@@ -326,6 +387,16 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
   hipError_t e = bca::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return BCA_OK;
+}
+
+bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                      const bca_tensor* q_tgt, const bca_tensor* k_cache,
+                      const bca_tensor* v_cache, const bca_tensor* k_tgt,
+                      const bca_tensor* v_tgt, const bca_tensor* o, void* stream) {
+  if (k_cache == nullptr || v_cache == nullptr)
+    return bca_decode_ex(plan, B, H, D, scale, q_tgt, nullptr, k_tgt, v_tgt, o, stream);
+  const bca_kv_cache c = bf16_cache(k_cache, v_cache);
+  return bca_decode_ex(plan, B, H, D, scale, q_tgt, &c, k_tgt, v_tgt, o, stream);
 }
 
 }  // extern "C"

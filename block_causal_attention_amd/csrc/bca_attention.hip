@@ -43,6 +43,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -88,9 +89,58 @@ __device__ inline float halves_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
 }
 
-template <bool kDecode, bool kDirect>
+// FP8 prefix cache (E4M3, one fp32 scale per (token, head) row; the exact rule is in bca.h).
+// A staged row of a quantised tensor travels as {8 code bytes, scale bits, 0}; dequant turns it
+// into the 8 bf16 values E4M3(code) * scale that the LDS tile holds.
+__device__ inline u32x4 dequant(u32x4 x) {
+  // (the element goes through a scalar first: hipcc lowers a bit_cast of an ext_vector element
+  // operand to a cast of element 0)
+  const uint32_t sc_bits = x[2];
+  const float sc = __builtin_bit_cast(float, sc_bits);
+  const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], false);  // bytes 0, 1
+  const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], true);   // bytes 2, 3
+  const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], false);
+  const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], true);
+  const bf16x8 r = {(__bf16)(p0[0] * sc), (__bf16)(p0[1] * sc), (__bf16)(p1[0] * sc),
+                    (__bf16)(p1[1] * sc), (__bf16)(p2[0] * sc), (__bf16)(p2[1] * sc),
+                    (__bf16)(p3[0] * sc), (__bf16)(p3[1] * sc)};
+  return __builtin_bit_cast(u32x4, r);
+}
+
+// Quantises this lane's 8 bf16 values of a 128-wide row held by 16 consecutive lanes (8 values
+// each): the row's amax comes from a 16-lane max, scale = max(amax / 448, 2^-126) (1 if amax is
+// 0) and codes = E4M3(x * (1 / scale)), all divisions correctly rounded and the conversion
+// round-to-nearest-even.  Returns the 8 codes; *scale_out gets the row scale.
+__device__ inline u32x2 quantize_row8(u32x4 x, float* scale_out) {
+  const bf16x8 xb = __builtin_bit_cast(bf16x8, x);
+  float f[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[i] = (float)xb[i];
+    amax = fmaxf(amax, fabsf(f[i]));
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float scale = amax > 0.0f ? fmaxf(amax / 448.0f, 0x1p-126f) : 1.0f;
+  const float inv = 1.0f / scale;
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv, f[1] * inv, 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv, f[3] * inv, w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * inv, f[5] * inv, 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * inv, f[7] * inv, w1, true);
+  *scale_out = scale;
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+
+template <bool kDecode, bool kDirect, int kFmt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOccupancy, kOccupancy)))
 void attn_fwd(const AttnArgs a) {
+  // The prefill stores a quantised cache; the decode reads one (its first key source).
+  constexpr bool kKq = kFmt == kCacheFp8KV;
+  constexpr bool kVq = kFmt != kCacheBf16;
+  constexpr bool kKqSrc = kDecode && kKq;
+  constexpr bool kVqSrc = kDecode && kVq;
+  static_assert(!(kDirect && (kKqSrc || kVqSrc)), "direct loads move bf16 rows only");
   // LDS rows: unpadded (256 B) with their 16-byte chunks swizzled, or padded (272 B / 288 B).
   constexpr bool kSwizzle = kDirect || kStageSwizzle;
   constexpr int kKStride = kSwizzle ? kHeadDim : kHeadDim + 8;
@@ -142,8 +192,13 @@ void attn_fwd(const AttnArgs a) {
     }
   }
 
-  const uint16_t* k_base = a.k + b * a.k_sb + h * a.k_sh;
-  const uint16_t* v_base = a.v + b * a.v_sb + h * a.v_sh;
+  // first key source: bf16, or (decode over a quantised cache) code bytes plus row scales
+  const uint16_t* k_base = static_cast<const uint16_t*>(a.k) + b * a.k_sb + h * a.k_sh;
+  const uint16_t* v_base = static_cast<const uint16_t*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const uint8_t* k8_base = static_cast<const uint8_t*>(a.k) + b * a.k_sb + h * a.k_sh;
+  const uint8_t* v8_base = static_cast<const uint8_t*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const float* ks_base = kKqSrc ? a.kcs + b * a.kcs_sb + h * a.kcs_sh : nullptr;
+  const float* vs_base = kVqSrc ? a.vcs + b * a.vcs_sb + h * a.vcs_sh : nullptr;
   const uint16_t* k2_base = a.k2 + b * a.k2_sb + h * a.k2_sh;
   const uint16_t* v2_base = a.v2 + b * a.v2_sb + h * a.v2_sh;
 
@@ -182,16 +237,76 @@ void attn_fwd(const AttnArgs a) {
       }
     }
   };
-  auto stage_k = [&](int n0) { stage_tile(n0, kst, k_base, a.k_ss, k2_base, a.k2_ss); };
-  auto stage_v = [&](int n0) { stage_tile(n0, vst, v_base, a.v_ss, v2_base, a.v2_ss); };
+  // The same for a quantised first source: each chunk is 8 code bytes plus its row's scale.
+  auto stage_tile_q = [&](int n0, u32x4* st, const uint8_t* base1, int64_t ss1,
+                          const float* sbase1, int64_t sss1, const uint16_t* base2, int64_t ss2) {
+    auto load1 = [&](int key) {
+      const u32x2 c = *reinterpret_cast<const u32x2*>(base1 + (int64_t)key * ss1 + ld_col);
+      const float sc = sbase1[(int64_t)key * sss1];
+      return u32x4{c[0], c[1], __builtin_bit_cast(uint32_t, sc), 0u};
+    };
+    const bool in_end = n0 + kBlockN <= kv_end;
+    if (in_end && n0 + kBlockN <= a.split) {
+#pragma unroll
+      for (int r = 0; r < kChunksPerThread; ++r) st[r] = load1(n0 + ld_row + kRowsPerPass * r);
+    } else if (in_end && n0 >= a.split) {
+      const uint16_t* t = base2 + (int64_t)(n0 - a.split + ld_row) * ss2 + ld_col;
+#pragma unroll
+      for (int r = 0; r < kChunksPerThread; ++r)
+        st[r] = *reinterpret_cast<const u32x4*>(t + (int64_t)(kRowsPerPass * r) * ss2);
+    } else {
+#pragma unroll
+      for (int r = 0; r < kChunksPerThread; ++r) {
+        const int key = n0 + ld_row + kRowsPerPass * r;
+        const bool valid = key < kv_end;
+        const int kc = valid ? key : kv_end - 1;
+        u32x4 x;
+        if (kc < a.split)
+          x = load1(kc);
+        else
+          x = *reinterpret_cast<const u32x4*>(base2 + (int64_t)(kc - a.split) * ss2 + ld_col);
+        st[r] = valid ? x : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto stage_k = [&](int n0) {
+    if constexpr (kKqSrc)
+      stage_tile_q(n0, kst, k8_base, a.k_ss, ks_base, a.kcs_ss, k2_base, a.k2_ss);
+    else
+      stage_tile(n0, kst, k_base, a.k_ss, k2_base, a.k2_ss);
+  };
+  auto stage_v = [&](int n0) {
+    if constexpr (kVqSrc)
+      stage_tile_q(n0, vst, v8_base, a.v_ss, vs_base, a.vcs_ss, v2_base, a.v2_ss);
+    else
+      stage_tile(n0, vst, v_base, a.v_ss, v2_base, a.v2_ss);
+  };
   // 16 consecutive threads write one whole 256-byte row, so the swizzle costs no conflicts here.
   // Rows ld_row + kRowsPerPass r share ld_row's swizzle (kRowsPerPass is a multiple of 16).
   const int st_col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(ld_row)) : ld_col;
   static_assert(kRowsPerPass % 16 == 0, "staging passes keep the swizzle phase");
-  auto stage_write = [&](__bf16* lds, int stride, const u32x4* st) {
+  // Rows of a quantised source (keys below split) are dequantised on the way into LDS.
+  auto stage_write = [&](auto quant_c, __bf16* lds, int stride, const u32x4* st, int n0) {
+    constexpr bool kQ = decltype(quant_c)::value;
+    const bool all_q = kQ && n0 + kBlockN <= a.split;
+    const bool some_q = kQ && n0 < a.split;
 #pragma unroll
-    for (int r = 0; r < kChunksPerThread; ++r)
-      *reinterpret_cast<u32x4*>(&lds[(ld_row + kRowsPerPass * r) * stride + st_col]) = st[r];
+    for (int r = 0; r < kChunksPerThread; ++r) {
+      u32x4 x = st[r];
+      if (kQ && all_q) {
+        x = dequant(x);
+      } else if (kQ && some_q) {
+        const u32x4 d = dequant(x);
+        x = n0 + ld_row + kRowsPerPass * r < a.split ? d : x;
+      }
+      *reinterpret_cast<u32x4*>(&lds[(ld_row + kRowsPerPass * r) * stride + st_col]) = x;
+    }
+  };
+  auto write_k = [&](__bf16* lds, int n0) {
+    stage_write(std::integral_constant<bool, kKqSrc>{}, lds, kKStride, kst, n0);
+  };
+  auto write_v = [&](__bf16* lds, int n0) {
+    stage_write(std::integral_constant<bool, kVqSrc>{}, lds, kVStride, vst, n0);
   };
 
   // ---- filling the ring: direct loads ----------------------------------------------------------
@@ -249,17 +364,45 @@ void attn_fwd(const AttnArgs a) {
   // twice.
   const int cache_lo = tile * kBlockM;
   const int cache_hi = kDecode || a.kc == nullptr ? 0 : min(cache_lo + kBlockM, a.cache_len);
+  // One 8-value chunk of cache row `key`: a bf16 copy, or (quantised tensor) 8 codes plus, from
+  // the row's first lane, the row scale.  The quantised form reduces over the row's 16 lanes, so
+  // every lane runs it; only the stores depend on `in`.
+  auto put_chunk = [&](auto quant_c, u32x4 x, void* base, int64_t ss, int64_t sb, int64_t sh,
+                       float* sbase, int64_t sss, int64_t ssb, int64_t ssh, int key, bool in) {
+    if constexpr (decltype(quant_c)::value) {
+      float sc;
+      const u32x2 c = quantize_row8(x, &sc);
+      if (in) {
+        *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(base) + b * sb + (int64_t)key * ss +
+                                  h * sh + ld_col) = c;
+        if ((tid & 15) == 0) sbase[b * ssb + (int64_t)key * sss + h * ssh] = sc;
+      }
+    } else if (in) {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + b * sb + (int64_t)key * ss +
+                                h * sh + ld_col) = x;
+    }
+  };
+  auto store_row = [&](int n0, int buf, int r) {
+    const int row = ld_row + kRowsPerPass * r;
+    const int key = n0 + row;
+    const bool in = key >= cache_lo && key < cache_hi;
+    if (!(kKq || kVq) && !in) return;
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds[buf][row * kKStride + st_col]);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds[buf][row * kVStride + st_col]);
+    put_chunk(std::integral_constant<bool, kKq>{}, kx, a.kc, a.kc_ss, a.kc_sb, a.kc_sh, a.kcs,
+              a.kcs_ss, a.kcs_sb, a.kcs_sh, key, in);
+    put_chunk(std::integral_constant<bool, kVq>{}, vx, a.vc, a.vc_ss, a.vc_sb, a.vc_sh, a.vcs,
+              a.vcs_ss, a.vcs_sb, a.vcs_sh, key, in);
+  };
   auto store_cache = [&](int n0, int buf) {
     if (kDecode || n0 >= cache_hi || n0 + kBlockN <= cache_lo) return;
+    if constexpr (kKq || kVq) {
+      // one row pass at a time: the quantiser's registers stay few next to the accumulators
+#pragma unroll 1
+      for (int r = 0; r < kChunksPerThread; ++r) store_row(n0, buf, r);
+    } else {
 #pragma unroll
-    for (int r = 0; r < kChunksPerThread; ++r) {
-      const int row = ld_row + kRowsPerPass * r;
-      const int key = n0 + row;
-      if (key < cache_lo || key >= cache_hi) continue;
-      const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds[buf][row * kKStride + st_col]);
-      const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds[buf][row * kVStride + st_col]);
-      *reinterpret_cast<u32x4*>(a.kc + b * a.kc_sb + (int64_t)key * a.kc_ss + h * a.kc_sh + ld_col) = kx;
-      *reinterpret_cast<u32x4*>(a.vc + b * a.vc_sb + (int64_t)key * a.vc_ss + h * a.vc_sh + ld_col) = vx;
+      for (int r = 0; r < kChunksPerThread; ++r) store_row(n0, buf, r);
     }
   };
 
@@ -303,8 +446,8 @@ void attn_fwd(const AttnArgs a) {
   } else {
     stage_k(0);
     stage_v(0);
-    stage_write(k_lds[0], kKStride, kst);
-    stage_write(v_lds[0], kVStride, vst);
+    write_k(k_lds[0], 0);
+    write_v(v_lds[0], 0);
     if (ntiles > 1) {
       stage_k(kBlockN);
       stage_v(kBlockN);
@@ -430,8 +573,8 @@ void attn_fwd(const AttnArgs a) {
       if (j + 2 < ntiles) dma_tile((j + 2) * kBlockN, cur);
     } else {
       if (j + 1 < ntiles) {
-        stage_write(k_lds[cur ^ 1], kKStride, kst);
-        stage_write(v_lds[cur ^ 1], kVStride, vst);
+        write_k(k_lds[cur ^ 1], n0 + kBlockN);
+        write_v(v_lds[cur ^ 1], n0 + kBlockN);
       }
       if (j + 2 < ntiles) {
         stage_k((j + 2) * kBlockN);
@@ -464,18 +607,29 @@ void attn_fwd(const AttnArgs a) {
   }
 }
 
+template <bool kDecode, bool kDirect>
+hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
+  switch (a.cache_fmt) {
+    case kCacheBf16:
+      hipLaunchKernelGGL((attn_fwd<kDecode, kDirect, kCacheBf16>), grid, dim3(kThreads), 0, stream, a);
+      break;
+    case kCacheFp8V:
+      hipLaunchKernelGGL((attn_fwd<kDecode, kDirect, kCacheFp8V>), grid, dim3(kThreads), 0, stream, a);
+      break;
+    case kCacheFp8KV:
+      hipLaunchKernelGGL((attn_fwd<kDecode, kDirect, kCacheFp8KV>), grid, dim3(kThreads), 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
-  hipLaunchKernelGGL((attn_fwd<false, true>), grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) { return launch<false, true>(a, stream); }
 
-hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
-  hipLaunchKernelGGL((attn_fwd<true, false>), grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) { return launch<true, false>(a, stream); }
 
 }  // namespace bca

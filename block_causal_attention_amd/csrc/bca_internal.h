@@ -24,14 +24,21 @@ constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup
 #endif
 constexpr int kBlockN = BCA_BLOCK_N;                 // keys per key tile (32 or 64)
 
+// Prefix-cache storage formats (values of bca_cache_format).
+constexpr int kCacheBf16 = 0;   // K and V bf16
+constexpr int kCacheFp8V = 1;   // V as E4M3 codes + fp32 scale per (token, head)
+constexpr int kCacheFp8KV = 2;  // K and V as E4M3 codes + scales
+
 // One attention launch.  Prefill and decode share the kernel: keys j < split come from (k, v),
-// keys j >= split from (k2, v2) at index j - split.  Prefill sets split = kv_len.
+// keys j >= split from (k2, v2) at index j - split.  Prefill sets split = kv_len.  k and v are
+// bf16, except in a decode over a quantised cache, where the quantised one holds uint8 codes
+// (strides in bytes) and kcs / vcs hold its scales.
 struct AttnArgs {
   const uint16_t* q;
   int64_t q_sb, q_ss, q_sh;
-  const uint16_t* k;
+  const void* k;
   int64_t k_sb, k_ss, k_sh;
-  const uint16_t* v;
+  const void* v;
   int64_t v_sb, v_ss, v_sh;
   const uint16_t* k2;
   int64_t k2_sb, k2_ss, k2_sh;
@@ -40,10 +47,11 @@ struct AttnArgs {
   float* o;
   int64_t o_sb, o_ss, o_sh;
   // Prefill only: prefix-K/V cache [B, cache_len, H, D] receiving K/V rows [0, cache_len), or
-  // NULL.  The workgroup of query tile t writes rows [t kBlockM, (t + 1) kBlockM) of it.
-  uint16_t* kc;
+  // NULL.  The workgroup of query tile t writes rows [t kBlockM, (t + 1) kBlockM) of it.  In a
+  // quantised format the quantised tensor holds uint8 codes.
+  void* kc;
   int64_t kc_sb, kc_ss, kc_sh;
-  uint16_t* vc;
+  void* vc;
   int64_t vc_sb, vc_ss, vc_sh;
   int32_t cache_len;
   int32_t n_q;       // query rows per (batch, head): S for prefill, N for decode
@@ -58,6 +66,13 @@ struct AttnArgs {
   const int32_t* kv_full;
   const int32_t* kv_end;
   const int32_t* order;
+  // Scales [B, cache_len, H] of the quantised cache tensors: written by the prefill, read by the
+  // decode (NULL for a bf16 tensor).
+  float* kcs;
+  int64_t kcs_sb, kcs_ss, kcs_sh;
+  float* vcs;
+  int64_t vcs_sb, vcs_ss, vcs_sh;
+  int32_t cache_fmt;  // kCacheBf16 / kCacheFp8V / kCacheFp8KV
 };
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);

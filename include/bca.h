@@ -146,6 +146,61 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
                       const bca_tensor* v_cache, const bca_tensor* k_tgt,
                       const bca_tensor* v_tgt, const bca_tensor* o, void* stream);
 
+/*
+ * FP8 prefix cache (10100.com article, FP8 part: the prefix K/V cache may be stored as FP8 E4M3
+ * with one fp32 scale per token and attention head; quantising V alone keeps K exact, which the
+ * article finds the safer trade, and still saves about a quarter of the cache).
+ *
+ * Formats.  BCA_CACHE_BF16: K and V bf16 [B, P, H, D].  BCA_CACHE_FP8_V: K bf16, V quantised.
+ * BCA_CACHE_FP8_KV: both quantised.  A quantised tensor is a uint8 code tensor [B, P, H, D]
+ * (OCP E4M3FN: bias 7, largest finite 448, subnormals, no infinities, 0x7F/0xFF = NaN) plus an
+ * fp32 scale tensor [B, P, H].  For each (b, j, h) row x of D values:
+ *     amax  = max_d |x[d]|
+ *     scale = amax > 0 ? max(amax / 448, 2^-126) : 1          (fp32, correctly rounded)
+ *     inv   = 1 / scale                                        (fp32, correctly rounded)
+ *     code[d] = E4M3(x[d] * inv)   (fp32 product, then nearest E4M3 value, ties to even)
+ * and the value the decode uses is E4M3 value(code[d]) * scale, rounded to bf16.  Inputs must be
+ * finite.
+ *
+ * Layout rules on top of the general ones: code tensors follow the bf16 rules with 1-byte
+ * elements (data 16-byte aligned, strides non-negative multiples of 16); scale tensors are fp32
+ * with data 4-byte aligned and non-negative strides (stride_h is the element stride between
+ * heads).  A scale tensor that its format does not use is ignored (data may be NULL).
+ */
+typedef enum bca_cache_format {
+  BCA_CACHE_BF16 = 0,
+  BCA_CACHE_FP8_V = 1,
+  BCA_CACHE_FP8_KV = 2
+} bca_cache_format;
+
+typedef struct bca_kv_cache {
+  int32_t format;      /* a bca_cache_format */
+  bca_tensor k;        /* bf16 [B, P, H, D], or uint8 codes [B, P, H, D] for BCA_CACHE_FP8_KV */
+  bca_tensor v;        /* bf16 [B, P, H, D], or uint8 codes for BCA_CACHE_FP8_V / _FP8_KV */
+  bca_tensor k_scale;  /* fp32 [B, P, H]: used by BCA_CACHE_FP8_KV */
+  bca_tensor v_scale;  /* fp32 [B, P, H]: used by BCA_CACHE_FP8_V and BCA_CACHE_FP8_KV */
+} bca_kv_cache;
+
+/*
+ * bca_prefill_ex -- bca_prefill with the prefix cache given as a descriptor of any format (NULL:
+ * no cache).  The attention itself always uses the bf16 k and v; only the stored cache is
+ * quantised, by the rule above, in the same kernel that reads those rows.  Ownership, errors and
+ * the other arguments are those of bca_prefill; an unknown format is BCA_ERR_ARG.
+ */
+bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                          const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
+                          const bca_tensor* o, const bca_kv_cache* cache, void* stream);
+
+/*
+ * bca_decode_ex -- bca_decode reading the prefix from a cache of any format.  Quantised rows are
+ * dequantised on their way into the kernel's on-chip tiles (value * scale, rounded to bf16);
+ * nothing is written back.  cache may be NULL only when the plan's prefix_len is 0.
+ */
+bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                         const bca_tensor* q_tgt, const bca_kv_cache* cache,
+                         const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
+                         void* stream);
+
 /* Static name of a status code ("BCA_OK", ...); "unknown status" for other values. */
 const char* bca_status_str(bca_status status);
 

@@ -161,3 +161,97 @@ def test_python_shim_rejects_bad_shapes_without_gpu():
     x = torch.zeros((1, 10, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         bca.prefill(p, x, x, x)  # S != plan's S
+
+
+def test_cache_descriptor_layout_matches_header(tmp_path):
+    """ctypes' bca_kv_cache / bca_tensor / bca_plan_info match the C compiler's layout."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "bca.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(bca_kv_cache),\n'
+        "         offsetof(bca_kv_cache, k), offsetof(bca_kv_cache, v),\n"
+        "         offsetof(bca_kv_cache, k_scale), offsetof(bca_kv_cache, v_scale),\n"
+        "         sizeof(bca_tensor), sizeof(bca_plan_info));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    C = _lib.BcaKvCache
+    want = [ctypes.sizeof(C), C.k.offset, C.v.offset, C.k_scale.offset, C.v_scale.offset,
+            ctypes.sizeof(_lib.BcaTensor), ctypes.sizeof(_lib.BcaPlanInfo)]
+    assert got == want
+
+
+def _cache(fmt, k=None, v=None, ks=None, vs=None):
+    c = _lib.BcaKvCache()
+    c.format = fmt
+    c.k, c.v = k or _t(), v or _t()
+    c.k_scale = ks or _lib.BcaTensor(0x20000, 4096, 32, 1)
+    c.v_scale = vs or _lib.BcaTensor(0x30000, 4096, 32, 1)
+    return c
+
+
+def test_fp8_cache_validation_before_any_device_work():
+    p = plan_host(W.TINY.block_ids())
+    h = p.handle
+    lib = _lib.load()
+    r = ctypes.byref
+
+    def pre(c, D=128):
+        return lib.bca_prefill_ex(h, 1, 2, D, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
+                                  None if c is None else r(c), None)
+
+    def dec(c, D=128):
+        return lib.bca_decode_ex(h, 1, 2, D, 0.0, r(_t()), None if c is None else r(c), r(_t()),
+                                 r(_t()), r(_t()), None)
+
+    err = lambda: lib.bca_last_error()
+    assert pre(_cache(3)) == _lib.BCA_ERR_ARG and b"unknown format" in err()
+    assert pre(_cache(-1)) == _lib.BCA_ERR_ARG
+    assert pre(_cache(2, k=_t(ss=4104))) == _lib.BCA_ERR_ARG        # codes: stride not x16
+    assert b"multiples of 16" in err()
+    assert pre(_cache(0, k=_t(ss=4104))) == _lib.BCA_ERR_ARG        # bf16: stride not x8
+    assert pre(_cache(1, v=_t(ptr=0x10008))) == _lib.BCA_ERR_ARG    # codes misaligned
+    assert pre(_cache(1, vs=_lib.BcaTensor(0x30002, 0, 1, 1))) == _lib.BCA_ERR_ARG
+    assert b"4-byte" in err()
+    assert pre(_cache(1, vs=_lib.BcaTensor(0, 0, 1, 1))) == _lib.BCA_ERR_ARG
+    assert pre(_cache(2, ks=_lib.BcaTensor(0x20000, 0, -1, 1))) == _lib.BCA_ERR_ARG
+    assert pre(_cache(2, k=_t(ss=1 << 24))) == _lib.BCA_ERR_ARG     # 32-bit row offsets
+    # scales a format does not use are ignored: reaches the host-only check
+    unused = _lib.BcaTensor(0, 0, 0, 0)
+    assert pre(_cache(0, ks=unused, vs=unused)) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in err()
+    assert pre(_cache(1, ks=unused)) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in err()
+    assert pre(_cache(2)) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in err()
+    assert pre(None) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in err()
+    assert pre(_cache(2), D=64) == _lib.BCA_ERR_UNSUPPORTED
+    assert dec(None) == _lib.BCA_ERR_ARG and b"cache" in err()       # P > 0 needs a cache
+    assert dec(_cache(7)) == _lib.BCA_ERR_ARG and b"unknown format" in err()
+    assert dec(_cache(2, vs=_lib.BcaTensor(0x30001, 0, 1, 1))) == _lib.BCA_ERR_ARG
+    assert dec(_cache(2)) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in err()
+    assert dec(_cache(2), D=256) == _lib.BCA_ERR_UNSUPPORTED
+    # the plain entry points are the bf16 format of the same calls
+    assert call_decode(h, kc=_t(ss=4100)) == _lib.BCA_ERR_ARG
+    p0 = plan_host(np.zeros(50, np.int32))                            # P = 0: no cache needed
+    assert lib.bca_decode_ex(p0.handle, 1, 2, 128, 0.0, r(_t()), None, r(_t()), r(_t()), r(_t()),
+                             None) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in err()
+
+
+def test_python_kv_cache_shapes_without_gpu():
+    torch = pytest.importorskip("torch")
+    p = plan_host(W.TINY.block_ids())
+    c = bca.KVCache.empty(p, 2, 3, bca.KVCache.FP8_V, device="cpu")
+    assert c.k.dtype == torch.bfloat16 and c.v.dtype == torch.uint8
+    assert c.k_scale is None and tuple(c.v_scale.shape) == (2, 82, 3)
+    assert c.nbytes() == 2 * 82 * 3 * (128 * 2 + 128 + 4)
+    kv = bca.KVCache.empty(p, 1, 2, bca.KVCache.FP8_KV, device="cpu")
+    assert kv.k.dtype == torch.uint8 and kv.k_scale is not None
+    with pytest.raises(ValueError):
+        bca.KVCache(5, c.k, c.v)
