@@ -27,7 +27,8 @@
 // while tile j is computed.  Two ways to fill the ring (template parameter kDirect):
 //   register staging (decode): 16-byte global loads into VGPRs, written to LDS one tile later;
 //                 the per-row cache/target source choice stays in registers;
-//   direct (prefill): global_load_lds_dwordx4 writes each wave's 1 KB straight into LDS.
+//   direct (prefill): buffer_load_dwordx4 ... lds writes each wave's 1 KB straight into LDS,
+//                 with a fixed per-lane offset and the tile's position in the descriptor.
 // Either way LDS rows are unpadded with an XOR swizzle of their 16-byte chunks (below) that keeps
 // the K reads and the transposed V reads free of bank conflicts.
 #include <type_traits>
@@ -66,6 +67,9 @@ constexpr int kDmaInstr = kDmaRowsPerWave / 4;                       // direct: 
 // fp32 overflow.  A lane's tile sum above kRescaleBound is what sends a wave to the exact path.
 constexpr float kRescaleThreshold = 16.0f;
 constexpr float kRescaleBound = 65536.0f;
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format; range-checked
+// against num_records with stride 0).
+constexpr int kBufferWord3 = 0x00020000;
 static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
 static_assert(kBlockN * kHeadDim / 8 % kThreads == 0, "whole 16-byte chunks per thread");
 static_assert(kDmaRowsPerWave % 16 == 0, "direct loads: each wave fills whole 16-row swizzle periods");
@@ -312,8 +316,7 @@ void attn_fwd(const AttnArgs a) {
   // ---- filling the ring: direct loads ----------------------------------------------------------
   // Wave w fills tile rows [w kDmaRowsPerWave, (w + 1) kDmaRowsPerWave), 4 rows per instruction:
   // lane L writes LDS chunk L % 16 of row L / 16 of the instruction's 4-row group, so it fetches
-  // logical chunk (L % 16) ^ swz(row) of that key.  Keys >= kv_end fetch row kv_end - 1 instead
-  // (always masked and finite).
+  // logical chunk (L % 16) ^ swz(row) of that key.
   // The common case (whole tile from one source, nothing past kv_end) adds a tile-uniform base
   // to per-lane offsets; a tile straddling the cache/target split or the end resolves each row.
   const int dma_r = lane >> 4;
@@ -322,7 +325,34 @@ void attn_fwd(const AttnArgs a) {
   // swz(row) for row = dma_row0 + 4 i: (row & 3) = dma_r, ((row >> 2) & 3) = i & 3 because each
   // wave's first row is a multiple of 16.
   auto dma_col = [&](int i) { return 8 * (dma_p ^ ((dma_r << 2) | (i & 3))); };
+  // Prefill: buffer loads.  A lane's byte offset inside a tile is fixed (row and swizzled chunk),
+  // the tile's first key moves the descriptor base (scalar work only), and the descriptor ends
+  // at the last key row of the sequence, so rows past it read as zero: those keys lie at or past
+  // every row's limit and are masked.
+  uint32_t dma_koff[kDmaInstr], dma_voff[kDmaInstr];
+#pragma unroll
+  for (int i = 0; i < kDmaInstr; ++i) {
+    const uint32_t row = (uint32_t)(dma_row0 + 4 * i), col = (uint32_t)dma_col(i);
+    dma_koff[i] = (row * (uint32_t)a.k_ss + col) * 2u;
+    dma_voff[i] = (row * (uint32_t)a.v_ss + col) * 2u;
+  }
+  auto dma_rsrc = [&](const uint16_t* base, int64_t ss, int n0) {
+    const int64_t bytes = ((int64_t)(a.kv_len - 1 - n0) * ss + kHeadDim) * 2;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)n0 * ss), (short)0,
+                                             (int)(uint32_t)bytes, kBufferWord3);
+  };
   auto dma_tile = [&](int n0, int buf) {
+    if constexpr (!kDecode) {
+      const __amdgpu_buffer_rsrc_t kr = dma_rsrc(k_base, a.k_ss, n0);
+      const __amdgpu_buffer_rsrc_t vr = dma_rsrc(v_base, a.v_ss, n0);
+#pragma unroll
+      for (int i = 0; i < kDmaInstr; ++i) {
+        const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds[buf][dst], 16, dma_koff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds[buf][dst], 16, dma_voff[i], 0, 0, 0);
+      }
+      return;
+    }
     const bool in_end = n0 + kBlockN <= kv_end;
     const bool src1 = !kDecode || n0 + kBlockN <= a.split;
     const bool src2 = kDecode && n0 >= a.split;
@@ -332,13 +362,7 @@ void attn_fwd(const AttnArgs a) {
       const int col = dma_col(i);
       const uint16_t* kp;
       const uint16_t* vp;
-      if (!kDecode) {
-        // One source: clamp the key (a no-op except on the last tile) and address it with a
-        // 32-bit element offset; the host keeps seq_len * stride below 2^31 and stride below 2^24.
-        const uint32_t key = (uint32_t)min(n0 + row, kv_end - 1);
-        kp = k_base + (key * (uint32_t)a.k_ss + (uint32_t)col);
-        vp = v_base + (key * (uint32_t)a.v_ss + (uint32_t)col);
-      } else if (in_end && src1) {
+      if (in_end && src1) {
         kp = k_base + (int64_t)(n0 + row) * a.k_ss + col;
         vp = v_base + (int64_t)(n0 + row) * a.v_ss + col;
       } else if (in_end && src2) {
@@ -396,6 +420,9 @@ void attn_fwd(const AttnArgs a) {
   };
   auto store_cache = [&](int n0, int buf) {
     if (kDecode || n0 >= cache_hi || n0 + kBlockN <= cache_lo) return;
+    // n0 made opaque: otherwise the compiler keeps this rare store's row pointers live across
+    // the whole loop and advances them every tile
+    asm volatile("" : "+s"(n0));
     if constexpr (kKq || kVq) {
       // one row pass at a time: the quantiser's registers stay few next to the accumulators
 #pragma unroll 1
@@ -424,6 +451,35 @@ void attn_fwd(const AttnArgs a) {
     const int col = 32 * d + tr_col;
     return row * kVStride + (kSwizzle ? 8 * ((col >> 3) ^ swz(row)) + (col & 7) : col);
   };
+  // The same offsets computed once.  Key block kb (K) and 16-row group kc (V) only add constants
+  // (swz(row) depends on row bits 0..3, and those do not change with kb or kc), which fold into
+  // the reads' immediate offsets.  In a swizzled tile the chunk index is not additive, so each
+  // MFMA step c (K) and each (row half hi, column block d) pair (V) keeps its own offset; the
+  // asm barrier stops the compiler from re-deriving them inside the loop.
+  int koff[8], voff[2][4];
+  if constexpr (kSwizzle) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      koff[c] = k_addr(0, c);
+      asm volatile("" : "+v"(koff[c]));
+    }
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        voff[hi][d] = v_addr(0, d, hi);
+        asm volatile("" : "+v"(voff[hi][d]));
+      }
+  } else {
+    int k0 = k_addr(0, 0), v0 = v_addr(0, 0, 0);
+    asm volatile("" : "+v"(k0), "+v"(v0));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) koff[c] = k0 + 16 * c;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) voff[hi][d] = v0 + 8 * hi * kVStride + 32 * d;
+  }
 
   f32x16 o[kQueryBlocks][4];
   float m_run[kQueryBlocks];   // running max of scale*log2(e)*s (same in both lane halves)
@@ -472,7 +528,8 @@ void attn_fwd(const AttnArgs a) {
       for (int qb = 0; qb < kQueryBlocks; ++qb) s[qb][kb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&k_lds[cur][k_addr(kb, c)]);
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(&k_lds[cur][koff[c] + 32 * kb * kKStride]);
 #pragma unroll
         for (int qb = 0; qb < kQueryBlocks; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[qb][kb], 0, 0, 0);
@@ -554,9 +611,9 @@ void attn_fwd(const AttnArgs a) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const bf16x4 lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&v_lds[cur][v_addr(kc, d, 0)]);
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&v_lds[cur][voff[0][d] + 16 * kc * kVStride]);
         const bf16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&v_lds[cur][v_addr(kc, d, 1)]);
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&v_lds[cur][voff[1][d] + 16 * kc * kVStride]);
         const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int qb = 0; qb < kQueryBlocks; ++qb)

@@ -25,6 +25,8 @@
  *    For K, V and the caches, stride_s must be below 2^24 and rows * stride_s below 2^31 (rows
  *    within one (batch, head) slice are addressed with 32-bit offsets); else BCA_ERR_ARG.
  *  - scale is the softmax multiplier of q.k; 0 selects 1/sqrt(D).  Negative or NaN -> ARG.
+ *  - Q, K and V must be finite: keys a row cannot see, inside a tile it computes, still enter the
+ *    P.V product with weight 0, so an infinite or NaN value there would reach the output.
  */
 #ifndef BCA_H
 #define BCA_H
