@@ -106,13 +106,18 @@ bca_status check_extent(const bca_tensor* t, const char* name, int64_t rows) {
   return BCA_OK;
 }
 
-// A scale tensor: fp32, 4-byte aligned, non-negative strides.
-bca_status check_scale_tensor(const bca_tensor* t, const char* name) {
+// A scale tensor: fp32, 4-byte aligned, non-negative strides; like K and V, rows of one (batch,
+// head) slice are addressed with 32-bit offsets.
+bca_status check_scale_tensor(const bca_tensor* t, const char* name, int64_t rows) {
   if (t->data == nullptr) return fail(BCA_ERR_ARG, std::string(name) + ": data is NULL");
   if (reinterpret_cast<uintptr_t>(t->data) % 4 != 0)
     return fail(BCA_ERR_ARG, std::string(name) + ": data is not 4-byte aligned");
   if (t->stride_b < 0 || t->stride_s < 0 || t->stride_h < 0)
     return fail(BCA_ERR_ARG, std::string(name) + ": strides must be non-negative");
+  if (t->stride_s >= (int64_t(1) << 24))
+    return fail(BCA_ERR_ARG, std::string(name) + ": stride_s must be below 2^24 elements");
+  if (rows * t->stride_s + 1 >= (int64_t(1) << 29))
+    return fail(BCA_ERR_ARG, std::string(name) + ": rows * stride_s must be below 2^29 elements");
   return BCA_OK;
 }
 
@@ -133,8 +138,8 @@ bca_status check_cache(const bca_kv_cache* c, int64_t rows) {
   if ((s = check_tensor(&c->v, vq ? "cache.v (codes)" : "cache.v", vq ? 1 : 2)) != BCA_OK) return s;
   if ((s = check_extent(&c->k, "cache.k", rows)) != BCA_OK) return s;
   if ((s = check_extent(&c->v, "cache.v", rows)) != BCA_OK) return s;
-  if (kq && (s = check_scale_tensor(&c->k_scale, "cache.k_scale")) != BCA_OK) return s;
-  if (vq && (s = check_scale_tensor(&c->v_scale, "cache.v_scale")) != BCA_OK) return s;
+  if (kq && (s = check_scale_tensor(&c->k_scale, "cache.k_scale", rows)) != BCA_OK) return s;
+  if (vq && (s = check_scale_tensor(&c->v_scale, "cache.v_scale", rows)) != BCA_OK) return s;
   return BCA_OK;
 }
 

@@ -214,19 +214,25 @@ void attn_fwd(const AttnArgs a) {
   // Loads one tile (K or V) starting at key n0; keys >= kv_end read as zero.  The common case
   // (whole tile from one source, nothing past kv_end) uses a tile-uniform base plus a per-thread
   // offset; only a tile that straddles the cache/target split or the end resolves each row.
+  // Whole tiles from one source use buffer loads: the lane's offset inside the tile is fixed, the
+  // row pass goes in the scalar offset and the tile's first row in the descriptor base.
+  auto tile_rsrc = [&](const void* first_row, int64_t row_bytes) {
+    const int64_t bytes = (int64_t)(kBlockN - 1) * row_bytes + kHeadDim * 2;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(first_row), (short)0,
+                                             (int)(uint32_t)bytes, kBufferWord3);
+  };
   auto stage_tile = [&](int n0, u32x4* st, const uint16_t* base1, int64_t ss1,
                         const uint16_t* base2, int64_t ss2) {
     const bool in_end = n0 + kBlockN <= kv_end;
-    if (in_end && (!kDecode || n0 + kBlockN <= a.split)) {
-      const uint16_t* t = base1 + (int64_t)(n0 + ld_row) * ss1 + ld_col;
+    const bool one_src1 = !kDecode || n0 + kBlockN <= a.split;
+    if (in_end && (one_src1 || n0 >= a.split)) {
+      const uint16_t* b = one_src1 ? base1 + (int64_t)n0 * ss1 : base2 + (int64_t)(n0 - a.split) * ss2;
+      const int64_t ss = one_src1 ? ss1 : ss2;
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(b, ss * 2);
+      const int voff = ((int)ld_row * (int)ss + ld_col) * 2;
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r)
-        st[r] = *reinterpret_cast<const u32x4*>(t + (int64_t)(kRowsPerPass * r) * ss1);
-    } else if (kDecode && in_end && n0 >= a.split) {
-      const uint16_t* t = base2 + (int64_t)(n0 - a.split + ld_row) * ss2 + ld_col;
-#pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r)
-        st[r] = *reinterpret_cast<const u32x4*>(t + (int64_t)(kRowsPerPass * r) * ss2);
+        st[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss * 2), 0);
     } else {
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r) {
@@ -251,13 +257,23 @@ void attn_fwd(const AttnArgs a) {
     };
     const bool in_end = n0 + kBlockN <= kv_end;
     if (in_end && n0 + kBlockN <= a.split) {
+      const __amdgpu_buffer_rsrc_t rc = tile_rsrc(base1 + (int64_t)n0 * ss1, ss1);
+      const __amdgpu_buffer_rsrc_t rsc = tile_rsrc(sbase1 + (int64_t)n0 * sss1, sss1 * 4);
+      const int voff = (int)ld_row * (int)ss1 + ld_col;
+      const int soff = (int)ld_row * (int)sss1 * 4;
 #pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r) st[r] = load1(n0 + ld_row + kRowsPerPass * r);
+      for (int r = 0; r < kChunksPerThread; ++r) {
+        const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(rc, voff, (int)(kRowsPerPass * r * ss1), 0);
+        const uint32_t sc =
+            __builtin_amdgcn_raw_buffer_load_b32(rsc, soff, (int)(kRowsPerPass * r * sss1 * 4), 0);
+        st[r] = u32x4{c[0], c[1], sc, 0u};
+      }
     } else if (in_end && n0 >= a.split) {
-      const uint16_t* t = base2 + (int64_t)(n0 - a.split + ld_row) * ss2 + ld_col;
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base2 + (int64_t)(n0 - a.split) * ss2, ss2 * 2);
+      const int voff = ((int)ld_row * (int)ss2 + ld_col) * 2;
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r)
-        st[r] = *reinterpret_cast<const u32x4*>(t + (int64_t)(kRowsPerPass * r) * ss2);
+        st[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss2 * 2), 0);
     } else {
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r) {

@@ -167,7 +167,8 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
  * Layout rules on top of the general ones: code tensors follow the bf16 rules with 1-byte
  * elements (data 16-byte aligned, strides non-negative multiples of 16); scale tensors are fp32
  * with data 4-byte aligned and non-negative strides (stride_h is the element stride between
- * heads).  A scale tensor that its format does not use is ignored (data may be NULL).
+ * heads), stride_s below 2^24 and P * stride_s below 2^29 elements.  A scale tensor that its
+ * format does not use is ignored (data may be NULL).
  */
 typedef enum bca_cache_format {
   BCA_CACHE_BF16 = 0,

@@ -225,6 +225,10 @@ def test_fp8_cache_validation_before_any_device_work():
     assert pre(_cache(1, vs=_lib.BcaTensor(0, 0, 1, 1))) == _lib.BCA_ERR_ARG
     assert pre(_cache(2, ks=_lib.BcaTensor(0x20000, 0, -1, 1))) == _lib.BCA_ERR_ARG
     assert pre(_cache(2, k=_t(ss=1 << 24))) == _lib.BCA_ERR_ARG     # 32-bit row offsets
+    assert pre(_cache(1, vs=_lib.BcaTensor(0x30000, 0, 1 << 24, 1))) == _lib.BCA_ERR_ARG
+    assert b"2^24" in err()
+    assert pre(_cache(1, vs=_lib.BcaTensor(0x30000, 0, 1 << 23, 1))) == _lib.BCA_ERR_ARG
+    assert b"2^29" in err()                                         # 82 rows * 2^23
     # scales a format does not use are ignored: reaches the host-only check
     unused = _lib.BcaTensor(0, 0, 0, 0)
     assert pre(_cache(0, ks=unused, vs=unused)) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in err()
