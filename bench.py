@@ -239,9 +239,9 @@ def main():
 
     # the dominant kernel: the call with the larger share of the step
     if dec_ms.mean() >= pre_ms.mean():
-        dom, key, achieved = "decode: attn_fwd<true, false, 0>, B=2", "decode_cfg_b2", dec_tf
+        dom, key, achieved = "decode: attn_decode<0> (bf16 cache), B=2", "decode_cfg_b2", dec_tf
     else:
-        dom, key, achieved = ("prefill: attn_fwd<false, true, 0> (writes the prefix cache), B=1",
+        dom, key, achieved = ("prefill: attn_prefill<0> (writes the bf16 prefix cache), B=1",
                               "prefill_b1", pre_tf)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -243,7 +243,7 @@ bca_status bca_plan_get_info(bca_plan_t plan, bca_plan_info* out) {
   out->useful_pairs = h.useful_pairs;
   out->n_segments = (int32_t)(h.segments.size() / 3);
   out->block_m = bca::kBlockM;
-  out->block_n = bca::kBlockN;
+  out->block_n = bca::kPrefillBlockN;
   out->n_qtiles = (int32_t)h.kv_end.size();
   out->decode_ok = h.decode_ok;
   out->host_only = plan->host_only;

@@ -9,7 +9,8 @@
 // row limit, and never loads the rest.  Decode is the same kernel with no mask except the tail.
 //
 // Work decomposition.  One workgroup = kWaves waves = one tile of kBlockM query rows of one
-// (batch, head); a wave owns kQueryBlocks blocks of 32 rows.  Per key tile of kBlockN keys:
+// (batch, head); a wave owns kQueryBlocks blocks of 32 rows.  Per key tile of kBlockN keys (32
+// in the prefill, which then fits 3 waves per SIMD; 64 in the decode, at 2 waves per SIMD):
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q rows held in VGPRs.
 //                 The accumulator gives each lane ONE query (lane % 32) and 16 keys, so the row
 //                 max is an in-lane reduction plus one swap of the two 32-lane halves.
@@ -48,20 +49,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef BCA_WAVES_PER_SIMD
-#define BCA_WAVES_PER_SIMD (kQueryBlocks == 1 ? 2 : 1)
+#ifndef BCA_DECODE_DIRECT
+#define BCA_DECODE_DIRECT 0
 #endif
 #ifndef BCA_STAGE_SWIZZLE
 #define BCA_STAGE_SWIZZLE 0
 #endif
 constexpr bool kStageSwizzle = BCA_STAGE_SWIZZLE;  // swizzled rows for the staging path too
 constexpr int kThreads = 64 * kWaves;
-constexpr int kOccupancy = BCA_WAVES_PER_SIMD;
-constexpr int kKeyBlocks = kBlockN / 32;  // 32-key MFMA blocks per key tile
-constexpr int kChunksPerThread = kBlockN * kHeadDim / 8 / kThreads;  // staging: 16 B chunks
-constexpr int kRowsPerPass = kThreads / 16;                          // staging: rows per pass
-constexpr int kDmaRowsPerWave = kBlockN / kWaves;                    // direct: rows per wave
-constexpr int kDmaInstr = kDmaRowsPerWave / 4;                       // direct: 4 rows per instr
+constexpr int kRowsPerPass = kThreads / 16;  // staging: rows per pass
 // A row's running max is raised only when its scores grew by more than kRescaleThreshold (log2
 // units), so p <= 2^16: exact in fp32, within bf16's exponent range, and l, O stay far below
 // fp32 overflow.  A lane's tile sum above kRescaleBound is what sends a wave to the exact path.
@@ -70,9 +66,6 @@ constexpr float kRescaleBound = 65536.0f;
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format; range-checked
 // against num_records with stride 0).
 constexpr int kBufferWord3 = 0x00020000;
-static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
-static_assert(kBlockN * kHeadDim / 8 % kThreads == 0, "whole 16-byte chunks per thread");
-static_assert(kDmaRowsPerWave % 16 == 0, "direct loads: each wave fills whole 16-row swizzle periods");
 
 // Swizzle of direct-load tiles: the 16-byte chunk c of tile row r sits at chunk c ^ swz(r).
 // swz is a bijection on each 16 consecutive rows (K reads: 16 lanes, 16 rows, one logical chunk
@@ -136,9 +129,18 @@ __device__ inline u32x2 quantize_row8(u32x4 x, float* scale_out) {
   return u32x2{(uint32_t)w0, (uint32_t)w1};
 }
 
-template <bool kDecode, bool kDirect, int kFmt>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOccupancy, kOccupancy)))
-void attn_fwd(const AttnArgs a) {
+// The body of both kernels.  kBlockN keys per key tile (32 or 64) is chosen per call, and so is
+// the occupancy (set on the kernels below): the prefill runs 32-key tiles at 3 waves per SIMD,
+// the decode 64-key tiles at 2.
+template <bool kDecode, bool kDirect, int kFmt, int kBlockN>
+__device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
+  constexpr int kKeyBlocks = kBlockN / 32;                            // 32-key MFMA blocks
+  constexpr int kChunksPerThread = kBlockN * kHeadDim / 8 / kThreads;  // staging: 16 B chunks
+  constexpr int kDmaRowsPerWave = kBlockN / kWaves;                    // direct: rows per wave
+  constexpr int kDmaInstr = kDmaRowsPerWave / 4;                       // direct: 4 rows per instr
+  static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
+  static_assert(kBlockN * kHeadDim / 8 % kThreads == 0, "whole 16-byte chunks per thread");
+  static_assert(kDmaRowsPerWave % 4 == 0, "direct loads: each wave fills whole 4-row groups");
   // The prefill stores a quantised cache; the decode reads one (its first key source).
   constexpr bool kKq = kFmt == kCacheFp8KV;
   constexpr bool kVq = kFmt != kCacheBf16;
@@ -338,20 +340,36 @@ void attn_fwd(const AttnArgs a) {
   const int dma_r = lane >> 4;
   const int dma_p = lane & 15;
   const int dma_row0 = wave * kDmaRowsPerWave + dma_r;  // + 4 i
-  // swz(row) for row = dma_row0 + 4 i: (row & 3) = dma_r, ((row >> 2) & 3) = i & 3 because each
-  // wave's first row is a multiple of 16.
-  auto dma_col = [&](int i) { return 8 * (dma_p ^ ((dma_r << 2) | (i & 3))); };
+  // swz(row) for row = dma_row0 + 4 i: (row & 3) = dma_r and ((row >> 2) & 3) =
+  // (first row of the wave's slice / 4 + i) & 3, since the slice starts at a multiple of 4.
+  auto dma_col = [&](int i) {
+    return 8 * (dma_p ^ ((dma_r << 2) | ((wave * (kDmaRowsPerWave / 4) + i) & 3)));
+  };
   // Prefill: buffer loads.  A lane's byte offset inside a tile is fixed (row and swizzled chunk),
   // the tile's first key moves the descriptor base (scalar work only), and the descriptor ends
   // at the last key row of the sequence, so rows past it read as zero: those keys lie at or past
   // every row's limit and are masked.
-  uint32_t dma_koff[kDmaInstr], dma_voff[kDmaInstr];
+  // (The decode also keeps offsets for its second source, the target.)
+  uint32_t dma_koff[kDmaInstr], dma_voff[kDmaInstr], dma_k2off[kDmaInstr], dma_v2off[kDmaInstr];
 #pragma unroll
   for (int i = 0; i < kDmaInstr; ++i) {
     const uint32_t row = (uint32_t)(dma_row0 + 4 * i), col = (uint32_t)dma_col(i);
     dma_koff[i] = (row * (uint32_t)a.k_ss + col) * 2u;
     dma_voff[i] = (row * (uint32_t)a.v_ss + col) * 2u;
+    dma_k2off[i] = (row * (uint32_t)a.k2_ss + col) * 2u;
+    dma_v2off[i] = (row * (uint32_t)a.v2_ss + col) * 2u;
   }
+  auto dma_whole = [&](const uint16_t* kb, int64_t kss, const uint16_t* vb, int64_t vss,
+                       const uint32_t* koff, const uint32_t* voff, int buf) {
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kb, kss * 2);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vb, vss * 2);
+#pragma unroll
+    for (int i = 0; i < kDmaInstr; ++i) {
+      const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds[buf][dst], 16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds[buf][dst], 16, voff[i], 0, 0, 0);
+    }
+  };
   auto dma_rsrc = [&](const uint16_t* base, int64_t ss, int n0) {
     const int64_t bytes = ((int64_t)(a.kv_len - 1 - n0) * ss + kHeadDim) * 2;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)n0 * ss), (short)0,
@@ -372,26 +390,28 @@ void attn_fwd(const AttnArgs a) {
     const bool in_end = n0 + kBlockN <= kv_end;
     const bool src1 = !kDecode || n0 + kBlockN <= a.split;
     const bool src2 = kDecode && n0 >= a.split;
+    // decode: whole tiles from one source through buffer loads, the rest row by row below
+    if (in_end && src1) {
+      dma_whole(k_base + (int64_t)n0 * a.k_ss, a.k_ss, v_base + (int64_t)n0 * a.v_ss, a.v_ss,
+                dma_koff, dma_voff, buf);
+      return;
+    }
+    if (in_end && src2) {
+      dma_whole(k2_base + (int64_t)(n0 - a.split) * a.k2_ss, a.k2_ss,
+                v2_base + (int64_t)(n0 - a.split) * a.v2_ss, a.v2_ss, dma_k2off, dma_v2off, buf);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kDmaInstr; ++i) {
       const int row = dma_row0 + 4 * i;
       const int col = dma_col(i);
-      const uint16_t* kp;
-      const uint16_t* vp;
-      if (in_end && src1) {
-        kp = k_base + (int64_t)(n0 + row) * a.k_ss + col;
-        vp = v_base + (int64_t)(n0 + row) * a.v_ss + col;
-      } else if (in_end && src2) {
-        kp = k2_base + (int64_t)(n0 - a.split + row) * a.k2_ss + col;
-        vp = v2_base + (int64_t)(n0 - a.split + row) * a.v2_ss + col;
-      } else {
-        const int key = min(n0 + row, kv_end - 1);
-        const bool first = !kDecode || key < a.split;
-        kp = (first ? k_base + (int64_t)key * a.k_ss
-                    : k2_base + (int64_t)(key - a.split) * a.k2_ss) + col;
-        vp = (first ? v_base + (int64_t)key * a.v_ss
-                    : v2_base + (int64_t)(key - a.split) * a.v2_ss) + col;
-      }
+      // keys past the end fetch row kv_end - 1 (masked, finite)
+      const int key = min(n0 + row, kv_end - 1);
+      const bool first = key < a.split;
+      const uint16_t* kp = (first ? k_base + (int64_t)key * a.k_ss
+                                  : k2_base + (int64_t)(key - a.split) * a.k2_ss) + col;
+      const uint16_t* vp = (first ? v_base + (int64_t)key * a.v_ss
+                                  : v2_base + (int64_t)(key - a.split) * a.v2_ss) + col;
       const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
       __builtin_amdgcn_global_load_lds((const void*)kp, (lds_void*)&k_lds[buf][dst], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)vp, (lds_void*)&v_lds[buf][dst], 16, 0, 0);
@@ -680,29 +700,59 @@ void attn_fwd(const AttnArgs a) {
   }
 }
 
-template <bool kDecode, bool kDirect>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+// Prefill: block-causal, direct-to-LDS fills, optional prefix-cache store in format kFmt.
+template <int kFmt>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
+void attn_prefill(const AttnArgs a) {
+  attn_fwd<false, true, kFmt, kPrefillBlockN>(a);
+}
+
+// Decode over [prefix cache in format kFmt ; target], register-staged fills.
+template <int kFmt>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd, kDecodeWavesPerSimd)))
+void attn_decode(const AttnArgs a) {
+  attn_fwd<true, false, kFmt, kDecodeBlockN>(a);
+}
+
+#if BCA_DECODE_DIRECT
+// Decode over a bf16 cache with direct-to-LDS fills (build option; measured slower).
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd, kDecodeWavesPerSimd)))
+void attn_decode_direct(const AttnArgs a) {
+  attn_fwd<true, true, kCacheBf16, kDecodeBlockN>(a);
+}
+#endif
+
+}  // namespace
+
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
   switch (a.cache_fmt) {
-    case kCacheBf16:
-      hipLaunchKernelGGL((attn_fwd<kDecode, kDirect, kCacheBf16>), grid, dim3(kThreads), 0, stream, a);
-      break;
-    case kCacheFp8V:
-      hipLaunchKernelGGL((attn_fwd<kDecode, kDirect, kCacheFp8V>), grid, dim3(kThreads), 0, stream, a);
-      break;
-    case kCacheFp8KV:
-      hipLaunchKernelGGL((attn_fwd<kDecode, kDirect, kCacheFp8KV>), grid, dim3(kThreads), 0, stream, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case kCacheBf16: hipLaunchKernelGGL(attn_prefill<kCacheBf16>, grid, dim3(kThreads), 0, stream, a); break;
+    case kCacheFp8V: hipLaunchKernelGGL(attn_prefill<kCacheFp8V>, grid, dim3(kThreads), 0, stream, a); break;
+    case kCacheFp8KV: hipLaunchKernelGGL(attn_prefill<kCacheFp8KV>, grid, dim3(kThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) { return launch<false, true>(a, stream); }
-
-hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) { return launch<true, false>(a, stream); }
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
+  switch (a.cache_fmt) {
+    case kCacheBf16:
+#if BCA_DECODE_DIRECT
+      hipLaunchKernelGGL(attn_decode_direct, grid, dim3(kThreads), 0, stream, a);
+#else
+      hipLaunchKernelGGL(attn_decode<kCacheBf16>, grid, dim3(kThreads), 0, stream, a);
+#endif
+      break;
+    case kCacheFp8V: hipLaunchKernelGGL(attn_decode<kCacheFp8V>, grid, dim3(kThreads), 0, stream, a); break;
+    case kCacheFp8KV: hipLaunchKernelGGL(attn_decode<kCacheFp8KV>, grid, dim3(kThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace bca

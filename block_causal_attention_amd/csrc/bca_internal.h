@@ -19,10 +19,25 @@ constexpr int kHeadDim = 128;  // the only head width the kernels are built for
 constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
 constexpr int kWaves = BCA_WAVES;
 constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup (= plan tile)
-#ifndef BCA_BLOCK_N
-#define BCA_BLOCK_N 64
+// Keys per key tile (32 or 64) and waves per SIMD, per call.  32-key tiles need fewer registers
+// and half the LDS, which lets the prefill run 3 waves per SIMD; the decode keeps 64-key tiles
+// at 2 waves per SIMD (measured faster for each).
+#ifndef BCA_PREFILL_BLOCK_N
+#define BCA_PREFILL_BLOCK_N 32
 #endif
-constexpr int kBlockN = BCA_BLOCK_N;                 // keys per key tile (32 or 64)
+#ifndef BCA_PREFILL_WAVES_PER_SIMD
+#define BCA_PREFILL_WAVES_PER_SIMD 3
+#endif
+#ifndef BCA_DECODE_BLOCK_N
+#define BCA_DECODE_BLOCK_N 64
+#endif
+#ifndef BCA_DECODE_WAVES_PER_SIMD
+#define BCA_DECODE_WAVES_PER_SIMD 2
+#endif
+constexpr int kPrefillBlockN = BCA_PREFILL_BLOCK_N;
+constexpr int kPrefillWavesPerSimd = BCA_PREFILL_WAVES_PER_SIMD;
+constexpr int kDecodeBlockN = BCA_DECODE_BLOCK_N;
+constexpr int kDecodeWavesPerSimd = BCA_DECODE_WAVES_PER_SIMD;
 
 // Prefix-cache storage formats (values of bca_cache_format).
 constexpr int kCacheBf16 = 0;   // K and V bf16
