@@ -390,3 +390,93 @@ def prefix_cache_bytes_fp8(layers: int, batch: int, prefix_len: int, heads: int,
     per_tensor_fp8 = prefix_len * heads * head_dim + prefix_len * heads * 4
     n_fp8 = {CACHE_BF16: 0, CACHE_FP8_V: 1, CACHE_FP8_KV: 2}[fmt]
     return layers * batch * ((2 - n_fp8) * per_tensor_bf16 + n_fp8 * per_tensor_fp8)
+
+
+# ----------------------------------------------------------------------------------------------
+# Q/K prologue: per-head RMS normalisation, then three-axis RoPE
+# ----------------------------------------------------------------------------------------------
+# [QI21-guide], "One stream for text, reference images, and the target": Q and K are normalised
+# per head (RMS over the 128 values of a head) before RoPE.  "Three-axis RoPE preserves image
+# geometry": the 128 dims of a head are split (16, 56, 56) over frame, height and width, base
+# 10,000; text positions advance one shared coordinate on all three axes; an image block keeps
+# the frame coordinate reached by the preceding text while its height and width coordinates form
+# a grid centred on zero; RoPE touches Q and K, not V.  Readings (the pages are silent on them):
+#   * RMS norm: y = x / sqrt(mean(x^2) + eps) * w with a learned weight w[128] shared by all
+#     heads; eps = 1e-6.
+#   * rotation pairs are adjacent dims (2i, 2i + 1) (the complex-number form); inside an axis
+#     section of width d_a, pair k turns by pos_axis * base^(-2k / d_a).
+#   * the shared counter c starts at 0; a text token gets (c, c, c) and advances c by one; an
+#     image block of H x W latents (row-major) gets (c, h - H//2, w - W//2) and then advances c by
+#     one, so adjacent blocks never share a frame coordinate.
+ROPE_SECTIONS = (16, 56, 56)
+ROPE_BASE = 10000.0
+RMS_EPS = 1e-6
+
+
+def rope_positions(ids: Sequence[int], image_hw: Optional[Sequence[Tuple[int, int]]] = None
+                   ) -> np.ndarray:
+    """int64 [S, 3] (frame, height, width) coordinates of every position.  image_hw lists
+    (H, W) of each image block in sequence order (default: square blocks)."""
+    ids = validate_block_ids(ids)
+    S = len(ids)
+    pos = np.zeros((S, 3), dtype=np.int64)
+    c = 0
+    img = 0
+    for a, e, bid in runs(ids, _validated=True):
+        if bid < 0:
+            for i in range(a, e):
+                pos[i] = (c, c, c)
+                c += 1
+            continue
+        n = e - a
+        if image_hw is None:
+            H = int(round(np.sqrt(n)))
+            W = H
+        else:
+            H, W = image_hw[img]
+        if H * W != n:
+            raise ValueError(f"image block of {n} positions is not {H} x {W}")
+        img += 1
+        for t in range(n):
+            h, w = divmod(t, W)
+            pos[a + t] = (c, h - H // 2, w - W // 2)
+        c += 1
+    return pos
+
+
+def rope_angles(pos: np.ndarray, base: float = ROPE_BASE,
+                sections: Sequence[int] = ROPE_SECTIONS) -> np.ndarray:
+    """float64 [S, 64] rotation angle of each adjacent pair of a head's 128 dims."""
+    pos = np.asarray(pos, dtype=np.float64)
+    cols = []
+    for axis, d in enumerate(sections):
+        k = np.arange(d // 2, dtype=np.float64)
+        inv = base ** (-2.0 * k / d)
+        cols.append(pos[:, axis:axis + 1] * inv[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """Per-head RMS normalisation over the last axis, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(w, dtype=np.float64)
+
+
+def apply_rope(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """Rotate adjacent pairs of x [B, S, H, D] by angles [S, D/2], in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.asarray(angles, dtype=np.float64)[None, :, None, :]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    c, s = np.cos(a), np.sin(a)
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def qk_prologue(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.ndarray, pos: np.ndarray,
+                eps: float = RMS_EPS, base: float = ROPE_BASE) -> Tuple[np.ndarray, np.ndarray]:
+    """(RoPE(RMSNorm(q) * wq), RoPE(RMSNorm(k) * wk)) in float64; pos is [S, 3]."""
+    ang = rope_angles(pos, base)
+    return apply_rope(rms_norm(q, wq, eps), ang), apply_rope(rms_norm(k, wk, eps), ang)
