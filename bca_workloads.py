@@ -134,3 +134,16 @@ def random_layout(rng: np.random.Generator, seq: int, p_text: float = 0.5,
         segs.append(("text" if rng.random() < p_text else "image", n))
         left -= n
     return block_ids_from_segments(segs)
+
+
+def prologue_inputs(seed: int, batch: int, seq: int, heads: int, head_dim: int = 128):
+    """Raw (pre-norm) Q and K as bf16 bits [B, S, H, D] with a spread of per-row scales, and
+    RMS-norm weights w_q, w_k float32 [D] near 1 (synthetic stand-ins for learned weights)."""
+    rng = np.random.default_rng(seed)
+    shape = (batch, seq, heads, head_dim)
+    row_scale = np.exp(rng.uniform(-2.0, 2.0, size=shape[:3] + (1,))).astype(np.float32)
+    q = rng.standard_normal(shape, dtype=np.float32) * row_scale
+    k = rng.standard_normal(shape, dtype=np.float32) * row_scale[:, :, ::-1]
+    wq = (1.0 + 0.1 * rng.standard_normal(head_dim)).astype(np.float32)
+    wk = (1.0 + 0.1 * rng.standard_normal(head_dim)).astype(np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), wq, wk

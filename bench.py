@@ -133,6 +133,39 @@ def fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od, flops_pre, flops_dec,
     return out
 
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published figure
+
+
+def prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev, iters=20):
+    """The Q/K prologue (per-head RMS norm + three-axis RoPE) on the prefill shape and on the
+    CFG target rows: ms per call and effective HBM GB/s.  Algorithmic bytes: Q and K read once
+    and written once (bf16), the table rows read once, the weights ignored (1 KB)."""
+    table = torch.from_numpy(bca.rope_table(bca.rope_positions(ids))).to(dev)
+    wq = torch.ones(HEAD_DIM, dtype=torch.float32, device=dev)
+    wk = torch.ones_like(wq)
+    out = {}
+    for name, B, rows, tab in (("prefill_b1", 1, S, table), ("target_b2", Bd, N, table[S - N:].contiguous())):
+        qb, kb, _, _ = W.prologue_inputs(7, B, rows, H)
+        q, k = to_dev(torch, qb, dev), to_dev(torch, kb, dev)
+        for _ in range(3):
+            bca.qk_prologue(q, k, wq, wk, tab, q_out=q, k_out=k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            bca.qk_prologue(q, k, wq, wk, tab, q_out=q, k_out=k)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        nbytes = 4 * B * rows * H * HEAD_DIM * 2 + rows * 64 * 2 * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"prologue {name}: {ms:.4f} ms, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
+        del q, k
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +280,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(key), "kernel": dom}
 
+    prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
     fp8 = None if args.no_fp8 else fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od,
                                                flops_pre, flops_dec, Bd, S, H, P, dev)
 
@@ -276,6 +310,7 @@ def main():
                    "useful_gflop": round(flops_dec / 1e9, 1)},
         "plan_ms": round(plan_ms, 3),
         "fp8_cache": fp8,
+        "qk_prologue": prologue,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

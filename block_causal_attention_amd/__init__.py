@@ -10,6 +10,9 @@ kernels.  PyTorch supplies device memory and the current stream.
     cache = KVCache.empty(plan, B, H, KVCache.FP8_V)    # FP8 prefix cache (bca_kv_cache)
     o = prefill_ex(plan, q, k, v, cache)
     o_t = decode_ex(plan, q_t, cache, k_t, v_t)
+
+    table = torch.from_numpy(rope_table(rope_positions(block_ids))).cuda()   # once per layout
+    qk_prologue(q, k, wq, wk, table, q_out=q, k_out=k)   # per-head RMS norm + 3-axis RoPE
 """
 from __future__ import annotations
 
@@ -22,7 +25,7 @@ from . import _lib
 from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
-           "plan_info"]
+           "plan_info", "rope_positions", "rope_table", "qk_prologue"]
 
 
 class BcaError(RuntimeError):
@@ -301,3 +304,67 @@ def decode_ex(plan: Plan, q, cache: Optional[KVCache], k, v, *, scale: Optional[
             ctypes.byref(_desc(v, "v", torch.bfloat16)),
             ctypes.byref(_desc(out, "out", torch.float32)), ctypes.c_void_p(stream)))
     return out
+
+
+def rope_positions(block_ids, image_hw=None) -> np.ndarray:
+    """(frame, height, width) of every position (bca_rope_positions): int32 [S, 3].  image_hw:
+    None (square image blocks) or a list of (H, W) per image block in sequence order."""
+    lib = _lib.load()
+    if hasattr(block_ids, "detach"):
+        block_ids = block_ids.detach().cpu().numpy()
+    ids = np.ascontiguousarray(np.asarray(block_ids, dtype=np.int64))
+    if ids.ndim != 1 or ids.size == 0:
+        raise ValueError("block ids must be a non-empty 1-D sequence")
+    ids32 = ids.astype(np.int32)
+    out = np.empty((ids32.size, 3), np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    hw = None
+    n_img = 0
+    if image_hw is not None:
+        hw = np.ascontiguousarray(np.asarray(image_hw, dtype=np.int32).reshape(-1, 2))
+        n_img = hw.shape[0]
+    _check(lib.bca_rope_positions(p(ids32), ids32.size, None if hw is None else p(hw), n_img,
+                                  p(out)))
+    return out
+
+
+def rope_table(pos, base: float = 10000.0) -> np.ndarray:
+    """{cos, sin} of every rotation pair at every position (bca_rope_table): float32
+    [S, 64, 2]."""
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int32).reshape(-1, 3))
+    out = np.empty((pos.shape[0], 64, 2), np.float32)
+    _check(_lib.load().bca_rope_table(pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      pos.shape[0], float(base),
+                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+    return out
+
+
+def qk_prologue(q, k, q_weight, k_weight, table, *, eps: float = 1e-6, q_out=None, k_out=None):
+    """Per-head RMS norm then three-axis RoPE of q and k (bca_qk_prologue).  q, k: bf16
+    [B, S, H, 128]; weights: fp32 [128]; table: fp32 [S, 64, 2] on the device.  Returns
+    (q_out, k_out); pass q_out=q, k_out=k to work in place."""
+    import torch
+
+    B, S, H, D = q.shape
+    if tuple(k.shape) != (B, S, H, D):
+        raise ValueError("q and k must share the shape [B, S, H, D]")
+    for name, t, shape in (("q_weight", q_weight, (D,)), ("k_weight", k_weight, (D,)),
+                           ("table", table, (S, 64, 2))):
+        if (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor {shape}")
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    for name, t in (("q_out", q_out), ("k_out", k_out)):
+        if tuple(t.shape) != (B, S, H, D):
+            raise ValueError(f"{name} has the wrong shape")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_qk_prologue(
+            B, S, H, D, float(eps), ctypes.byref(_desc(q, "q", torch.bfloat16)),
+            ctypes.byref(_desc(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc(q_out, "q_out", torch.bfloat16)),
+            ctypes.byref(_desc(k_out, "k_out", torch.bfloat16)), vp(q_weight), vp(k_weight),
+            vp(table), ctypes.c_void_p(stream)))
+    return q_out, k_out

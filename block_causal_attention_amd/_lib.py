@@ -21,7 +21,8 @@ BCA_CACHE_FP8_KV = 2
 
 # every symbol include/bca.h declares
 EXPORTED = ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export", "bca_prefill",
-            "bca_decode", "bca_prefill_ex", "bca_decode_ex", "bca_status_str", "bca_last_error")
+            "bca_decode", "bca_prefill_ex", "bca_decode_ex", "bca_rope_positions", "bca_rope_table",
+            "bca_qk_prologue", "bca_status_str", "bca_last_error")
 
 
 class BcaTensor(ctypes.Structure):
@@ -70,12 +71,18 @@ def load() -> ctypes.CDLL:
                                    ctypes.c_float, T, T, T, T, C, P]
     lib.bca_decode_ex.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_float, T, C, T, T, T, P]
+    f32p = ctypes.POINTER(ctypes.c_float)
+    lib.bca_rope_positions.argtypes = [i32p, ctypes.c_int64, i32p, ctypes.c_int32, i32p]
+    lib.bca_rope_table.argtypes = [i32p, ctypes.c_int64, ctypes.c_double, f32p]
+    lib.bca_qk_prologue.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_float, T, T, T, T, P, P, P, P]
     lib.bca_status_str.argtypes = [ctypes.c_int]
     lib.bca_status_str.restype = ctypes.c_char_p
     lib.bca_last_error.argtypes = []
     lib.bca_last_error.restype = ctypes.c_char_p
     for name in ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export",
-                 "bca_prefill", "bca_decode", "bca_prefill_ex", "bca_decode_ex"):
+                 "bca_prefill", "bca_decode", "bca_prefill_ex", "bca_decode_ex",
+                 "bca_rope_positions", "bca_rope_table", "bca_qk_prologue"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -170,6 +170,11 @@ bool grid_fits(int64_t tiles, int32_t B, int32_t H) {
 
 }  // namespace
 
+namespace bca {
+// Error reporting for the other host files of the library (same thread-local text).
+bca_status set_error(bca_status s, const std::string& msg) { return fail(s, msg); }
+}  // namespace bca
+
 extern "C" {
 
 const char* bca_status_str(bca_status s) {
@@ -402,6 +407,50 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
     return bca_decode_ex(plan, B, H, D, scale, q_tgt, nullptr, k_tgt, v_tgt, o, stream);
   const bca_kv_cache c = bf16_cache(k_cache, v_cache);
   return bca_decode_ex(plan, B, H, D, scale, q_tgt, &c, k_tgt, v_tgt, o, stream);
+}
+
+bca_status bca_qk_prologue(int32_t B, int64_t S, int32_t H, int32_t D, float eps,
+                           const bca_tensor* q, const bca_tensor* k, const bca_tensor* q_out,
+                           const bca_tensor* k_out, const float* q_weight, const float* k_weight,
+                           const float* rope_table, void* stream) {
+  if (B < 1 || H < 1 || S < 1) return fail(BCA_ERR_ARG, "B, S and H must be >= 1");
+  if (S > INT32_MAX) return fail(BCA_ERR_ARG, "S must be below 2^31");
+  if (D != bca::kHeadDim)
+    return fail(BCA_ERR_UNSUPPORTED, "head width " + std::to_string(D) + " (only 128 is built)");
+  if (!(eps >= 0.0f) || std::isinf(eps)) return fail(BCA_ERR_ARG, "eps must be finite and >= 0");
+  bca_status s;
+  if ((s = check_tensor(q, "q", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(k, "k", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(q_out, "q_out", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(k_out, "k_out", 2)) != BCA_OK) return s;
+  const void* vecs[3] = {q_weight, k_weight, rope_table};
+  const char* names[3] = {"q_weight", "k_weight", "rope_table"};
+  for (int i = 0; i < 3; ++i) {
+    if (vecs[i] == nullptr) return fail(BCA_ERR_ARG, std::string(names[i]) + " is NULL");
+    if (reinterpret_cast<uintptr_t>(vecs[i]) % 16 != 0)
+      return fail(BCA_ERR_ARG, std::string(names[i]) + " is not 16-byte aligned");
+  }
+  const int64_t rows = (int64_t)B * S * H;
+  if ((rows + 15) / 16 > (int64_t)UINT32_MAX) return fail(BCA_ERR_ARG, "B * S * H is too large");
+  bca::PrologueArgs a{};
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.q_sb = q->stride_b; a.q_ss = q->stride_s; a.q_sh = q->stride_h;
+  a.k = static_cast<const uint16_t*>(k->data);
+  a.k_sb = k->stride_b; a.k_ss = k->stride_s; a.k_sh = k->stride_h;
+  a.qo = static_cast<uint16_t*>(q_out->data);
+  a.qo_sb = q_out->stride_b; a.qo_ss = q_out->stride_s; a.qo_sh = q_out->stride_h;
+  a.ko = static_cast<uint16_t*>(k_out->data);
+  a.ko_sb = k_out->stride_b; a.ko_ss = k_out->stride_s; a.ko_sh = k_out->stride_h;
+  a.wq = q_weight;
+  a.wk = k_weight;
+  a.table = rope_table;
+  a.rows = rows;
+  a.seq = (int32_t)S;
+  a.heads = H;
+  a.eps = eps;
+  hipError_t e = bca::launch_prologue(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  return BCA_OK;
 }
 
 }  // extern "C"

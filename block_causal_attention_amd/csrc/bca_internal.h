@@ -90,7 +90,28 @@ struct AttnArgs {
   int32_t cache_fmt;  // kCacheBf16 / kCacheFp8V / kCacheFp8KV
 };
 
+// Q/K prologue: RMS-normalise each 128-value head row of q and k (weights wq, wk), rotate its
+// adjacent pairs by the position's angles (table [S][64][2] of {cos, sin}), store bf16.
+struct PrologueArgs {
+  const uint16_t* q;
+  int64_t q_sb, q_ss, q_sh;
+  const uint16_t* k;
+  int64_t k_sb, k_ss, k_sh;
+  uint16_t* qo;
+  int64_t qo_sb, qo_ss, qo_sh;
+  uint16_t* ko;
+  int64_t ko_sb, ko_ss, ko_sh;
+  const float* wq;
+  const float* wk;
+  const float* table;
+  int64_t rows;  // B * S * H head rows
+  int32_t seq;   // S
+  int32_t heads;
+  float eps;
+};
+
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace bca

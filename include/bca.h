@@ -204,6 +204,48 @@ bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float
                          const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
                          void* stream);
 
+/*
+ * Q/K prologue ("Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo": section
+ * "One stream for text, reference images, and the target" normalises Q and K per head before
+ * RoPE; section "Three-axis RoPE preserves image geometry" splits a head's 128 dims (16, 56, 56)
+ * over frame, height and width, base 10,000, advances text on all three axes together and gives
+ * an image the frame reached by preceding text plus a height/width grid centred on zero).
+ * Readings where the pages are silent: a counter c starts at 0; a text token takes (c, c, c) and
+ * advances c; an H x W image block (row-major) takes (c, h - H/2, w - W/2) and then advances c by
+ * one; rotation pairs are adjacent dims (2i, 2i + 1); pair k of an axis of width d turns by
+ * pos * base^(-2k/d); the RMS norm is x / sqrt(mean(x^2) + eps) * w with w[128] shared by heads.
+ */
+
+/*
+ * bca_rope_positions -- HOST.  pos_out[3 * i + {0, 1, 2}] = (frame, height, width) of position i
+ * of the block-id layout (same ids and rules as bca_plan).  image_hw: NULL (every image block is
+ * square) or [n_images][2] = (H, W) of each image block in sequence order; H * W must equal the
+ * block's length (else BCA_ERR_ARG).  pos_out: HOST int32 [seq_len][3].
+ */
+bca_status bca_rope_positions(const int32_t* block_ids, int64_t seq_len, const int32_t* image_hw,
+                              int32_t n_images, int32_t* pos_out);
+
+/*
+ * bca_rope_table -- HOST.  table_out[(i * 64 + p) * 2 + {0, 1}] = {cos, sin} of the angle of
+ * rotation pair p at position i (pairs 0..7 frame, 8..35 height, 36..63 width), computed in
+ * double and rounded to float.  pos: HOST int32 [n][3]; table_out: HOST float [n][64][2].  Copy
+ * it to the device for bca_qk_prologue; one table serves every layer, head and step.
+ */
+bca_status bca_rope_table(const int32_t* pos, int64_t n, double base, float* table_out);
+
+/*
+ * bca_qk_prologue -- q_out = RoPE(RMSNorm(q) * q_weight) and k_out likewise, for S positions:
+ * q, k, q_out, k_out bf16 [B, S, H, D] (D = 128; bca_tensor rules); q_weight, k_weight DEVICE
+ * fp32 [D]; rope_table DEVICE fp32 [S][64][2] from bca_rope_table for the same S positions (for a
+ * cached step, the table rows of the target).  eps >= 0.  fp32 arithmetic, bf16 (RNE) output.
+ * q_out may be q itself (in place), and k_out k; other overlaps are not allowed.  The prefill
+ * then stores the post-RoPE K it is given in the prefix cache.  Enqueues one kernel on stream.
+ */
+bca_status bca_qk_prologue(int32_t B, int64_t S, int32_t H, int32_t D, float eps,
+                           const bca_tensor* q, const bca_tensor* k, const bca_tensor* q_out,
+                           const bca_tensor* k_out, const float* q_weight, const float* k_weight,
+                           const float* rope_table, void* stream);
+
 /* Static name of a status code ("BCA_OK", ...); "unknown status" for other values. */
 const char* bca_status_str(bca_status status);
 
