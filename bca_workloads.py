@@ -147,3 +147,35 @@ def prologue_inputs(seed: int, batch: int, seq: int, heads: int, head_dim: int =
     wq = (1.0 + 0.1 * rng.standard_normal(head_dim)).astype(np.float32)
     wk = (1.0 + 0.1 * rng.standard_normal(head_dim)).astype(np.float32)
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), wq, wk
+
+
+def neo_like_batch(seed: int, batch: int, max_seq_len: int, image_tokens: int):
+    """A batch shaped like a row of the NEO-Unify mixed-mask prefill table (batch, max_seq_len,
+    image_token_num): mostly text; the first sequence has max_seq_len positions and the others a
+    length drawn from [max_seq_len / 2, max_seq_len]; image_tokens image positions in total, in
+    spans of 16..64 tokens placed at random inside the text.  Returns (ids_list, lengths)."""
+    rng = np.random.default_rng(seed)
+    lengths = [max_seq_len] + [int(rng.integers(max_seq_len // 2, max_seq_len + 1))
+                               for _ in range(batch - 1)]
+    spans: List[List[int]] = [[] for _ in range(batch)]
+    left = image_tokens
+    while left > 0:
+        n = int(min(left, rng.integers(16, 65)))
+        spans[int(rng.integers(0, batch))].append(n)
+        left -= n
+    ids_list = []
+    for b, L in enumerate(lengths):
+        segs: List[Tuple[str, int]] = []
+        imgs = spans[b]
+        text = L - sum(imgs)
+        cuts = np.sort(rng.integers(0, text + 1, size=len(imgs)))
+        prev = 0
+        for c, n in zip(cuts, imgs):
+            if c > prev:
+                segs.append(("text", int(c - prev)))
+            segs.append(("image", n))
+            prev = int(c)
+        if text > prev:
+            segs.append(("text", text - prev))
+        ids_list.append(block_ids_from_segments(segs))
+    return ids_list, lengths

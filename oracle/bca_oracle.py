@@ -480,3 +480,33 @@ def qk_prologue(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.ndarray, po
     """(RoPE(RMSNorm(q) * wq), RoPE(RMSNorm(k) * wk)) in float64; pos is [S, 3]."""
     ang = rope_angles(pos, base)
     return apply_rope(rms_norm(q, wq, eps), ang), apply_rope(rms_norm(k, wk, eps), ang)
+
+
+# ----------------------------------------------------------------------------------------------
+# Batches of sequences with different lengths and layouts (varlen)
+# ----------------------------------------------------------------------------------------------
+# [QI21-guide], "Block-causal attention is the cache-enabling boundary" (padded keys are ignored)
+# and [infra], "NEO-Unify 多模态 Prefill 的注意力" (batches of prompts up to 64k positions with few
+# image tokens): every sequence of a batch is attended on its own, under its own block-id layout;
+# rows of one sequence never see keys of another or padding.  Sequences sit along one row axis of
+# [rows, H, D] tensors, sequence b at rows [row_start[b], row_start[b] + len_b).
+def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, ids_list: Sequence[Sequence[int]],
+                     row_start: Sequence[int], scale: Optional[float] = None,
+                     rows_of: Optional[Dict[int, np.ndarray]] = None,
+                     heads: Optional[Sequence[int]] = None) -> Dict[int, np.ndarray]:
+    """{b: float64 [len_b or len(rows_of[b]), H', D]} for each sequence b; q, k, v are [R, H, D].
+    rows_of[b] (optional) selects local query rows of sequence b, heads a subset of heads."""
+    out = {}
+    for b, ids in enumerate(ids_list):
+        a = int(row_start[b])
+        n = len(ids)
+        sl = slice(a, a + n)
+        rows = None if rows_of is None else rows_of.get(b)
+        out[b] = attention(q[None, sl], k[None, sl], v[None, sl], ids, scale=scale, rows=rows,
+                           heads=heads)[0]
+    return out
+
+
+def packed_row_starts(lengths: Sequence[int]) -> np.ndarray:
+    """Row of each sequence when the batch is packed without gaps."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))[:-1]])
