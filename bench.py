@@ -166,6 +166,34 @@ def prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev, iters=20):
     return out
 
 
+def varlen_timing(torch, bca, W, dev, H, iters=10):
+    """Batch-of-sequences prefill on a NEO-Unify-table-like batch (batch 16, max_seq_len 8,192,
+    246 image tokens; heads and width are not on that page: 32 x 128 assumed), packed."""
+    ids_list, lens = W.neo_like_batch(16, 16, 8192, 246)
+    plan = bca.Plan.varlen(ids_list)
+    R = int(sum(lens))
+    q, k, v = (to_dev(torch, x[0], dev) for x in W.qkv(17, 1, R, H))
+    o = torch.empty((R, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        bca.prefill_varlen(plan, q, k, v, out=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        bca.prefill_varlen(plan, q, k, v, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    flops = 4.0 * HEAD_DIM * H * plan.info.useful_pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"varlen NEO-like batch 16 x <=8192 ({R} rows): {ms:.3f} ms = {tf:.1f} TFLOP/s")
+    plan.free()
+    return {"workload": "16 sequences, max 8192 positions (lengths 4096..8192), 246 image tokens, "
+                        f"H={H}, packed ({R} rows)",
+            "ms": round(ms, 4), "useful_tflops": round(tf, 2),
+            "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "useful_gflop": round(flops / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +309,7 @@ def main():
                 "traffic": measured_traffic(key), "kernel": dom}
 
     prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
+    varlen = varlen_timing(torch, bca, W, dev, H)
     fp8 = None if args.no_fp8 else fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od,
                                                flops_pre, flops_dec, Bd, S, H, P, dev)
 
@@ -311,6 +340,7 @@ def main():
         "plan_ms": round(plan_ms, 3),
         "fp8_cache": fp8,
         "qk_prologue": prologue,
+        "varlen_prefill": varlen,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

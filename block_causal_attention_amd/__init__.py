@@ -25,7 +25,7 @@ from . import _lib
 from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
-           "plan_info", "rope_positions", "rope_table", "qk_prologue"]
+           "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen"]
 
 
 class BcaError(RuntimeError):
@@ -61,6 +61,32 @@ class Plan:
         ptr = ids32.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if ids32.size else None
         _check(lib.bca_plan(ptr, ids32.size, flags, ctypes.byref(self._h)))
         self.info = plan_info(self)
+
+    @classmethod
+    def varlen(cls, ids_list, row_start=None, host_only: bool = False) -> "Plan":
+        """Plan for a batch of sequences with their own layouts (bca_plan_varlen): sequence b
+        at rows [row_start[b], row_start[b] + len_b) (default: packed)."""
+        lib = _lib.load()
+        seqs = [np.asarray(i.detach().cpu().numpy() if hasattr(i, "detach") else i, np.int64)
+                for i in ids_list]
+        if not seqs or any(x.ndim != 1 for x in seqs):
+            raise ValueError("ids_list must be a non-empty list of 1-D id vectors")
+        flat = np.ascontiguousarray(np.concatenate(seqs).astype(np.int32))
+        lens = np.ascontiguousarray(np.array([x.size for x in seqs], dtype=np.int64))
+        starts = None
+        if row_start is not None:
+            starts = np.ascontiguousarray(np.asarray(row_start, dtype=np.int64))
+            if starts.shape != lens.shape:
+                raise ValueError("row_start needs one entry per sequence")
+        self = cls.__new__(cls)
+        self._h = ctypes.c_void_p()
+        flags = _lib.BCA_PLAN_HOST_ONLY if host_only else 0
+        i64 = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        ptr = flat.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if flat.size else None
+        _check(lib.bca_plan_varlen(ptr, i64(lens), i64(starts), lens.size, flags,
+                                   ctypes.byref(self._h)))
+        self.info = plan_info(self)
+        return self
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -368,3 +394,40 @@ def qk_prologue(q, k, q_weight, k_weight, table, *, eps: float = 1e-6, q_out=Non
             ctypes.byref(_desc(k_out, "k_out", torch.bfloat16)), vp(q_weight), vp(k_weight),
             vp(table), ctypes.c_void_p(stream)))
     return q_out, k_out
+
+
+def _desc3(t, name: str, dtype) -> BcaTensor:
+    """bca_tensor of a 3-D [rows, H, D] torch tensor with D contiguous (stride_b unused)."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 3 or not t.is_cuda:
+        raise ValueError(f"{name} must be a 3-D [rows, H, D] device tensor")
+    ss, sh, sd = t.stride()
+    if sd != 1 and t.shape[2] > 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return BcaTensor(t.data_ptr(), 0, ss, sh)
+
+
+def prefill_varlen(plan: Plan, q, k, v, *, scale: Optional[float] = None, out=None):
+    """Block-causal prefill of every sequence of a varlen plan (bca_prefill_varlen).  q, k, v:
+    bf16 [rows, H, D]; returns fp32 [rows, H, D] (rows outside the sequences left untouched:
+    zero when `out` is not given)."""
+    import torch
+
+    R, H, D = q.shape
+    if tuple(k.shape) != (R, H, D) or tuple(v.shape) != (R, H, D):
+        raise ValueError("q, k, v must share the shape [rows, H, D]")
+    if R < plan.info.rows:
+        raise ValueError(f"the plan spans {plan.info.rows} rows, the tensors {R}")
+    if out is None:
+        out = torch.zeros((R, H, D), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (R, H, D):
+        raise ValueError("out has the wrong shape")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_prefill_varlen(
+            plan.handle, H, D, _scale(scale), ctypes.byref(_desc3(q, "q", torch.bfloat16)),
+            ctypes.byref(_desc3(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc3(v, "v", torch.bfloat16)),
+            ctypes.byref(_desc3(out, "out", torch.float32)), ctypes.c_void_p(stream)))
+    return out

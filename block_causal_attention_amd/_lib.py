@@ -22,7 +22,8 @@ BCA_CACHE_FP8_KV = 2
 # every symbol include/bca.h declares
 EXPORTED = ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export", "bca_prefill",
             "bca_decode", "bca_prefill_ex", "bca_decode_ex", "bca_rope_positions", "bca_rope_table",
-            "bca_qk_prologue", "bca_status_str", "bca_last_error")
+            "bca_qk_prologue", "bca_plan_varlen", "bca_prefill_varlen", "bca_status_str",
+            "bca_last_error")
 
 
 class BcaTensor(ctypes.Structure):
@@ -40,7 +41,9 @@ class BcaPlanInfo(ctypes.Structure):
                 ("target_len", ctypes.c_int64), ("useful_pairs", ctypes.c_int64),
                 ("n_segments", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("block_n", ctypes.c_int32), ("n_qtiles", ctypes.c_int32),
-                ("decode_ok", ctypes.c_int32), ("host_only", ctypes.c_int32)]
+                ("decode_ok", ctypes.c_int32), ("host_only", ctypes.c_int32),
+                ("n_sequences", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rows", ctypes.c_int64)]
 
 
 _lib = None
@@ -76,13 +79,19 @@ def load() -> ctypes.CDLL:
     lib.bca_rope_table.argtypes = [i32p, ctypes.c_int64, ctypes.c_double, f32p]
     lib.bca_qk_prologue.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_float, T, T, T, T, P, P, P, P]
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.bca_plan_varlen.argtypes = [i32p, i64p, i64p, ctypes.c_int32, ctypes.c_uint32,
+                                    ctypes.POINTER(P)]
+    lib.bca_prefill_varlen.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                       T, T, T, T, P]
     lib.bca_status_str.argtypes = [ctypes.c_int]
     lib.bca_status_str.restype = ctypes.c_char_p
     lib.bca_last_error.argtypes = []
     lib.bca_last_error.restype = ctypes.c_char_p
     for name in ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export",
                  "bca_prefill", "bca_decode", "bca_prefill_ex", "bca_decode_ex",
-                 "bca_rope_positions", "bca_rope_table", "bca_qk_prologue"):
+                 "bca_rope_positions", "bca_rope_table", "bca_qk_prologue", "bca_plan_varlen",
+                 "bca_prefill_varlen"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

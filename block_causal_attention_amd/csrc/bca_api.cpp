@@ -18,6 +18,7 @@ struct bca_plan_s {
   int32_t* d_kv_full = nullptr;
   int32_t* d_kv_end = nullptr;
   int32_t* d_order = nullptr;
+  int32_t* d_tiles = nullptr;
 };
 
 namespace {
@@ -35,7 +36,7 @@ bca_status hip_fail(hipError_t e, const char* what) {
 }
 
 void free_device(bca_plan_s* p) {
-  int32_t** arrs[] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end, &p->d_order};
+  int32_t** arrs[] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end, &p->d_order, &p->d_tiles};
   for (int32_t** a : arrs) {
     if (*a) (void)hipFree(*a);
     *a = nullptr;
@@ -192,7 +193,13 @@ const char* bca_status_str(bca_status s) {
 
 const char* bca_last_error(void) { return g_last_error.c_str(); }
 
-bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, bca_plan_t* out) {
+}  // extern "C"
+
+namespace {
+
+// Builds the host plan with `build`, then (unless host-only) uploads its arrays.
+template <typename Build>
+bca_status make_plan(uint32_t flags, bca_plan_t* out, Build build) {
   if (out == nullptr) return fail(BCA_ERR_ARG, "out is NULL");
   *out = nullptr;
   if (flags & ~(uint32_t)BCA_PLAN_HOST_ONLY) return fail(BCA_ERR_ARG, "unknown plan flags");
@@ -201,7 +208,7 @@ bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, b
   std::string err;
   int rc;
   try {
-    rc = bca::build_host_plan(block_ids, seq_len, bca::kBlockM, &p->host, &err);
+    rc = build(&p->host, &err);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(BCA_ERR_ALLOC, "host allocation of the plan failed");
@@ -222,6 +229,7 @@ bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, b
     if (s == BCA_OK) s = upload(p->host.kv_full, &p->d_kv_full);
     if (s == BCA_OK) s = upload(p->host.kv_end, &p->d_kv_end);
     if (s == BCA_OK) s = upload(p->host.order, &p->d_order);
+    if (s == BCA_OK) s = upload(p->host.tiles, &p->d_tiles);
     if (s != BCA_OK) {
       free_device(p);
       delete p;
@@ -230,6 +238,24 @@ bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, b
   }
   *out = p;
   return BCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, bca_plan_t* out) {
+  return make_plan(flags, out, [&](bca::HostPlan* h, std::string* err) {
+    return bca::build_host_plan(block_ids, seq_len, bca::kBlockM, h, err);
+  });
+}
+
+bca_status bca_plan_varlen(const int32_t* block_ids, const int64_t* lengths,
+                           const int64_t* row_start, int32_t batch, uint32_t flags,
+                           bca_plan_t* out) {
+  return make_plan(flags, out, [&](bca::HostPlan* h, std::string* err) {
+    return bca::build_varlen_plan(block_ids, lengths, row_start, batch, bca::kBlockM, h, err);
+  });
 }
 
 bca_status bca_plan_free(bca_plan_t plan) {
@@ -252,6 +278,9 @@ bca_status bca_plan_get_info(bca_plan_t plan, bca_plan_info* out) {
   out->n_qtiles = (int32_t)h.kv_end.size();
   out->decode_ok = h.decode_ok;
   out->host_only = plan->host_only;
+  out->n_sequences = h.n_sequences;
+  out->reserved = 0;
+  out->rows = h.rows;
   return BCA_OK;
 }
 
@@ -281,6 +310,8 @@ bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, floa
   if ((s = check_tensor(v, "v", 2)) != BCA_OK) return s;
   if ((s = check_tensor(o, "o", 4)) != BCA_OK) return s;
   const bca::HostPlan& hp = plan->host;
+  if (hp.n_sequences != 1)
+    return fail(BCA_ERR_ARG, "plan holds several sequences: launch it with bca_prefill_varlen");
   const bool store = cache != nullptr && hp.prefix_len > 0;  // P = 0: nothing to store
   if (cache != nullptr && (s = check_format(cache)) != BCA_OK) return s;
   if (store && (s = check_cache(cache, hp.prefix_len)) != BCA_OK) return s;
@@ -314,6 +345,7 @@ bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, floa
   a.kv_full = plan->d_kv_full;
   a.kv_end = plan->d_kv_end;
   a.order = plan->d_order;
+  a.tiles = plan->d_tiles;
   a.cache_fmt = BCA_CACHE_BF16;
   if (store) {
     a.kc = cache->k.data;
@@ -337,6 +369,54 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   if (k_cache == nullptr) return bca_prefill_ex(plan, B, H, D, scale, q, k, v, o, nullptr, stream);
   const bca_kv_cache c = bf16_cache(k_cache, v_cache);
   return bca_prefill_ex(plan, B, H, D, scale, q, k, v, o, &c, stream);
+}
+
+bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
+                              const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
+                              const bca_tensor* o, void* stream) {
+  float scale_log2 = 0.0f;
+  bca_status s = check_common(plan, 1, H, D, scale, &scale_log2);
+  if (s != BCA_OK) return s;
+  if ((s = check_tensor(q, "q", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(k, "k", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(v, "v", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(o, "o", 4)) != BCA_OK) return s;
+  const bca::HostPlan& hp = plan->host;
+  if ((s = check_extent(k, "k", hp.rows)) != BCA_OK) return s;
+  if ((s = check_extent(v, "v", hp.rows)) != BCA_OK) return s;
+  const int64_t nt = (int64_t)hp.kv_end.size();
+  if (!grid_fits(nt, 1, H)) return fail(BCA_ERR_ARG, "H * query tiles exceeds 2^31 - 1");
+  if ((s = check_launchable(plan)) != BCA_OK) return s;
+
+  bca::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.q_ss = q->stride_s; a.q_sh = q->stride_h;
+  a.k = k->data;
+  a.k_ss = k->stride_s; a.k_sh = k->stride_h;
+  a.v = v->data;
+  a.v_ss = v->stride_s; a.v_sh = v->stride_h;
+  a.k2 = static_cast<const uint16_t*>(k->data);
+  a.k2_ss = a.k_ss; a.k2_sh = a.k_sh;
+  a.v2 = static_cast<const uint16_t*>(v->data);
+  a.v2_ss = a.v_ss; a.v2_sh = a.v_sh;
+  a.o = static_cast<float*>(o->data);
+  a.o_ss = o->stride_s; a.o_sh = o->stride_h;
+  a.n_q = (int32_t)hp.rows;
+  a.kv_len = (int32_t)hp.rows;
+  a.split = (int32_t)hp.rows;
+  a.heads = H;
+  a.batch = 1;
+  a.n_qtiles = (int32_t)nt;
+  a.scale_log2 = scale_log2;
+  a.row_limit = plan->d_row_limit;
+  a.kv_full = plan->d_kv_full;
+  a.kv_end = plan->d_kv_end;
+  a.order = plan->d_order;
+  a.tiles = plan->d_tiles;
+  a.cache_fmt = BCA_CACHE_BF16;
+  hipError_t e = bca::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return BCA_OK;
 }
 
 bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,

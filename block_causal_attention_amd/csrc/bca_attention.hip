@@ -175,8 +175,20 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const int b = bh / a.heads;
   const int h = bh - b * a.heads;
   const int tile = kDecode ? slot : a.order[slot];
-  const int kv_end = kDecode ? a.kv_len : a.kv_end[tile];
-  const int kv_full = kDecode ? a.kv_len : a.kv_full[tile];
+  // The tile's sequence (prefill plans may hold several): its first tensor row, the tile's first
+  // local row, its length and where its row limits start.  Rows, keys and limits below are local
+  // to the sequence; the decode has one sequence of n_q query rows over kv_len keys.
+  int seq_row0 = 0, row0 = tile * kBlockM, n_rows = a.n_q, rl_off = 0;
+  int kv_end = a.kv_len, kv_full = a.kv_len;
+  if constexpr (!kDecode) {
+    const int32_t* td = a.tiles + tile * kTileInts;
+    seq_row0 = td[0];
+    row0 = td[1];
+    n_rows = td[2];
+    rl_off = td[3];
+    kv_full = td[4];
+    kv_end = td[5];
+  }
   const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
@@ -185,11 +197,11 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   bf16x8 qreg[kQueryBlocks][8];
 #pragma unroll
   for (int qb = 0; qb < kQueryBlocks; ++qb) {
-    const int row = tile * kBlockM + (wave * kQueryBlocks + qb) * 32 + qn;
-    row_ok[qb] = row < a.n_q;
-    lim[qb] = kDecode ? a.kv_len : a.row_limit[row_ok[qb] ? row : a.n_q - 1];
-    const uint16_t* qp =
-        a.q + b * a.q_sb + (int64_t)(row_ok[qb] ? row : 0) * a.q_ss + h * a.q_sh + 8 * half;
+    const int row = row0 + (wave * kQueryBlocks + qb) * 32 + qn;
+    row_ok[qb] = row < n_rows;
+    lim[qb] = kDecode ? a.kv_len : a.row_limit[rl_off + (row_ok[qb] ? row : n_rows - 1)];
+    const uint16_t* qp = a.q + b * a.q_sb + (int64_t)(seq_row0 + (row_ok[qb] ? row : 0)) * a.q_ss +
+                         h * a.q_sh + 8 * half;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const u32x4 x =
@@ -199,8 +211,10 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   }
 
   // first key source: bf16, or (decode over a quantised cache) code bytes plus row scales
-  const uint16_t* k_base = static_cast<const uint16_t*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const uint16_t* v_base = static_cast<const uint16_t*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const uint16_t* k_base =
+      static_cast<const uint16_t*>(a.k) + b * a.k_sb + h * a.k_sh + (int64_t)seq_row0 * a.k_ss;
+  const uint16_t* v_base =
+      static_cast<const uint16_t*>(a.v) + b * a.v_sb + h * a.v_sh + (int64_t)seq_row0 * a.v_ss;
   const uint8_t* k8_base = static_cast<const uint8_t*>(a.k) + b * a.k_sb + h * a.k_sh;
   const uint8_t* v8_base = static_cast<const uint8_t*>(a.v) + b * a.v_sb + h * a.v_sh;
   const float* ks_base = kKqSrc ? a.kcs + b * a.kcs_sb + h * a.kcs_sh : nullptr;
@@ -371,7 +385,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     }
   };
   auto dma_rsrc = [&](const uint16_t* base, int64_t ss, int n0) {
-    const int64_t bytes = ((int64_t)(a.kv_len - 1 - n0) * ss + kHeadDim) * 2;
+    const int64_t bytes = ((int64_t)(n_rows - 1 - n0) * ss + kHeadDim) * 2;  // to the sequence end
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)n0 * ss), (short)0,
                                              (int)(uint32_t)bytes, kBufferWord3);
   };
@@ -422,7 +436,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // This workgroup owns cache rows [cache_lo, cache_hi), which lie inside its own diagonal key
   // tiles; they are copied out of the LDS tile while it is resident, so no K/V row is fetched
   // twice.
-  const int cache_lo = tile * kBlockM;
+  const int cache_lo = row0;
   const int cache_hi = kDecode || a.kc == nullptr ? 0 : min(cache_lo + kBlockM, a.cache_len);
   // One 8-value chunk of cache row `key`: a bf16 copy, or (quantised tensor) 8 codes plus, from
   // the row's first lane, the row scale.  The quantised form reduces over the row's 16 lanes, so
@@ -686,8 +700,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   for (int qb = 0; qb < kQueryBlocks; ++qb) {
     const float inv = 1.0f / halves_sum(l_part[qb]);
     if (row_ok[qb]) {
-      const int row = tile * kBlockM + (wave * kQueryBlocks + qb) * 32 + qn;
-      float* op = a.o + b * a.o_sb + (int64_t)row * a.o_ss + h * a.o_sh + 4 * half;
+      const int row = row0 + (wave * kQueryBlocks + qb) * 32 + qn;
+      float* op = a.o + b * a.o_sb + (int64_t)(seq_row0 + row) * a.o_ss + h * a.o_sh + 4 * half;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll

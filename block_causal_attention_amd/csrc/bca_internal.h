@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "bca_plan.h"  // kTileInts: ints per prefill tile descriptor
+
 namespace bca {
 
 // Tile shape.  A wave owns kQueryBlocks blocks of 32 query rows; a workgroup has kWaves waves.
@@ -81,6 +83,10 @@ struct AttnArgs {
   const int32_t* kv_full;
   const int32_t* kv_end;
   const int32_t* order;
+  // Prefill only: per query tile {sequence's first tensor row, first local row, sequence length,
+  // offset of the sequence's row limits, kv_full, kv_end, 0, 0}; row_limit and the key bounds
+  // are local to the sequence.
+  const int32_t* tiles;
   // Scales [B, cache_len, H] of the quantised cache tensors: written by the prefill, read by the
   // decode (NULL for a bf16 tensor).
   float* kcs;

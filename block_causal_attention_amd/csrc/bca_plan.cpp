@@ -82,6 +82,95 @@ int build_host_plan(const int32_t* ids, int64_t S, int block_m, HostPlan* out, s
   p.target_len = S - p.prefix_len;
   p.decode_ok = p.segments[3 * (nseg - 1) + 2] >= 0 ? 1 : 0;
   p.block_m = block_m;
+  p.tiles.assign((size_t)nt * kTileInts, 0);
+  for (int64_t t = 0; t < nt; ++t) {
+    int32_t* d = &p.tiles[(size_t)t * kTileInts];
+    d[1] = (int32_t)(t * block_m);
+    d[2] = (int32_t)S;
+    d[4] = p.kv_full[(size_t)t];
+    d[5] = p.kv_end[(size_t)t];
+  }
+  p.rows = S;
+  *out = std::move(p);
+  return kPlanOk;
+}
+
+int build_varlen_plan(const int32_t* ids, const int64_t* lengths, const int64_t* row_start,
+                      int32_t batch, int block_m, HostPlan* out, std::string* err) {
+  if (ids == nullptr || lengths == nullptr) {
+    *err = "block_ids or lengths is NULL";
+    return kPlanErrArg;
+  }
+  if (batch < 1) {
+    *err = "batch must be >= 1";
+    return kPlanErrArg;
+  }
+  std::vector<int64_t> start((size_t)batch);
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (lengths[b] < 1 || lengths[b] > INT32_MAX) {
+      *err = "sequence " + std::to_string(b) + " has length " + std::to_string(lengths[b]);
+      return kPlanErrArg;
+    }
+    start[(size_t)b] = row_start ? row_start[b] : total;
+    total += lengths[b];
+    if (start[(size_t)b] < 0 || start[(size_t)b] + lengths[b] > INT32_MAX) {
+      *err = "sequence " + std::to_string(b) + " starts at row " +
+             std::to_string(start[(size_t)b]) + ", outside [0, 2^31 - length]";
+      return kPlanErrArg;
+    }
+  }
+  if (total > INT32_MAX) {
+    *err = "the sequences hold more than 2^31 - 1 positions";
+    return kPlanErrArg;
+  }
+  // rows of different sequences must not overlap
+  std::vector<int32_t> by_start((size_t)batch);
+  std::iota(by_start.begin(), by_start.end(), 0);
+  std::sort(by_start.begin(), by_start.end(),
+            [&](int32_t x, int32_t y) { return start[(size_t)x] < start[(size_t)y]; });
+  for (int32_t i = 1; i < batch; ++i) {
+    const int32_t x = by_start[(size_t)i - 1], y = by_start[(size_t)i];
+    if (start[(size_t)x] + lengths[x] > start[(size_t)y]) {
+      *err = "sequences " + std::to_string(x) + " and " + std::to_string(y) + " overlap";
+      return kPlanErrArg;
+    }
+  }
+  HostPlan p;
+  p.block_m = block_m;
+  p.n_sequences = batch;
+  int64_t off = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    HostPlan one;
+    const int rc = build_host_plan(ids + off, lengths[b], block_m, &one, err);
+    if (rc != kPlanOk) {
+      *err = "sequence " + std::to_string(b) + ": " + *err;
+      return rc;
+    }
+    for (size_t r = 0; r < one.segments.size(); ++r) p.segments.push_back(one.segments[r]);
+    p.row_limit.insert(p.row_limit.end(), one.row_limit.begin(), one.row_limit.end());
+    const size_t nt = one.kv_end.size();
+    for (size_t t = 0; t < nt; ++t) {
+      p.kv_full.push_back(one.kv_full[t]);
+      p.kv_end.push_back(one.kv_end[t]);
+      const int32_t d[kTileInts] = {(int32_t)start[(size_t)b], (int32_t)(t * block_m),
+                                    (int32_t)lengths[b], (int32_t)off, one.kv_full[t],
+                                    one.kv_end[t], 0, 0};
+      p.tiles.insert(p.tiles.end(), d, d + kTileInts);
+    }
+    p.useful_pairs += one.useful_pairs;
+    p.seq_len += lengths[b];
+    p.rows = std::max<int64_t>(p.rows, start[(size_t)b] + lengths[b]);
+    off += lengths[b];
+  }
+  // heavy-first over the whole batch: kv_end descending, ties by tile index ascending
+  p.order.resize(p.kv_end.size());
+  std::iota(p.order.begin(), p.order.end(), 0);
+  std::stable_sort(p.order.begin(), p.order.end(),
+                   [&](int32_t x, int32_t y) { return p.kv_end[(size_t)x] > p.kv_end[(size_t)y]; });
+  p.prefix_len = 0;
+  p.target_len = 0;
+  p.decode_ok = 0;
   *out = std::move(p);
   return kPlanOk;
 }

@@ -21,9 +21,23 @@ struct HostPlan {
   std::vector<int32_t> kv_full;    // per query tile: min hi over its rows
   std::vector<int32_t> kv_end;     // per query tile: max hi over its rows
   std::vector<int32_t> order;      // query tiles by kv_end descending, ties by index
+  // Per query tile, kTileInts ints: tensor row of its sequence's first position, first local row
+  // of the tile, positions of the sequence, offset of the sequence's limits in row_limit,
+  // kv_full, kv_end (local key indices), two zeros.
+  std::vector<int32_t> tiles;
+  int32_t n_sequences = 1;
+  int64_t rows = 0;                // tensor rows spanned: max(row_start + length)
 };
+
+constexpr int kTileInts = 8;
 
 // Returns kPlanOk, kPlanErrArg or kPlanErrBlockIds (with *err set).
 int build_host_plan(const int32_t* ids, int64_t S, int block_m, HostPlan* out, std::string* err);
+
+// A batch of independent sequences: ids holds the sequences' id vectors one after another,
+// lengths[b] their lengths and row_start[b] (NULL: packed) the tensor row where sequence b
+// starts.  Rows of different sequences must not overlap.  Tiles never cross a sequence.
+int build_varlen_plan(const int32_t* ids, const int64_t* lengths, const int64_t* row_start,
+                      int32_t batch, int block_m, HostPlan* out, std::string* err);
 
 }  // namespace bca

@@ -69,6 +69,9 @@ typedef struct bca_plan_info {
   int32_t n_qtiles;     /* ceil(S / block_m) */
   int32_t decode_ok;    /* 1 when the last block is an image block (the target) */
   int32_t host_only;    /* 1 when built with BCA_PLAN_HOST_ONLY (no device arrays) */
+  int32_t n_sequences;  /* 1, or the batch of a bca_plan_varlen plan */
+  int32_t reserved;     /* 0 */
+  int64_t rows;         /* tensor rows the plan spans: S, or max(row_start + length) */
 } bca_plan_info;
 
 enum { BCA_PLAN_HOST_ONLY = 1u };
@@ -96,6 +99,26 @@ enum { BCA_PLAN_HOST_ONLY = 1u };
  */
 bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, bca_plan_t* out);
 
+/*
+ * bca_plan_varlen -- a plan for a batch of independent sequences with their own lengths and
+ * block-id layouts (the guide's section "Block-causal attention is the cache-enabling boundary":
+ * padded keys are ignored; the SenseNova-U1 infrastructure document, section "NEO-Unify 多模态
+ * Prefill 的注意力": batches of long, mostly-text prompts).  Each sequence is planned as by
+ * bca_plan; its query tiles never cross into another sequence, and all tiles of the batch run in
+ * one heavy-first order.
+ *
+ * block_ids: HOST [sum(lengths)], the sequences' id vectors one after another (ids are local to
+ * a sequence).  lengths: HOST int64 [batch], each >= 1.  row_start: HOST int64 [batch], the row of
+ * the [rows, H, D] tensors where sequence b starts, or NULL for packed (row_start[b] =
+ * sum_{c<b} lengths[c]).  Rows of different sequences must not overlap; gaps (padding) are
+ * allowed and never read or written.  Such a plan has n_sequences = batch, prefix_len = 0 and
+ * decode_ok = 0; it is launched with bca_prefill_varlen.  Exported arrays are concatenated over
+ * the sequences (segments and row_limit local to each sequence).
+ */
+bca_status bca_plan_varlen(const int32_t* block_ids, const int64_t* lengths,
+                           const int64_t* row_start, int32_t batch, uint32_t flags,
+                           bca_plan_t* out);
+
 /* Releases a plan (host and device arrays).  NULL is accepted and ignored. */
 bca_status bca_plan_free(bca_plan_t plan);
 
@@ -112,7 +135,8 @@ bca_status bca_plan_export(bca_plan_t plan, int32_t* segments, int32_t* row_limi
                            int32_t* kv_full, int32_t* kv_end, int32_t* order);
 
 /*
- * bca_prefill -- block-causal attention over the whole joint sequence (the first denoising step,
+ * bca_prefill -- block-causal attention over the whole joint sequence (single-sequence plans;
+ * a plan with n_sequences > 1 is BCA_ERR_ARG here) (the first denoising step,
  * "extract" in the guide's section "Timestep-zero conditioning makes the prefix invariant"),
  * optionally storing the per-layer prefix K/V cache.
  *
@@ -128,6 +152,17 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
                        const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
                        const bca_tensor* o, const bca_tensor* k_cache, const bca_tensor* v_cache,
                        void* stream);
+
+/*
+ * bca_prefill_varlen -- block-causal attention of every sequence of a bca_plan_varlen plan (or of
+ * the single sequence of a bca_plan plan): q, k, v bf16 and o fp32 are [rows, H, D] tensors
+ * (bca_tensor with stride_b unused), sequence b at rows [row_start[b], row_start[b] + len_b).
+ * Output rows of a sequence are fully written; rows outside every sequence are not touched.  No
+ * prefix cache is stored.  D must be 128.
+ */
+bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
+                              const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
+                              const bca_tensor* o, void* stream);
 
 /*
  * bca_decode -- a cached denoising step: the N target queries attend with no mask to the

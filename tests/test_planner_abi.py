@@ -259,3 +259,61 @@ def test_python_kv_cache_shapes_without_gpu():
     assert kv.k.dtype == torch.uint8 and kv.k_scale is not None
     with pytest.raises(ValueError):
         bca.KVCache(5, c.k, c.v)
+
+
+def varlen_batch(seed, n_seq, max_len):
+    rng = np.random.default_rng(seed)
+    return [W.random_layout(rng, int(rng.integers(1, max_len)), p_text=float(rng.random()),
+                            max_seg=int(rng.integers(1, 200))) for _ in range(n_seq)]
+
+
+@pytest.mark.parametrize("seed", [41, 42, 43])
+def test_varlen_plan_bit_exact(seed):
+    ids_list = varlen_batch(seed, int(np.random.default_rng(seed).integers(1, 9)), 900)
+    p = bca.Plan.varlen(ids_list, host_only=True)
+    info = p.info
+    got = p.export()
+    want = [O.plan_from_mask(ids, info.block_m) for ids in ids_list]
+    for key in ("row_limit", "kv_full", "kv_end"):
+        assert np.array_equal(got[key].astype(np.int64), np.concatenate([w[key] for w in want]))
+    segs = np.concatenate([w["segments"].reshape(-1, 3) for w in want])
+    assert np.array_equal(got["segments"].astype(np.int64), segs)
+    kv_end = np.concatenate([w["kv_end"] for w in want])
+    assert np.array_equal(got["order"], np.argsort(-kv_end, kind="stable"))
+    assert info.n_sequences == len(ids_list) and info.decode_ok == 0 and info.prefix_len == 0
+    assert info.seq_len == sum(len(i) for i in ids_list) == info.rows
+    assert info.useful_pairs == sum(int(w["useful_pairs"]) for w in want)
+    assert info.n_qtiles == sum(-(-len(i) // info.block_m) for i in ids_list)
+    gaps = bca.Plan.varlen(ids_list, row_start=[1000 * b + 7 for b in range(len(ids_list))],
+                           host_only=True)
+    assert gaps.info.rows == 1000 * (len(ids_list) - 1) + 7 + len(ids_list[-1])
+
+
+def test_varlen_plan_errors():
+    a, b = np.array([-1, 0, 0], np.int32), np.array([-1, -1], np.int32)
+    status = lambda f: status_of(f)
+    assert status(lambda: bca.Plan.varlen([a, b], row_start=[0, 2], host_only=True)) == \
+        _lib.BCA_ERR_ARG                                                # overlap
+    assert b"overlap" in _lib.load().bca_last_error()
+    assert status(lambda: bca.Plan.varlen([a, b], row_start=[-1, 5], host_only=True)) == \
+        _lib.BCA_ERR_ARG
+    assert status(lambda: bca.Plan.varlen([a, np.array([], np.int32)], host_only=True)) == \
+        _lib.BCA_ERR_ARG                                                # empty sequence
+    assert status(lambda: bca.Plan.varlen([a, np.array([0, -1, 0])], host_only=True)) == \
+        _lib.BCA_ERR_BLOCK_IDS
+    assert b"sequence 1" in _lib.load().bca_last_error()
+    ok = bca.Plan.varlen([a, b], row_start=[3, 0], host_only=True)   # gaps, any order
+    assert ok.info.rows == 6
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    lens = (ctypes.c_int64 * 2)(3, 2)
+    assert lib.bca_plan_varlen(None, lens, None, 2, 0, ctypes.byref(h)) == _lib.BCA_ERR_ARG
+    # a batch plan is not a single-sequence prefill
+    assert call_prefill(ok.handle) == _lib.BCA_ERR_ARG
+    assert b"bca_prefill_varlen" in lib.bca_last_error()
+    r = ctypes.byref
+    assert lib.bca_prefill_varlen(ok.handle, 2, 64, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
+                                  None) == _lib.BCA_ERR_UNSUPPORTED
+    assert lib.bca_prefill_varlen(ok.handle, 2, 128, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
+                                  None) == _lib.BCA_ERR_ARG             # host-only plan
+    assert b"HOST_ONLY" in lib.bca_last_error()
