@@ -81,10 +81,17 @@ EDIT_2REF_CFG = Layout("2-ref 1024^2 edit under CFG (B=2)", _two_ref_edit(), bat
 LONG_4REF = Layout("4-ref 1024^2 + 2048^2 target: [t96][ref]([t16][ref])x3[target 16384]",
                    _four_ref_long(), batch=1, heads=32)
 
+# A small target under the same two references (512^2 target: 32 x 32 = 1,024 latents): the
+# cached step then has too few query tiles to fill the GPU, the case split-KV decode is for.
+EDIT_2REF_T512 = Layout("2-ref 1024^2 edit, 512^2 target: [t48][ref 4096][t40][ref 4096][t24]"
+                        "[target 1024]", _two_ref_edit()[:-1] + (("image", 1024),), batch=1,
+                        heads=32)
+
 WORKLOADS = {"tiny": TINY, "t2i_1024": T2I_1024, "edit_2ref": EDIT_2REF,
-             "edit_2ref_cfg": EDIT_2REF_CFG, "long_4ref": LONG_4REF}
+             "edit_2ref_cfg": EDIT_2REF_CFG, "long_4ref": LONG_4REF,
+             "edit_2ref_t512": EDIT_2REF_T512}
 SEEDS = {"tiny": 1001, "t2i_1024": 2001, "edit_2ref": 3001, "edit_2ref_cfg": 4000,
-         "long_4ref": 5001}
+         "long_4ref": 5001, "edit_2ref_t512": 6001}
 DECODE_STEPS = 49  # 50 denoising steps: one prefill, then 49 cached steps
 
 

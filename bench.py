@@ -194,6 +194,42 @@ def varlen_timing(torch, bca, W, dev, H, iters=10):
             "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "useful_gflop": round(flops / 1e9, 1)}
 
 
+def split_decode_timing(torch, bca, W, dev, iters=20):
+    """Cached step of the 512^2-target edit (N = 1,024 under P = 8,304, B = 1, H = 32): the
+    plain decode (8 x 32 = 256 workgroups) against the split-KV decode (library-chosen ranges)."""
+    lay = W.EDIT_2REF_T512
+    ids = lay.block_ids()
+    H = lay.heads
+    plan = bca.Plan(ids)
+    P, N = plan.info.prefix_len, plan.info.target_len
+    qb, kb, vb = W.qkv(W.SEEDS["edit_2ref_t512"], 1, len(ids), H)
+    cache = bca.KVCache(bca.KVCache.BF16, to_dev(torch, kb[:, :P], dev), to_dev(torch, vb[:, :P], dev))
+    q, k, v = (to_dev(torch, x[:, P:], dev) for x in (qb, kb, vb))
+    nbytes, used = bca.split_workspace(plan, 1, H)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    o = torch.empty((1, N, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    flops = 4.0 * HEAD_DIM * H * N * (P + N)
+    out = {"workload": f"512^2 target under two 1024^2 references: N={N}, P={P}, B=1, H={H}",
+           "useful_gflop": round(flops / 1e9, 2)}
+    for name, fn in (("plain", lambda: bca.decode_ex(plan, q, cache, k, v, out=o)),
+                     ("split", lambda: bca.decode_split(plan, q, cache, k, v, workspace=ws, out=o))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[name] = {"ms": round(ms, 4), "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        log(f"512^2-target decode, {name}: {ms:.4f} ms = {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    out["split"]["ranges"] = used
+    plan.free()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +346,7 @@ def main():
 
     prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
     varlen = varlen_timing(torch, bca, W, dev, H)
+    split = split_decode_timing(torch, bca, W, dev)
     fp8 = None if args.no_fp8 else fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od,
                                                flops_pre, flops_dec, Bd, S, H, P, dev)
 
@@ -341,6 +378,7 @@ def main():
         "fp8_cache": fp8,
         "qk_prologue": prologue,
         "varlen_prefill": varlen,
+        "split_decode": split,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -25,7 +25,8 @@ from . import _lib
 from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
-           "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen"]
+           "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen",
+           "decode_split", "split_workspace"]
 
 
 class BcaError(RuntimeError):
@@ -430,4 +431,49 @@ def prefill_varlen(plan: Plan, q, k, v, *, scale: Optional[float] = None, out=No
             ctypes.byref(_desc3(k, "k", torch.bfloat16)),
             ctypes.byref(_desc3(v, "v", torch.bfloat16)),
             ctypes.byref(_desc3(out, "out", torch.float32)), ctypes.c_void_p(stream)))
+    return out
+
+
+def split_workspace(plan: Plan, batch: int, heads: int, n_split: int = 0):
+    """(bytes, n_split_used) of a split decode (bca_decode_split_workspace)."""
+    nbytes = ctypes.c_int64()
+    used = ctypes.c_int32()
+    _check(_lib.load().bca_decode_split_workspace(plan.handle, batch, heads, n_split,
+                                                  ctypes.byref(nbytes), ctypes.byref(used)))
+    return nbytes.value, used.value
+
+
+def decode_split(plan: Plan, q, cache: Optional[KVCache], k, v, *, n_split: int = 0,
+                 workspace=None, scale: Optional[float] = None, out=None):
+    """Split-KV cached decode (bca_decode_split).  The workspace (a uint8 device tensor) is
+    allocated here when not given."""
+    import torch
+
+    B, N, H, D = q.shape
+    P = plan.info.prefix_len
+    if N != plan.info.target_len:
+        raise ValueError(f"target length {N} != plan's {plan.info.target_len}")
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (B, N, H, D):
+            raise ValueError(f"{name} must be [B, {N}, H, D]")
+    if P > 0 and cache is None:
+        raise ValueError("the prefix is not empty: a cache is required")
+    nbytes, _ = split_workspace(plan, B, H, n_split)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None and workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+    c = ctypes.byref(cache._struct(B, P, H, D)) if P > 0 else None
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_decode_split(
+            plan.handle, B, H, D, _scale(scale), ctypes.byref(_desc(q, "q", torch.bfloat16)), c,
+            ctypes.byref(_desc(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc(v, "v", torch.bfloat16)),
+            ctypes.byref(_desc(out, "out", torch.float32)), n_split, ws, wsb,
+            ctypes.c_void_p(stream)))
     return out

@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued.
 #include "bca.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -419,10 +420,37 @@ bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale
   return BCA_OK;
 }
 
-bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
-                         const bca_tensor* q_tgt, const bca_kv_cache* cache,
-                         const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Key ranges of a split decode: the requested count (0 = enough workgroups for about four per
+// CU, each range at least 8 key tiles), at most one per key tile, and no empty range.
+void split_shape(const bca::HostPlan& hp, int32_t B, int32_t H, int32_t n_split,
+                 int32_t* n_used, int32_t* tiles_per) {
+  const int64_t ktiles = (hp.prefix_len + hp.target_len + bca::kDecodeBlockN - 1) / bca::kDecodeBlockN;
+  const int64_t nt = (hp.target_len + bca::kBlockM - 1) / bca::kBlockM;
+  int64_t want = n_split;
+  if (want == 0) {
+    const int64_t base = nt * B * H;
+    want = (1024 + base - 1) / base;
+    want = std::min<int64_t>(want, std::max<int64_t>(1, ktiles / 8));
+  }
+  want = std::max<int64_t>(1, std::min<int64_t>(want, ktiles));
+  const int64_t per = (ktiles + want - 1) / want;
+  *tiles_per = (int32_t)per;
+  *n_used = (int32_t)((ktiles + per - 1) / per);
+}
+
+int64_t split_bytes(const bca::HostPlan& hp, int32_t B, int32_t H, int32_t n_used) {
+  return n_used <= 1 ? 0 : (int64_t)n_used * B * hp.target_len * H * (bca::kHeadDim + 2) * 4;
+}
+
+bca_status decode_impl(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                       const bca_tensor* q_tgt, const bca_kv_cache* cache,
+                       const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
+                       bool split_call, int32_t n_split, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
   float scale_log2 = 0.0f;
   bca_status s = check_common(plan, B, H, D, scale, &scale_log2);
   if (s != BCA_OK) return s;
@@ -444,7 +472,20 @@ bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float
   if ((s = check_extent(k_tgt, "k_tgt", N)) != BCA_OK) return s;
   if ((s = check_extent(v_tgt, "v_tgt", N)) != BCA_OK) return s;
   const int64_t nt = (N + bca::kBlockM - 1) / bca::kBlockM;
-  if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles exceeds 2^31 - 1");
+  int32_t n_used = 1, per = 0;
+  if (split_call) {
+    if (n_split < 0) return fail(BCA_ERR_ARG, "n_split must be >= 0 (0 = chosen by the library)");
+    split_shape(hp, B, H, n_split, &n_used, &per);
+    const int64_t need = split_bytes(hp, B, H, n_used);
+    if (n_used > 1) {
+      if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return fail(BCA_ERR_ARG, "workspace must be a 16-byte aligned device pointer");
+      if (workspace_bytes < need)
+        return fail(BCA_ERR_ARG, "workspace holds " + std::to_string(workspace_bytes) +
+                                     " bytes, " + std::to_string(need) + " needed");
+    }
+  }
+  if (!grid_fits(nt * n_used, B, H)) return fail(BCA_ERR_ARG, "the grid exceeds 2^31 - 1");
   if ((s = check_launchable(plan)) != BCA_OK) return s;
 
   bca::AttnArgs a{};
@@ -474,9 +515,50 @@ bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float
   a.batch = B;
   a.n_qtiles = (int32_t)nt;
   a.scale_log2 = scale_log2;
+  a.n_split = n_used;
+  if (n_used > 1) {
+    a.split_tiles = per;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = a.part_o + (int64_t)n_used * B * N * H * bca::kHeadDim;
+  }
   hipError_t e = bca::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return BCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                         const bca_tensor* q_tgt, const bca_kv_cache* cache,
+                         const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
+                         void* stream) {
+  return decode_impl(plan, B, H, D, scale, q_tgt, cache, k_tgt, v_tgt, o, false, 1, nullptr, 0,
+                     stream);
+}
+
+bca_status bca_decode_split_workspace(bca_plan_t plan, int32_t B, int32_t H, int32_t n_split,
+                                      int64_t* bytes, int32_t* n_split_used) {
+  if (plan == nullptr || bytes == nullptr) return fail(BCA_ERR_ARG, "plan or bytes is NULL");
+  if (B < 1 || H < 1) return fail(BCA_ERR_ARG, "B and H must be >= 1");
+  if (n_split < 0) return fail(BCA_ERR_ARG, "n_split must be >= 0 (0 = chosen by the library)");
+  if (!plan->host.decode_ok)
+    return fail(BCA_ERR_NO_DECODE, "the layout's last block is text");
+  int32_t n_used = 1, per = 0;
+  split_shape(plan->host, B, H, n_split, &n_used, &per);
+  *bytes = split_bytes(plan->host, B, H, n_used);
+  if (n_split_used) *n_split_used = n_used;
+  return BCA_OK;
+}
+
+bca_status bca_decode_split(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                            const bca_tensor* q_tgt, const bca_kv_cache* cache,
+                            const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
+                            int32_t n_split, void* workspace, int64_t workspace_bytes,
+                            void* stream) {
+  return decode_impl(plan, B, H, D, scale, q_tgt, cache, k_tgt, v_tgt, o, true, n_split,
+                     workspace, workspace_bytes, stream);
 }
 
 bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,

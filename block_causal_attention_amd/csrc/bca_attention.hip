@@ -165,13 +165,18 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // the (batch, head)-major work list: all query tiles of one head then run on one XCD at about
   // the same time and share that head's K/V tiles in its L2.  Within a head, tiles run in the
   // plan's heavy-first order.  (A remainder of fewer than 8 workgroups keeps its own index.)
-  const int bh_count = a.batch * a.heads;
+  // A split decode adds a key-range index inside each (batch, head): workgroups of one (batch,
+  // head, key range) stay contiguous, so they share that range's K/V tiles in one L2.
+  const int n_split = kDecode && a.n_split > 1 ? a.n_split : 1;
+  const int bh_count = a.batch * a.heads * n_split;
   const int total = a.n_qtiles * bh_count;
   const int full8 = total & ~7;
   int work = blockIdx.x;
   if (work < full8) work = (work & 7) * (full8 >> 3) + (work >> 3);
-  const int bh = work / a.n_qtiles;
-  const int slot = work - bh * a.n_qtiles;
+  const int bhs = work / a.n_qtiles;
+  const int slot = work - bhs * a.n_qtiles;
+  const int bh = kDecode ? bhs / n_split : bhs;
+  const int split = kDecode ? bhs - bh * n_split : 0;
   const int b = bh / a.heads;
   const int h = bh - b * a.heads;
   const int tile = kDecode ? slot : a.order[slot];
@@ -190,6 +195,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     kv_end = td[5];
   }
   const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
+  // key tiles this workgroup visits: all of them, or its split's range
+  const int j_begin = n_split > 1 ? split * a.split_tiles : 0;
+  const int j_end = n_split > 1 ? min(ntiles, j_begin + a.split_tiles) : ntiles;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
   int lim[kQueryBlocks];
@@ -544,19 +552,20 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const float c2 = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // ---- prologue: tile 0 resident in buffer 0; tile 1 on its way ---------------------------------
+  // ---- prologue: the first tile resident in its buffer; the next one on its way ------------------
   if constexpr (kDirect) {
-    dma_tile(0, 0);
-    if (ntiles > 1) dma_tile(kBlockN, 1);
+    dma_tile(j_begin * kBlockN, j_begin & 1);
+    if (j_begin + 1 < j_end) dma_tile((j_begin + 1) * kBlockN, (j_begin + 1) & 1);
     __builtin_amdgcn_s_waitcnt(0);
   } else {
-    stage_k(0);
-    stage_v(0);
-    write_k(k_lds[0], 0);
-    write_v(v_lds[0], 0);
-    if (ntiles > 1) {
-      stage_k(kBlockN);
-      stage_v(kBlockN);
+    const int first = j_begin * kBlockN;
+    stage_k(first);
+    stage_v(first);
+    write_k(k_lds[j_begin & 1], first);
+    write_v(v_lds[j_begin & 1], first);
+    if (j_begin + 1 < j_end) {
+      stage_k(first + kBlockN);
+      stage_v(first + kBlockN);
     }
   }
   __syncthreads();
@@ -677,13 +686,13 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     if constexpr (kDirect) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (j + 2 < ntiles) dma_tile((j + 2) * kBlockN, cur);
+      if (j + 2 < j_end) dma_tile((j + 2) * kBlockN, cur);
     } else {
-      if (j + 1 < ntiles) {
+      if (j + 1 < j_end) {
         write_k(k_lds[cur ^ 1], n0 + kBlockN);
         write_v(v_lds[cur ^ 1], n0 + kBlockN);
       }
-      if (j + 2 < ntiles) {
+      if (j + 2 < j_end) {
         stage_k((j + 2) * kBlockN);
         stage_v((j + 2) * kBlockN);
       }
@@ -691,9 +700,36 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     }
   };
   // tiles [0, n_full) lie entirely below every row's limit; the rest need the mask
-  const int n_full = min(ntiles, kv_full / kBlockN);
-  for (int j = 0; j < n_full; ++j) tile_step(std::false_type{}, j);
-  for (int j = n_full; j < ntiles; ++j) tile_step(std::true_type{}, j);
+  const int n_full = min(j_end, kv_full / kBlockN);
+  for (int j = j_begin; j < n_full; ++j) tile_step(std::false_type{}, j);
+  for (int j = max(j_begin, n_full); j < j_end; ++j) tile_step(std::true_type{}, j);
+
+  // ---- split epilogue: this key range's unnormalised O, running max m (scaled, base 2) and row
+  // sum l, to be merged by split_combine.  Layout [split][b][row][h] (x 128 for O).
+  if (n_split > 1) {
+#pragma unroll
+    for (int qb = 0; qb < kQueryBlocks; ++qb) {
+      const float l = halves_sum(l_part[qb]);
+      if (row_ok[qb]) {
+        const int row = row0 + (wave * kQueryBlocks + qb) * 32 + qn;
+        const int64_t r = (((int64_t)split * a.batch + b) * a.n_q + row) * a.heads + h;
+        float* op = a.part_o + r * kHeadDim + 4 * half;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 val = {o[qb][d][4 * jj], o[qb][d][4 * jj + 1], o[qb][d][4 * jj + 2],
+                               o[qb][d][4 * jj + 3]};
+            *reinterpret_cast<f32x4*>(op + 32 * d + 8 * jj) = val;
+          }
+        if (half == 0) {
+          a.part_ml[2 * r] = m_run[qb];
+          a.part_ml[2 * r + 1] = l;
+        }
+      }
+    }
+    return;
+  }
 
   // ---- epilogue: O = O_acc / l; lane holds dims 32 d + 8 jj + 4 half + (0..3) of its query
 #pragma unroll
@@ -712,6 +748,39 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
         }
     }
   }
+}
+
+// Merges the key ranges of a split decode: per (b, row, h), M = max m_c, w_c = 2^(m_c - M),
+// O = sum_c w_c O_c / sum_c w_c l_c.  Sixteen lanes per row, eight dims per lane.
+__global__ __launch_bounds__(256) void split_combine(const AttnArgs a) {
+  const int64_t rows = (int64_t)a.batch * a.n_q * a.heads;
+  const int64_t r_raw = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (r_raw >= rows) return;  // whole 16-lane groups; no cross-lane exchange below
+  const int d0 = 8 * (threadIdx.x & 15);
+  const int h = (int)(r_raw % a.heads);
+  const int64_t bn = r_raw / a.heads;
+  const int row = (int)(bn % a.n_q);
+  const int b = (int)(bn / a.n_q);
+  float mx = -__builtin_inff();
+  for (int c = 0; c < a.n_split; ++c) mx = fmaxf(mx, a.part_ml[2 * (c * rows + r_raw)]);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float l = 0.0f;
+  for (int c = 0; c < a.n_split; ++c) {
+    const int64_t r = c * rows + r_raw;
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * r] - mx);
+    l = __builtin_fmaf(w, a.part_ml[2 * r + 1], l);
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + r * kHeadDim + d0);
+    const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = __builtin_fmaf(w, x0[i], acc[i]);
+      acc[4 + i] = __builtin_fmaf(w, x1[i], acc[4 + i]);
+    }
+  }
+  const float inv = 1.0f / l;
+  float* op = a.o + b * a.o_sb + (int64_t)row * a.o_ss + h * a.o_sh + d0;
+  *reinterpret_cast<f32x4*>(op) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  *reinterpret_cast<f32x4*>(op + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
 }
 
 // Prefill: block-causal, direct-to-LDS fills, optional prefix-cache store in format kFmt.
@@ -753,7 +822,8 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
+  const int n_split = a.n_split > 1 ? a.n_split : 1;
+  const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads * n_split);
   switch (a.cache_fmt) {
     case kCacheBf16:
 #if BCA_DECODE_DIRECT
@@ -766,6 +836,10 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
     case kCacheFp8KV: hipLaunchKernelGGL(attn_decode<kCacheFp8KV>, grid, dim3(kThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_split == 1) return e;
+  const int64_t rows = (int64_t)a.batch * a.n_q * a.heads;
+  hipLaunchKernelGGL(split_combine, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -94,6 +94,13 @@ struct AttnArgs {
   float* vcs;
   int64_t vcs_sb, vcs_ss, vcs_sh;
   int32_t cache_fmt;  // kCacheBf16 / kCacheFp8V / kCacheFp8KV
+  // Decode only: key ranges of split_tiles key tiles each, n_split of them (1 = no split), whose
+  // partial results go to part_o [n_split][B][N][H][D] and part_ml [n_split][B][N][H][2] (m, l)
+  // and are merged into o by a second kernel.
+  int32_t n_split;
+  int32_t split_tiles;
+  float* part_o;
+  float* part_ml;
 };
 
 // Q/K prologue: RMS-normalise each 128-value head row of q and k (weights wq, wk), rotate its

@@ -281,6 +281,33 @@ bca_status bca_qk_prologue(int32_t B, int64_t S, int32_t H, int32_t D, float eps
                            const bca_tensor* k_out, const float* q_weight, const float* k_weight,
                            const float* rope_table, void* stream);
 
+/*
+ * Split-KV decode.  The cached step of bca_decode_ex (same arguments and result; the guide's
+ * section "Two exact attention paths, with different operating requirements") for targets too
+ * small to fill the GPU, e.g. a 512 x 512 target (N = 1,024) under a long prefix: each
+ * (batch, head, query tile) is cut into n_split ranges of key tiles handled by separate
+ * workgroups.  Each range leaves its unnormalised output, running maximum m (base 2, scaled) and
+ * row sum l in a caller workspace; a second kernel merges them:
+ *     O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,   M = max_c m_c,
+ * which is the same softmax up to rounding.
+ *
+ * bca_decode_split_workspace -- HOST.  *bytes = workspace bytes for (plan, B, H, n_split);
+ * n_split = 0 lets the library choose (enough workgroups for about four per CU, ranges of at
+ * least 8 key tiles); *n_split_used (may be NULL) = the number of ranges it will use (1 = plain
+ * decode, bytes = 0).  The plan's last block must be an image block (else BCA_ERR_NO_DECODE).
+ *
+ * bca_decode_split -- as bca_decode_ex, plus n_split (>= 0) and a DEVICE workspace of at least
+ * that many bytes, 16-byte aligned, owned by the caller and not used by anything else while the
+ * call runs (it may be NULL when n_split_used is 1).  Enqueues two kernels on stream.
+ */
+bca_status bca_decode_split_workspace(bca_plan_t plan, int32_t B, int32_t H, int32_t n_split,
+                                      int64_t* bytes, int32_t* n_split_used);
+bca_status bca_decode_split(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                            const bca_tensor* q_tgt, const bca_kv_cache* cache,
+                            const bca_tensor* k_tgt, const bca_tensor* v_tgt, const bca_tensor* o,
+                            int32_t n_split, void* workspace, int64_t workspace_bytes,
+                            void* stream);
+
 /* Static name of a status code ("BCA_OK", ...); "unknown status" for other values. */
 const char* bca_status_str(bca_status status);
 

@@ -317,3 +317,37 @@ def test_varlen_plan_errors():
     assert lib.bca_prefill_varlen(ok.handle, 2, 128, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
                                   None) == _lib.BCA_ERR_ARG             # host-only plan
     assert b"HOST_ONLY" in lib.bca_last_error()
+
+
+def test_split_workspace_sizing_and_errors():
+    lib = _lib.load()
+    p = plan_host(W.EDIT_2REF_T512.block_ids())            # P = 8,304, N = 1,024
+    # B = 1, H = 32: 8 query tiles x 32 heads = 256 workgroups -> 4 ranges of 37 key tiles
+    nbytes, used = bca.split_workspace(p, 1, 32)
+    assert used == 4 and nbytes == 4 * 1 * 1024 * 32 * 130 * 4
+    assert bca.split_workspace(p, 1, 32, 1) == (0, 1)      # one range: the plain decode
+    assert bca.split_workspace(p, 1, 32, 146) == (146 * 1024 * 32 * 520, 146)
+    assert bca.split_workspace(p, 1, 32, 500)[1] == 146    # at most one range per key tile
+    assert bca.split_workspace(p, 1, 32, 3)[1] == 3
+    # the CFG shape already fills the GPU: the library keeps one range
+    big = plan_host(W.EDIT_2REF.block_ids())
+    assert bca.split_workspace(big, 2, 32) == (0, 1)
+    with pytest.raises(bca.BcaError) as e:
+        bca.split_workspace(p, 1, 32, -1)
+    assert e.value.status == _lib.BCA_ERR_ARG
+    text_last = plan_host([-1, 0, 0, -1])
+    with pytest.raises(bca.BcaError) as e:
+        bca.split_workspace(text_last, 1, 1)
+    assert e.value.status == _lib.BCA_ERR_NO_DECODE
+    r = ctypes.byref
+    c = _cache(0)
+    call = lambda n, ws, wsb: lib.bca_decode_split(p.handle, 1, 32, 128, 0.0, r(_t()), r(c),
+                                                   r(_t()), r(_t()), r(_t()), n, ws, wsb, None)
+    assert call(4, None, 0) == _lib.BCA_ERR_ARG                                # no workspace
+    assert call(4, ctypes.c_void_p(0x100008), 1 << 30) == _lib.BCA_ERR_ARG      # misaligned
+    assert call(4, ctypes.c_void_p(0x100000), 1000) == _lib.BCA_ERR_ARG        # too small
+    assert b"needed" in lib.bca_last_error()
+    assert call(-2, None, 0) == _lib.BCA_ERR_ARG
+    assert call(4, ctypes.c_void_p(0x100000), 1 << 30) == _lib.BCA_ERR_ARG     # host-only plan
+    assert b"HOST_ONLY" in lib.bca_last_error()
+    assert call(1, None, 0) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in lib.bca_last_error()
