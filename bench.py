@@ -242,6 +242,8 @@ def main():
                     help="heads in the CPU-oracle sample")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 prefix-cache timings (reported beside the bf16 step)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prologue, varlen and split-decode timings (profiling runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -344,9 +346,11 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(key), "kernel": dom}
 
-    prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
-    varlen = varlen_timing(torch, bca, W, dev, H)
-    split = split_decode_timing(torch, bca, W, dev)
+    prologue = varlen = split = None
+    if not args.no_extras:
+        prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
+        varlen = varlen_timing(torch, bca, W, dev, H)
+        split = split_decode_timing(torch, bca, W, dev)
     fp8 = None if args.no_fp8 else fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od,
                                                flops_pre, flops_dec, Bd, S, H, P, dev)
 

@@ -52,6 +52,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef BCA_DECODE_DIRECT
 #define BCA_DECODE_DIRECT 0
 #endif
+#ifndef BCA_V_PAD
+#define BCA_V_PAD 16
+#endif
 #ifndef BCA_STAGE_SWIZZLE
 #define BCA_STAGE_SWIZZLE 0
 #endif
@@ -150,7 +153,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // LDS rows: unpadded (256 B) with their 16-byte chunks swizzled, or padded (272 B / 288 B).
   constexpr bool kSwizzle = kDirect || kStageSwizzle;
   constexpr int kKStride = kSwizzle ? kHeadDim : kHeadDim + 8;
-  constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + 16;
+  // Padded V rows: 288 B.  (320 B rows make the transposed reads bank-conflict-free on 64 banks,
+  // BCA_V_PAD = 32, but measured no faster: the decode is not bound by LDS conflicts.)
+  constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + BCA_V_PAD;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBlockN * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBlockN * kVStride];
 
