@@ -96,8 +96,11 @@ def cpu_baseline(W, lay, ids, P, N, budget_rows, heads):
 def fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od, flops_pre, flops_dec, Bd, S, H, P,
                 dev, iters=10):
     """The same prefill and decode calls with the prefix cache stored as FP8 E4M3 (V only, then
-    K and V): ms per call, useful TFLOP/s and the cache bytes per layer of the CFG pair."""
+    K and V): ms per call, useful TFLOP/s and the cache bytes per layer of the CFG pair; also the
+    cache's expansion to bf16 alone (GB/s over codes + scales read and bf16 written) and followed
+    by the bf16 decode."""
     out = {}
+    wide = bca.KVCache.empty(plan, Bd, H, bca.KVCache.BF16, device=dev)
     for name, fmt in (("fp8_v", bca.KVCache.FP8_V), ("fp8_kv", bca.KVCache.FP8_KV)):
         c1 = bca.KVCache.empty(plan, 1, H, fmt, device=dev)
         c2 = bca.KVCache.empty(plan, Bd, H, fmt, device=dev)
@@ -118,15 +121,34 @@ def fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od, flops_pre, flops_dec,
             qt, kt, vt = sets[i % len(sets)]
             bca.decode_ex(plan, qt, c2, kt, vt, out=od)
         ev[2].record()
+        # the layer's cache expanded to bf16 first, then the bf16 decode
+        for i in range(iters):
+            bca.dequantize_cache(c2, wide)
+        ev.append(torch.cuda.Event(enable_timing=True))
+        ev[3].record()
+        for i in range(iters):
+            qt, kt, vt = sets[i % len(sets)]
+            bca.dequantize_cache(c2, wide)
+            bca.decode_ex(plan, qt, wide, kt, vt, out=od)
+        ev.append(torch.cuda.Event(enable_timing=True))
+        ev[4].record()
         torch.cuda.synchronize()
         pre_ms = ev[0].elapsed_time(ev[1]) / iters
         dec_ms = ev[1].elapsed_time(ev[2]) / iters
+        exp_ms = ev[2].elapsed_time(ev[3]) / iters
+        both_ms = ev[3].elapsed_time(ev[4]) / iters
+        moved = c2.nbytes() + wide.nbytes()          # codes + scales read, bf16 written
         out[name] = {"prefill_ms": round(pre_ms, 4),
                      "prefill_useful_tflops": round(flops_pre / (pre_ms * 1e-3) / 1e12, 2),
                      "decode_ms": round(dec_ms, 4),
                      "decode_useful_tflops": round(flops_dec / (dec_ms * 1e-3) / 1e12, 2),
+                     "expand_ms": round(exp_ms, 4),
+                     "expand_gbs": round(moved / (exp_ms * 1e-3) / 1e9, 1),
+                     "expand_then_decode_ms": round(both_ms, 4),
+                     "expand_then_decode_useful_tflops": round(flops_dec / (both_ms * 1e-3) / 1e12, 2),
                      "cache_mb_per_layer_b2": round(c2.nbytes() / 1e6, 2)}
-        log(f"{name}: prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms, cache "
+        log(f"{name}: prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms, expand {exp_ms:.3f} ms "
+            f"({moved / (exp_ms * 1e-3) / 1e9:.0f} GB/s), expand+decode {both_ms:.3f} ms, cache "
             f"{c2.nbytes() / 1e6:.1f} MB per layer (B={Bd})")
         del c1, c2
     out["bf16_cache_mb_per_layer_b2"] = round(2 * Bd * P * H * HEAD_DIM * 2 / 1e6, 2)

@@ -26,7 +26,7 @@ from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
            "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen",
-           "decode_split", "split_workspace"]
+           "decode_split", "split_workspace", "dequantize_cache"]
 
 
 class BcaError(RuntimeError):
@@ -476,4 +476,31 @@ def decode_split(plan: Plan, q, cache: Optional[KVCache], k, v, *, n_split: int 
             ctypes.byref(_desc(v, "v", torch.bfloat16)),
             ctypes.byref(_desc(out, "out", torch.float32)), n_split, ws, wsb,
             ctypes.c_void_p(stream)))
+    return out
+
+
+def dequantize_cache(cache: KVCache, out: Optional[KVCache] = None) -> KVCache:
+    """The cache written back as bf16 (bca_cache_dequantize): values E4M3(code) * scale in fp32,
+    rounded to bf16, bitwise what the FP8 decode uses.  `out` (a bf16 KVCache of the same
+    shape) is reused when given."""
+    import torch
+
+    B, P, H, D = cache.k.shape
+    if out is None:
+        out = KVCache(KVCache.BF16,
+                      torch.empty((B, P, H, D), dtype=torch.bfloat16, device=cache.k.device),
+                      torch.empty((B, P, H, D), dtype=torch.bfloat16, device=cache.k.device))
+    if out.format != KVCache.BF16:
+        raise ValueError("out must be a bf16 cache")
+    for name, t in (("out.k", out.k), ("out.v", out.v)):
+        if tuple(t.shape) != (B, P, H, D) or t.device != cache.k.device:
+            raise ValueError(f"{name} must be [B, P={P}, H, D] on the cache's device")
+    if P == 0:
+        return out
+    c = cache._struct(B, P, H, D)
+    stream = torch.cuda.current_stream(cache.k.device).cuda_stream
+    with torch.cuda.device(cache.k.device):
+        _check(_lib.load().bca_cache_dequantize(
+            B, P, H, D, ctypes.byref(c), ctypes.byref(_desc(out.k, "out.k", torch.bfloat16)),
+            ctypes.byref(_desc(out.v, "out.v", torch.bfloat16)), ctypes.c_void_p(stream)))
     return out

@@ -23,7 +23,8 @@ BCA_CACHE_FP8_KV = 2
 EXPORTED = ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export", "bca_prefill",
             "bca_decode", "bca_prefill_ex", "bca_decode_ex", "bca_rope_positions", "bca_rope_table",
             "bca_qk_prologue", "bca_plan_varlen", "bca_prefill_varlen",
-            "bca_decode_split_workspace", "bca_decode_split", "bca_status_str", "bca_last_error")
+            "bca_decode_split_workspace", "bca_decode_split", "bca_cache_dequantize",
+            "bca_status_str", "bca_last_error")
 
 
 class BcaTensor(ctypes.Structure):
@@ -89,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.bca_decode_split.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_float, T, C, T, T, T, ctypes.c_int32, P,
                                      ctypes.c_int64, P]
+    lib.bca_cache_dequantize.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int32, C, T, T, P]
     lib.bca_status_str.argtypes = [ctypes.c_int]
     lib.bca_status_str.restype = ctypes.c_char_p
     lib.bca_last_error.argtypes = []
@@ -96,7 +99,8 @@ def load() -> ctypes.CDLL:
     for name in ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export",
                  "bca_prefill", "bca_decode", "bca_prefill_ex", "bca_decode_ex",
                  "bca_rope_positions", "bca_rope_table", "bca_qk_prologue", "bca_plan_varlen",
-                 "bca_prefill_varlen", "bca_decode_split_workspace", "bca_decode_split"):
+                 "bca_prefill_varlen", "bca_decode_split_workspace", "bca_decode_split",
+                 "bca_cache_dequantize"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -615,4 +615,46 @@ bca_status bca_qk_prologue(int32_t B, int64_t S, int32_t H, int32_t D, float eps
   return BCA_OK;
 }
 
+bca_status bca_cache_dequantize(int32_t B, int64_t P, int32_t H, int32_t D,
+                                const bca_kv_cache* cache, const bca_tensor* k_out,
+                                const bca_tensor* v_out, void* stream) {
+  if (B < 1 || H < 1 || P < 1) return fail(BCA_ERR_ARG, "B, P and H must be >= 1");
+  if (P > INT32_MAX) return fail(BCA_ERR_ARG, "P must be below 2^31");
+  if (D != bca::kHeadDim)
+    return fail(BCA_ERR_UNSUPPORTED, "head width " + std::to_string(D) + " (only 128 is built)");
+  if (cache == nullptr) return fail(BCA_ERR_ARG, "cache is NULL");
+  bca_status s;
+  if ((s = check_cache(cache, P)) != BCA_OK) return s;
+  if ((s = check_tensor(k_out, "k_out", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(v_out, "v_out", 2)) != BCA_OK) return s;
+  const int64_t rows = (int64_t)B * P * H;
+  if ((rows + 15) / 16 > (int64_t)UINT32_MAX) return fail(BCA_ERR_ARG, "B * P * H is too large");
+  bca::DequantArgs a{};
+  a.k = cache->k.data;
+  a.k_sb = cache->k.stride_b; a.k_ss = cache->k.stride_s; a.k_sh = cache->k.stride_h;
+  a.v = cache->v.data;
+  a.v_sb = cache->v.stride_b; a.v_ss = cache->v.stride_s; a.v_sh = cache->v.stride_h;
+  if (cache->format == BCA_CACHE_FP8_KV) {
+    a.ks = static_cast<const float*>(cache->k_scale.data);
+    a.ks_sb = cache->k_scale.stride_b; a.ks_ss = cache->k_scale.stride_s;
+    a.ks_sh = cache->k_scale.stride_h;
+  }
+  if (cache->format != BCA_CACHE_BF16) {
+    a.vs = static_cast<const float*>(cache->v_scale.data);
+    a.vs_sb = cache->v_scale.stride_b; a.vs_ss = cache->v_scale.stride_s;
+    a.vs_sh = cache->v_scale.stride_h;
+  }
+  a.ko = static_cast<uint16_t*>(k_out->data);
+  a.ko_sb = k_out->stride_b; a.ko_ss = k_out->stride_s; a.ko_sh = k_out->stride_h;
+  a.vo = static_cast<uint16_t*>(v_out->data);
+  a.vo_sb = v_out->stride_b; a.vo_ss = v_out->stride_s; a.vo_sh = v_out->stride_h;
+  a.rows = rows;
+  a.prefix = (int32_t)P;
+  a.heads = H;
+  a.fmt = cache->format;
+  hipError_t e = bca::launch_dequant(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return BCA_OK;
+}
+
 }  // extern "C"

@@ -123,7 +123,30 @@ struct PrologueArgs {
   float eps;
 };
 
+// Cache expansion: K and V of a prefix cache (any format) written as bf16 [B, P, H, D].  A
+// quantised tensor's values are E4M3(code) * scale in fp32, rounded to bf16 (RNE); a bf16 tensor
+// is copied.
+struct DequantArgs {
+  const void* k;
+  int64_t k_sb, k_ss, k_sh;
+  const void* v;
+  int64_t v_sb, v_ss, v_sh;
+  const float* ks;
+  int64_t ks_sb, ks_ss, ks_sh;
+  const float* vs;
+  int64_t vs_sb, vs_ss, vs_sh;
+  uint16_t* ko;
+  int64_t ko_sb, ko_ss, ko_sh;
+  uint16_t* vo;
+  int64_t vo_sb, vo_ss, vo_sh;
+  int64_t rows;  // B * P * H
+  int32_t prefix;
+  int32_t heads;
+  int32_t fmt;   // kCacheBf16 / kCacheFp8V / kCacheFp8KV
+};
+
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 

@@ -240,6 +240,19 @@ bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float
                          void* stream);
 
 /*
+ * bca_cache_dequantize -- writes a prefix cache of any format back as bf16: k_out, v_out bf16
+ * [B, P, H, D] receive E4M3(code) * scale formed in fp32 and rounded to bf16 (RNE) for a quantised
+ * tensor, a copy for a bf16 one.  That is the value bca_decode_ex uses for the same code, so
+ * bca_decode over the expanded cache gives bitwise the result of bca_decode_ex over the FP8 one.
+ * Meant for expanding one layer's FP8 cache into a transient buffer just before that layer's
+ * cached step (the FP8 form keeps the memory of all layers; the bf16 decode is the faster one).
+ * The outputs must not overlap the cache.  D must be 128.  Enqueues one kernel on stream.
+ */
+bca_status bca_cache_dequantize(int32_t B, int64_t P, int32_t H, int32_t D,
+                                const bca_kv_cache* cache, const bca_tensor* k_out,
+                                const bca_tensor* v_out, void* stream);
+
+/*
  * Q/K prologue ("Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo": section
  * "One stream for text, reference images, and the target" normalises Q and K per head before
  * RoPE; section "Three-axis RoPE preserves image geometry" splits a head's 128 dims (16, 56, 56)

@@ -319,6 +319,32 @@ def test_varlen_plan_errors():
     assert b"HOST_ONLY" in lib.bca_last_error()
 
 
+def test_cache_dequantize_argument_errors():
+    """bca_cache_dequantize rejects bad arguments before any device call (only invalid calls are
+    made here: a valid one would launch)."""
+    lib = _lib.load()
+    r = ctypes.byref
+    err = lambda: lib.bca_last_error()
+
+    def call(B=1, P=82, H=2, D=128, c="ok", ko=None, vo=None):
+        cache = _cache(2) if c == "ok" else c
+        return lib.bca_cache_dequantize(B, P, H, D, None if cache is None else r(cache),
+                                        r(ko or _t()), r(vo or _t()), None)
+
+    assert call(D=64) == _lib.BCA_ERR_UNSUPPORTED
+    assert call(B=0) == _lib.BCA_ERR_ARG
+    assert call(P=0) == _lib.BCA_ERR_ARG
+    assert call(H=0) == _lib.BCA_ERR_ARG
+    assert call(P=1 << 31) == _lib.BCA_ERR_ARG and b"2^31" in err()
+    assert call(c=None) == _lib.BCA_ERR_ARG and b"NULL" in err()
+    assert call(c=_cache(5)) == _lib.BCA_ERR_ARG and b"unknown format" in err()
+    assert call(c=_cache(1, v=_t(ptr=0x10008))) == _lib.BCA_ERR_ARG
+    assert call(c=_cache(2, ks=_lib.BcaTensor(0x20002, 0, 1, 1))) == _lib.BCA_ERR_ARG
+    assert call(ko=_t(ptr=0x10004)) == _lib.BCA_ERR_ARG and b"k_out" in err()
+    assert call(vo=_t(ss=4100)) == _lib.BCA_ERR_ARG and b"v_out" in err()
+    assert call(vo=_lib.BcaTensor(0, 0, 4096, 128)) == _lib.BCA_ERR_ARG and b"NULL" in err()
+
+
 def test_split_workspace_sizing_and_errors():
     lib = _lib.load()
     p = plan_host(W.EDIT_2REF_T512.block_ids())            # P = 8,304, N = 1,024
