@@ -64,6 +64,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef BCA_STAGE_SWIZZLE
 #define BCA_STAGE_SWIZZLE 0
 #endif
+// Which exponentials of the softmax run on the FMA pipe (exp2_fma below) instead of the
+// transcendental unit: 0 none, 1 all, 2 one of each pair.
+#ifndef BCA_EXP_POLY
+#define BCA_EXP_POLY 0
+#endif
 constexpr bool kStageSwizzle = BCA_STAGE_SWIZZLE;  // swizzled rows for the staging path too
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerPass = kThreads / 16;  // staging: rows per pass
@@ -96,6 +101,24 @@ __device__ inline float halves_sum(float x) {
 }
 
 // FP8 prefix cache (E4M3, one fp32 scale per (token, head) row; the exact rule is in bca.h).
+// 2^x on the FMA pipe, for the softmax's p (rounded to bf16 right after, 2^-9 relative): x is
+// clamped to [-127, 64], split into n = rint(x) (the 1.5 * 2^23 rounding trick) and f = x - n in
+// [-0.5, 0.5]; 2^f comes from a cubic fitted for relative error (1.0e-4 at most, constant term
+// exactly 1, so integer x gives an exact power of two) and n is added to its exponent field.  At
+// the clamp floor f = 0 and the sum is exactly +0, so masked scores (-inf) give p = 0; elsewhere
+// below -126 the result is a denormal or 0.  x above 64 (only on a first tile or a rescale, which
+// the caller redoes) saturates at 2^64.
+__device__ inline float exp2_fma(float x) {
+  constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+  const float xc = __builtin_amdgcn_fmed3f(x, -127.0f, 64.0f);
+  const float t = xc + kRound;
+  const float f = xc - (t - kRound);
+  const float p = __builtin_fmaf(f, __builtin_fmaf(f, __builtin_fmaf(f, 0.05500871f, 0.24221068f),
+                                                   0.69328292f), 1.0f);
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) +
+                                       (__builtin_bit_cast(uint32_t, t) << 23));
+}
+
 // A staged row of a quantised tensor travels as {8 code bytes, scale bits, 0}; dequant turns it
 // into the 8 bf16 values E4M3(code) * scale that the LDS tile holds.
 __device__ inline u32x4 dequant(u32x4 x) {
@@ -163,8 +186,27 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // Padded V rows: 288 B.  (320 B rows make the transposed reads bank-conflict-free on 64 banks,
   // BCA_V_PAD = 32, but measured no faster: the decode is not bound by LDS conflicts.)
   constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + BCA_V_PAD;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBlockN * kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBlockN * kVStride];
+  // The two ring buffers.  The bf16 prefill (swizzled tiles, read by buffer constants: its tile
+  // loop is unrolled by two below) keeps them in separate arrays: reads of one are then provably
+  // independent of the direct loads in flight into the other, so the compiler adds no vmcnt wait
+  // before them (the ring's own waits and barrier order the buffers).  The other calls index one
+  // array of two at run time (an unrolled FP8 prefill runs out of registers in its quantiser).
+  constexpr bool kConstBuf = kSwizzle && kFmt == kCacheBf16;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBlockN * kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBlockN * kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kBlockN * kVStride];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBlockN * kVStride];
+  __shared__ __attribute__((aligned(16))) __bf16 k_pair[2][kBlockN * kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 v_pair[2][kBlockN * kVStride];
+  // Buffer `buf`: an int, or a std::integral_constant that names it at compile time.
+  auto k_lds = [](auto buf) -> __bf16* {
+    if constexpr (kConstBuf) return buf ? k_lds1 : k_lds0;
+    else return k_pair[buf];
+  };
+  auto v_lds = [](auto buf) -> __bf16* {
+    if constexpr (kConstBuf) return buf ? v_lds1 : v_lds0;
+    else return v_pair[buf];
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -400,8 +442,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
 #pragma unroll
     for (int i = 0; i < kDmaInstr; ++i) {
       const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds[buf][dst], 16, koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds[buf][dst], 16, voff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds(buf)[dst], 16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds(buf)[dst], 16, voff[i], 0, 0, 0);
     }
   };
   auto dma_rsrc = [&](const uint16_t* base, int64_t ss, int n0) {
@@ -416,8 +458,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
 #pragma unroll
       for (int i = 0; i < kDmaInstr; ++i) {
         const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds[buf][dst], 16, dma_koff[i], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds[buf][dst], 16, dma_voff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds(buf)[dst], 16, dma_koff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds(buf)[dst], 16, dma_voff[i], 0, 0, 0);
       }
       return;
     }
@@ -447,8 +489,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       const uint16_t* vp = (first ? v_base + (int64_t)key * a.v_ss
                                   : v2_base + (int64_t)(key - a.split) * a.v2_ss) + col;
       const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
-      __builtin_amdgcn_global_load_lds((const void*)kp, (lds_void*)&k_lds[buf][dst], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)vp, (lds_void*)&v_lds[buf][dst], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)kp, (lds_void*)&k_lds(buf)[dst], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vp, (lds_void*)&v_lds(buf)[dst], 16, 0, 0);
     }
   };
 
@@ -481,8 +523,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const int key = n0 + row;
     const bool in = key >= cache_lo && key < cache_hi;
     if (!(kKq || kVq) && !in) return;
-    const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds[buf][row * kKStride + st_col]);
-    const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds[buf][row * kVStride + st_col]);
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds(buf)[row * kKStride + st_col]);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds(buf)[row * kVStride + st_col]);
     put_chunk(std::integral_constant<bool, kKq>{}, kx, a.kc, a.kc_ss, a.kc_sb, a.kc_sh, a.kcs,
               a.kcs_ss, a.kcs_sb, a.kcs_sh, key, in);
     put_chunk(std::integral_constant<bool, kVq>{}, vx, a.vc, a.vc_ss, a.vc_sb, a.vc_sh, a.vcs,
@@ -503,7 +545,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     }
   };
 
-  // ---- per-lane LDS read addresses (element offsets inside one buffer) ---------------------------
+  // ---- per-lane LDS read addresses (byte offsets inside one buffer) ------------------------------
   // K operand of MFMA step c, key block kb: row 32 kb + qn, d = 16 c + 8 half .. + 7.
   // V^T operand (ds_read_b64_tr_b16): lane t of each 16-lane group points at row t / 4 and
   // column 4 (t % 4) of a 4 x 16 block and receives that block's column t (4 rows).
@@ -521,35 +563,46 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const int col = 32 * d + tr_col;
     return row * kVStride + (kSwizzle ? 8 * ((col >> 3) ^ swz(row)) + (col & 7) : col);
   };
-  // The same offsets computed once.  Key block kb (K) and 16-row group kc (V) only add constants
-  // (swz(row) depends on row bits 0..3, and those do not change with kb or kc), which fold into
-  // the reads' immediate offsets.  In a swizzled tile the chunk index is not additive, so each
-  // MFMA step c (K) and each (row half hi, column block d) pair (V) keeps its own offset; the
-  // asm barrier stops the compiler from re-deriving them inside the loop.
+  // The same offsets computed once, in bytes.  Key block kb (K) and 16-row group kc (V) only add
+  // constants (swz(row) depends on row bits 0..3, and those do not change with kb or kc), and so
+  // does the buffer where the loop below names it by a constant; all of these fold into the
+  // reads' immediate offsets.  In a swizzled tile the chunk index is not additive, so each MFMA
+  // step c (K) and each (row half hi, column block d) pair (V) keeps its own offset; the asm
+  // barrier stops the compiler from re-deriving them inside the loop.
   int koff[8], voff[2][4];
   if constexpr (kSwizzle) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      koff[c] = k_addr(0, c);
+      koff[c] = 2 * k_addr(0, c);
       asm volatile("" : "+v"(koff[c]));
     }
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        voff[hi][d] = v_addr(0, d, hi);
+        voff[hi][d] = 2 * v_addr(0, d, hi);
         asm volatile("" : "+v"(voff[hi][d]));
       }
   } else {
-    int k0 = k_addr(0, 0), v0 = v_addr(0, 0, 0);
+    int k0 = 2 * k_addr(0, 0), v0 = 2 * v_addr(0, 0, 0);
     asm volatile("" : "+v"(k0), "+v"(v0));
 #pragma unroll
-    for (int c = 0; c < 8; ++c) koff[c] = k0 + 16 * c;
+    for (int c = 0; c < 8; ++c) koff[c] = k0 + 32 * c;
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) voff[hi][d] = v0 + 8 * hi * kVStride + 32 * d;
+      for (int d = 0; d < 4; ++d) voff[hi][d] = v0 + 2 * (8 * hi * kVStride + 32 * d);
   }
+  // Operand reads from buffer `cur`: an int, or a std::integral_constant where the loop is
+  // unrolled by two tiles, which leaves no address arithmetic in the loop at all.
+  auto k_read = [&](auto cur, int c, int kb) {
+    const char* p = reinterpret_cast<const char*>(&k_lds(cur)[0]) + koff[c] + 64 * kb * kKStride;
+    return *reinterpret_cast<const bf16x8*>(p);
+  };
+  auto v_read = [&](auto cur, int hi, int d, int kc) {
+    const char* p = reinterpret_cast<const char*>(&v_lds(cur)[0]) + voff[hi][d] + 32 * kc * kVStride;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  };
 
   f32x16 o[kQueryBlocks][4];
   float m_run[kQueryBlocks];   // running max of scale*log2(e)*s (same in both lane halves)
@@ -573,8 +626,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const int first = j_begin * kBlockN;
     stage_k(first);
     stage_v(first);
-    write_k(k_lds[j_begin & 1], first);
-    write_v(v_lds[j_begin & 1], first);
+    write_k(k_lds(j_begin & 1), first);
+    write_v(v_lds(j_begin & 1), first);
     if (j_begin + 1 < j_end) {
       stage_k(first + kBlockN);
       stage_v(first + kBlockN);
@@ -582,13 +635,12 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   }
   __syncthreads();
 
-  // One key tile j from buffer j & 1.  kMasked: the tile crosses some row's key limit.  Full
+  // One key tile j from buffer cur = j & 1.  kMasked: the tile crosses some row's key limit.  Full
   // tiles run in a loop of their own, with no mask code between the score MFMAs and the
   // softmax, so the compiler can overlap the two inside one wave.
-  auto tile_step = [&](auto masked_c, int j) {
+  auto tile_step = [&](auto masked_c, int j, auto cur) {
     constexpr bool kMasked = decltype(masked_c)::value;
     const int n0 = j * kBlockN;
-    const int cur = j & 1;
     store_cache(n0, cur);
 
     // ---- S^T = K Q^T
@@ -600,8 +652,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       for (int qb = 0; qb < kQueryBlocks; ++qb) s[qb][kb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&k_lds[cur][koff[c] + 32 * kb * kKStride]);
+        const bf16x8 ka = k_read(cur, c, kb);
 #pragma unroll
         for (int qb = 0; qb < kQueryBlocks; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[qb][kb], 0, 0, 0);
@@ -638,8 +689,10 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][i], c2, mneg));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][i + 1], c2, mneg));
+          const float x0 = __builtin_fmaf(s[qb][kb][i], c2, mneg);
+          const float x1 = __builtin_fmaf(s[qb][kb][i + 1], c2, mneg);
+          const float p0 = BCA_EXP_POLY == 1 ? exp2_fma(x0) : __builtin_amdgcn_exp2f(x0);
+          const float p1 = BCA_EXP_POLY != 0 ? exp2_fma(x1) : __builtin_amdgcn_exp2f(x1);
           const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
           pb[qb][2 * kb + (i >> 3)][i & 7] = pp[0];
           pb[qb][2 * kb + (i >> 3)][(i & 7) + 1] = pp[1];
@@ -684,10 +737,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     for (int kc = 0; kc < 2 * kKeyBlocks; ++kc) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const bf16x4 lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&v_lds[cur][voff[0][d] + 16 * kc * kVStride]);
-        const bf16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&v_lds[cur][voff[1][d] + 16 * kc * kVStride]);
+        const bf16x4 lo = v_read(cur, 0, d, kc);
+        const bf16x4 hi = v_read(cur, 1, d, kc);
         const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int qb = 0; qb < kQueryBlocks; ++qb)
@@ -705,8 +756,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       if (j + 2 < j_end) dma_tile((j + 2) * kBlockN, cur);
     } else {
       if (j + 1 < j_end) {
-        write_k(k_lds[cur ^ 1], n0 + kBlockN);
-        write_v(v_lds[cur ^ 1], n0 + kBlockN);
+        write_k(k_lds(cur ^ 1), n0 + kBlockN);
+        write_v(v_lds(cur ^ 1), n0 + kBlockN);
       }
       if (j + 2 < j_end) {
         stage_k((j + 2) * kBlockN);
@@ -717,8 +768,25 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   };
   // tiles [0, n_full) lie entirely below every row's limit; the rest need the mask
   const int n_full = min(j_end, kv_full / kBlockN);
-  for (int j = j_begin; j < n_full; ++j) tile_step(std::false_type{}, j);
-  for (int j = max(j_begin, n_full); j < j_end; ++j) tile_step(std::true_type{}, j);
+  if constexpr (kConstBuf) {
+    // two tiles per trip, buffer 0 then buffer 1, so that each copy names its buffer by a constant
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
+    auto run = [&](auto masked_c, int lo, int hi) {
+      int j = lo;
+      if (j < hi && (j & 1)) tile_step(masked_c, j++, Buf1{});
+      for (; j + 1 < hi; j += 2) {
+        tile_step(masked_c, j, Buf0{});
+        tile_step(masked_c, j + 1, Buf1{});
+      }
+      if (j < hi) tile_step(masked_c, j, Buf0{});
+    };
+    run(std::false_type{}, j_begin, n_full);
+    run(std::true_type{}, max(j_begin, n_full), j_end);
+  } else {
+    for (int j = j_begin; j < n_full; ++j) tile_step(std::false_type{}, j, j & 1);
+    for (int j = max(j_begin, n_full); j < j_end; ++j) tile_step(std::true_type{}, j, j & 1);
+  }
 
   // ---- split epilogue: this key range's unnormalised O, running max m (scaled, base 2) and row
   // sum l, to be merged by split_combine.  Layout [split][b][row][h] (x 128 for O).
