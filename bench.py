@@ -13,6 +13,7 @@ Prints ONE JSON line on stdout.  Diagnostics go to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -93,6 +94,24 @@ def cpu_baseline(W, lay, ids, P, N, budget_rows, heads):
     }
 
 
+# Untimed run-in before each measurement.  The card lowers its clocks while it idles (the host
+# generates the next inputs between measurements) and raises them over the first tens of
+# milliseconds of sustained load; the first dispatches of a cold run are up to a third slower.
+SETTLE = {"main_ms": 500.0, "extra_ms": 200.0}
+
+
+def settle(torch, fn, ms):
+    """Calls fn (one unit of the work about to be timed) untimed for `ms` of wall time."""
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od, flops_pre, flops_dec, Bd, S, H, P,
                 dev, iters=10):
     """The same prefill and decode calls with the prefix cache stored as FP8 E4M3 (V only, then
@@ -107,11 +126,14 @@ def fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od, flops_pre, flops_dec,
         q2, k2, v2 = (to_dev(torch, x, dev) for x in W.qkv(W.SEEDS["edit_2ref_cfg"], Bd, S, H))
         bca.prefill_ex(plan, q2, k2, v2, c2)
         del q2, k2, v2
-        for i in range(3):
-            qt, kt, vt = sets[i % len(sets)]
+        n_unit = [0]
+
+        def unit():
+            qt, kt, vt = sets[n_unit[0] % len(sets)]
+            n_unit[0] += 1
             bca.prefill_ex(plan, q, k, v, c1, out=o)
             bca.decode_ex(plan, qt, c2, kt, vt, out=od)
-        torch.cuda.synchronize()
+        settle(torch, unit, SETTLE["extra_ms"])
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record()
         for i in range(iters):
@@ -169,9 +191,8 @@ def prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev, iters=20):
     for name, B, rows, tab in (("prefill_b1", 1, S, table), ("target_b2", Bd, N, table[S - N:].contiguous())):
         qb, kb, _, _ = W.prologue_inputs(7, B, rows, H)
         q, k = to_dev(torch, qb, dev), to_dev(torch, kb, dev)
-        for _ in range(3):
-            bca.qk_prologue(q, k, wq, wk, tab, q_out=q, k_out=k)
-        torch.cuda.synchronize()
+        settle(torch, lambda: bca.qk_prologue(q, k, wq, wk, tab, q_out=q, k_out=k),
+               SETTLE["extra_ms"])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(iters):
@@ -196,9 +217,7 @@ def varlen_timing(torch, bca, W, dev, H, iters=10):
     R = int(sum(lens))
     q, k, v = (to_dev(torch, x[0], dev) for x in W.qkv(17, 1, R, H))
     o = torch.empty((R, H, HEAD_DIM), dtype=torch.float32, device=dev)
-    for _ in range(2):
-        bca.prefill_varlen(plan, q, k, v, out=o)
-    torch.cuda.synchronize()
+    settle(torch, lambda: bca.prefill_varlen(plan, q, k, v, out=o), SETTLE["extra_ms"])
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
@@ -235,9 +254,7 @@ def split_decode_timing(torch, bca, W, dev, iters=20):
            "useful_gflop": round(flops / 1e9, 2)}
     for name, fn in (("plain", lambda: bca.decode_ex(plan, q, cache, k, v, out=o)),
                      ("split", lambda: bca.decode_split(plan, q, cache, k, v, workspace=ws, out=o))):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        settle(torch, fn, SETTLE["extra_ms"])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(iters):
@@ -257,6 +274,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE["main_ms"],
+                    help="untimed steps for this long before the warm-up steps (the side "
+                         "measurements get up to 200 ms each): the GPU's clocks ramp up over the "
+                         "first tens of milliseconds of sustained load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=12400,
                     help="prefill rows in the CPU-oracle sample")
@@ -321,6 +342,10 @@ def main():
     od = torch.empty((Bd, N, H, HEAD_DIM), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log(f"setup done: S={S} P={P} N={N} useful pairs/head={pairs} plan {plan_ms:.2f} ms")
+    # no garbage-collector pauses inside a timed loop (a host stall leaves the GPU idle between
+    # launches, and that idle time would count)
+    gc.collect()
+    gc.disable()
 
     flops_pre = 4.0 * HEAD_DIM * H * pairs
     flops_dec = 4.0 * HEAD_DIM * Bd * H * N * (P + N)
@@ -336,6 +361,15 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    # clock run-in (see SETTLE), then the warm-up steps
+    SETTLE["main_ms"] = args.settle_ms
+    SETTLE["extra_ms"] = min(SETTLE["extra_ms"], args.settle_ms)
+    n_run = [0]
+
+    def run_in_step():
+        step(n_run[0])
+        n_run[0] += 1
+    n_settle = settle(torch, run_in_step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -385,6 +419,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "settle": {"ms": args.settle_ms, "steps": n_settle},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)/sqrt(128) bf16 Q/K/V)",
         "config": {
