@@ -425,10 +425,11 @@ bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale
 namespace {
 
 // Key ranges of a split decode: the requested count (0 = enough workgroups for about four per
-// CU, each range at least 8 key tiles), at most one per key tile, and no empty range.
+// CU, each range at least 8 units of 64 keys), at most one per unit, and no empty range.
 void split_shape(const bca::HostPlan& hp, int32_t B, int32_t H, int32_t n_split,
                  int32_t* n_used, int32_t* tiles_per) {
-  const int64_t ktiles = (hp.prefix_len + hp.target_len + bca::kDecodeBlockN - 1) / bca::kDecodeBlockN;
+  // in units of kSplitUnit keys, the same for every cache format
+  const int64_t ktiles = (hp.prefix_len + hp.target_len + bca::kSplitUnit - 1) / bca::kSplitUnit;
   const int64_t nt = (hp.target_len + bca::kBlockM - 1) / bca::kBlockM;
   int64_t want = n_split;
   if (want == 0) {
@@ -517,7 +518,7 @@ bca_status decode_impl(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   a.scale_log2 = scale_log2;
   a.n_split = n_used;
   if (n_used > 1) {
-    a.split_tiles = per;
+    a.split_units = per;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = a.part_o + (int64_t)n_used * B * N * H * bca::kHeadDim;
   }

@@ -21,9 +21,10 @@ constexpr int kHeadDim = 128;  // the only head width the kernels are built for
 constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
 constexpr int kWaves = BCA_WAVES;
 constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup (= plan tile)
-// Keys per key tile (32 or 64) and waves per SIMD, per call.  32-key tiles need fewer registers
-// and half the LDS, which lets the prefill run 3 waves per SIMD; the decode keeps 64-key tiles
-// at 2 waves per SIMD (measured faster for each).
+// Keys per key tile (32 or 64) and waves per SIMD, per kernel.  32-key tiles need fewer registers
+// and half the LDS, which lets the prefill and the bf16-cache decode (both filled by direct loads)
+// run 3 waves per SIMD; the decode over an FP8 cache, which dequantises through registers, keeps
+// 64-key tiles at 2 waves per SIMD (measured fastest for each).
 #ifndef BCA_PREFILL_BLOCK_N
 #define BCA_PREFILL_BLOCK_N 32
 #endif
@@ -36,10 +37,23 @@ constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup
 #ifndef BCA_DECODE_WAVES_PER_SIMD
 #define BCA_DECODE_WAVES_PER_SIMD 2
 #endif
+#ifndef BCA_DECODE_DIRECT_BLOCK_N
+#define BCA_DECODE_DIRECT_BLOCK_N 32
+#endif
+#ifndef BCA_DECODE_DIRECT_WAVES_PER_SIMD
+#define BCA_DECODE_DIRECT_WAVES_PER_SIMD 3
+#endif
 constexpr int kPrefillBlockN = BCA_PREFILL_BLOCK_N;
 constexpr int kPrefillWavesPerSimd = BCA_PREFILL_WAVES_PER_SIMD;
-constexpr int kDecodeBlockN = BCA_DECODE_BLOCK_N;
+constexpr int kDecodeBlockN = BCA_DECODE_BLOCK_N;  // register-staged decode (FP8 caches)
 constexpr int kDecodeWavesPerSimd = BCA_DECODE_WAVES_PER_SIMD;
+constexpr int kDecodeDirectBlockN = BCA_DECODE_DIRECT_BLOCK_N;  // direct-fill decode (bf16 cache)
+constexpr int kDecodeDirectWavesPerSimd = BCA_DECODE_DIRECT_WAVES_PER_SIMD;
+// A split decode's key ranges are whole multiples of kSplitUnit keys, whatever the kernel's tile
+// width (which divides it), so the workspace a plan needs does not depend on the cache format.
+constexpr int kSplitUnit = 64;
+static_assert(kSplitUnit % kDecodeBlockN == 0 && kSplitUnit % kDecodeDirectBlockN == 0,
+              "split units hold whole key tiles");
 
 // Prefix-cache storage formats (values of bca_cache_format).
 constexpr int kCacheBf16 = 0;   // K and V bf16
@@ -94,11 +108,11 @@ struct AttnArgs {
   float* vcs;
   int64_t vcs_sb, vcs_ss, vcs_sh;
   int32_t cache_fmt;  // kCacheBf16 / kCacheFp8V / kCacheFp8KV
-  // Decode only: key ranges of split_tiles key tiles each, n_split of them (1 = no split), whose
-  // partial results go to part_o [n_split][B][N][H][D] and part_ml [n_split][B][N][H][2] (m, l)
-  // and are merged into o by a second kernel.
+  // Decode only: key ranges of split_units x kSplitUnit keys each, n_split of them (1 = no
+  // split), whose partial results go to part_o [n_split][B][N][H][D] and part_ml
+  // [n_split][B][N][H][2] (m, l) and are merged into o by a second kernel.
   int32_t n_split;
-  int32_t split_tiles;
+  int32_t split_units;
   float* part_o;
   float* part_ml;
 };

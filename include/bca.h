@@ -242,8 +242,10 @@ bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float
 /*
  * bca_cache_dequantize -- writes a prefix cache of any format back as bf16: k_out, v_out bf16
  * [B, P, H, D] receive E4M3(code) * scale formed in fp32 and rounded to bf16 (RNE) for a quantised
- * tensor, a copy for a bf16 one.  That is the value bca_decode_ex uses for the same code, so
- * bca_decode over the expanded cache gives bitwise the result of bca_decode_ex over the FP8 one.
+ * tensor, a copy for a bf16 one.  That is the value bca_decode_ex uses for the same code, so the
+ * decode over the expanded cache sees bitwise the K and V of bca_decode_ex over the FP8 one (the
+ * two outputs agree to rounding: the bf16 and FP8 decodes walk the keys in tiles of different
+ * width).
  * Meant for expanding one layer's FP8 cache into a transient buffer just before that layer's
  * cached step (the FP8 form keeps the memory of all layers; the bf16 decode is the faster one).
  * The outputs must not overlap the cache.  D must be 128.  Enqueues one kernel on stream.
@@ -298,16 +300,16 @@ bca_status bca_qk_prologue(int32_t B, int64_t S, int32_t H, int32_t D, float eps
  * Split-KV decode.  The cached step of bca_decode_ex (same arguments and result; the guide's
  * section "Two exact attention paths, with different operating requirements") for targets too
  * small to fill the GPU, e.g. a 512 x 512 target (N = 1,024) under a long prefix: each
- * (batch, head, query tile) is cut into n_split ranges of key tiles handled by separate
- * workgroups.  Each range leaves its unnormalised output, running maximum m (base 2, scaled) and
+ * (batch, head, query tile) is cut into n_split key ranges, each a whole number of 64-key
+ * units (the last may be shorter), handled by separate workgroups.  Each range leaves its unnormalised output, running maximum m (base 2, scaled) and
  * row sum l in a caller workspace; a second kernel merges them:
  *     O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,   M = max_c m_c,
  * which is the same softmax up to rounding.
  *
  * bca_decode_split_workspace -- HOST.  *bytes = workspace bytes for (plan, B, H, n_split);
  * n_split = 0 lets the library choose (enough workgroups for about four per CU, ranges of at
- * least 8 key tiles); *n_split_used (may be NULL) = the number of ranges it will use (1 = plain
- * decode, bytes = 0).  The plan's last block must be an image block (else BCA_ERR_NO_DECODE).
+ * least 8 units of 64 keys; at most one range per unit); *n_split_used (may be NULL) = the number
+ * of ranges it will use (1 = plain decode, bytes = 0).  Neither depends on the cache format.  The plan's last block must be an image block (else BCA_ERR_NO_DECODE).
  *
  * bca_decode_split -- as bca_decode_ex, plus n_split (>= 0) and a DEVICE workspace of at least
  * that many bytes, 16-byte aligned, owned by the caller and not used by anything else while the

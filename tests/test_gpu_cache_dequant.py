@@ -4,9 +4,11 @@
   every value must be the exact product E4M3(code) * scale rounded to fp32, then to bf16 (RNE),
   bit for bit, and within half a bf16 ulp (plus an fp32 one) of the exact product.  Rows of zeros
   (scale 1) and rows of tiny values (floored scale) are included; a bf16 tensor is copied.
-* Decoding over the expanded cache with the bf16 decode gives bitwise the decode over the FP8
-  cache itself (both see the same bf16 K and V), on a random layout and on the two-reference
-  editing shape at full size (P = 8,304, N = 4,096, H = 32).
+* Decoding over the expanded cache with the bf16 decode matches the oracle's decode over the
+  oracle's FP8 cache, and the decode over the FP8 cache itself to the same tolerance (both see the
+  same bf16 K and V, but the bf16 decode walks 32-key tiles and the FP8 decode 64-key tiles, so
+  their running maxima, and p's bf16 rounding, differ), on a random layout and on the
+  two-reference editing shape at full size (P = 8,304, N = 4,096, H = 32).
 * Strided (non-contiguous) inputs and outputs.
 """
 import numpy as np
@@ -145,21 +147,25 @@ def _fp8_decode_pair(ids, B, H, fmt, seed):
     return plan, (qb, kb, vb), fused, expanded
 
 
+def check(got, ref, what):
+    err = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    say(f"  {what}: max|err|={err.max():.3e} mean|err|={err.mean():.3e}")
+    assert np.isfinite(got).all() and err.max() <= MAX_TOL and err.mean() <= MEAN_TOL, what
+
+
 @pytest.mark.parametrize("fmt", [bca.KVCache.FP8_V, bca.KVCache.FP8_KV])
-def test_decode_over_expansion_is_the_fp8_decode(fmt):
+def test_decode_over_expansion_matches_the_fp8_decode(fmt):
     rng = np.random.default_rng(77)
     ids = W.random_layout(rng, 1100, max_seg=250)
     ids[-200:] = 10 ** 6
     B, H = 2, 2
     say(f"case: decode over expansion fmt={fmt}")
     plan, (qb, kb, vb), fused, expanded = _fp8_decode_pair(ids, B, H, fmt, 77)
-    assert torch.equal(fused, expanded)
     P = plan.info.prefix_len
     oc = O.prefix_cache_fp8(f32(kb), f32(vb), ids, fmt)
     ref = O.decode_cached(f32(qb[:, P:]), oc, f32(kb[:, P:]), f32(vb[:, P:]))
-    err = np.abs(expanded.cpu().numpy().astype(np.float64) - ref)
-    say(f"  vs oracle: max|err|={err.max():.3e} mean|err|={err.mean():.3e}")
-    assert err.max() <= MAX_TOL and err.mean() <= MEAN_TOL
+    check(expanded.cpu().numpy(), ref, "expanded, bf16 decode vs oracle")
+    check(expanded.cpu().numpy(), fused.cpu().numpy(), "expanded vs the FP8 decode")
 
 
 @pytest.mark.parametrize("fmt", [bca.KVCache.FP8_V, bca.KVCache.FP8_KV])
@@ -169,4 +175,4 @@ def test_decode_over_expansion_full_size(fmt):
     plan, _, fused, expanded = _fp8_decode_pair(lay.block_ids(), 1, lay.heads, fmt,
                                                 W.SEEDS["edit_2ref"])
     assert (plan.info.prefix_len, plan.info.target_len) == (8304, 4096)
-    assert torch.equal(fused, expanded)
+    check(expanded.cpu().numpy(), fused.cpu().numpy(), "expanded vs the FP8 decode, full size")
