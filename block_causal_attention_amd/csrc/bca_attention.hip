@@ -10,7 +10,8 @@
 //
 // Work decomposition.  One workgroup = kWaves waves = one tile of kBlockM query rows of one
 // (batch, head); a wave owns kQueryBlocks blocks of 32 rows.  Per key tile of kBlockN keys (32
-// in the prefill, which then fits 3 waves per SIMD; 64 in the decode, at 2 waves per SIMD):
+// in the prefill and the bf16-cache decode, which then fit 3 waves per SIMD; 64 in the
+// FP8-cache decode, at 2 waves per SIMD):
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q rows held in VGPRs.
 //                 The accumulator gives each lane ONE query (lane % 32) and 16 keys, so the row
 //                 max is an in-lane reduction plus one swap of the two 32-lane halves.
@@ -26,12 +27,14 @@
 //                 is permuted identically in A and B, which leaves the sum unchanged.
 // K/V tiles go through a two-buffer LDS ring with one barrier per tile: tile j+1 is in flight
 // while tile j is computed.  Two ways to fill the ring (template parameter kDirect):
-//   register staging (decode): 16-byte global loads into VGPRs, written to LDS one tile later;
-//                 the per-row cache/target source choice stays in registers;
-//   direct (prefill): buffer_load_dwordx4 ... lds writes each wave's 1 KB straight into LDS,
-//                 with a fixed per-lane offset and the tile's position in the descriptor.
-// Either way LDS rows are unpadded with an XOR swizzle of their 16-byte chunks (below) that keeps
-// the K reads and the transposed V reads free of bank conflicts.
+//   register staging (FP8-cache decode): 16-byte global loads into VGPRs, dequantised and
+//                 written to LDS one tile later;
+//   direct (prefill, bf16-cache decode): buffer_load_dwordx4 ... lds writes each wave's 1 KB
+//                 straight into LDS, with a fixed per-lane offset and the tile's position in the
+//                 descriptor.
+// Direct fills write unpadded rows, with an XOR swizzle of their 16-byte chunks (below) that
+// keeps the K reads and the transposed V reads free of bank conflicts; staged fills write padded
+// rows.
 #include <type_traits>
 
 #include "bca_internal.h"
