@@ -394,7 +394,8 @@ def main():
 
     # the dominant kernel: the call with the larger share of the step
     if dec_ms.mean() >= pre_ms.mean():
-        dom, key, achieved = "decode: attn_decode_direct (bf16 cache), B=2", "decode_cfg_b2", dec_tf
+        dom, key, achieved = ("decode: attn_decode_direct<12> (bf16 cache), B=2", "decode_cfg_b2",
+                              dec_tf)
     else:
         dom, key, achieved = ("prefill: attn_prefill<0> (writes the bf16 prefix cache), B=1",
                               "prefill_b1", pre_tf)

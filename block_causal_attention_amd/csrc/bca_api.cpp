@@ -430,7 +430,8 @@ void split_shape(const bca::HostPlan& hp, int32_t B, int32_t H, int32_t n_split,
                  int32_t* n_used, int32_t* tiles_per) {
   // in units of kSplitUnit keys, the same for every cache format
   const int64_t ktiles = (hp.prefix_len + hp.target_len + bca::kSplitUnit - 1) / bca::kSplitUnit;
-  const int64_t nt = (hp.target_len + bca::kBlockM - 1) / bca::kBlockM;
+  // query tiles counted in 128-row units, also independent of the format
+  const int64_t nt = (hp.target_len + 127) / 128;
   int64_t want = n_split;
   if (want == 0) {
     const int64_t base = nt * B * H;
@@ -472,7 +473,8 @@ bca_status decode_impl(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   const int64_t N = hp.target_len;
   if ((s = check_extent(k_tgt, "k_tgt", N)) != BCA_OK) return s;
   if ((s = check_extent(v_tgt, "v_tgt", N)) != BCA_OK) return s;
-  const int64_t nt = (N + bca::kBlockM - 1) / bca::kBlockM;
+  // the largest grid any decode kernel takes (launch_decode picks the kernel and its tiles)
+  const int64_t nt = (N + bca::kDecodeMinBlockM - 1) / bca::kDecodeMinBlockM;
   int32_t n_used = 1, per = 0;
   if (split_call) {
     if (n_split < 0) return fail(BCA_ERR_ARG, "n_split must be >= 0 (0 = chosen by the library)");
@@ -514,7 +516,6 @@ bca_status decode_impl(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   a.split = (int32_t)hp.prefix_len;
   a.heads = H;
   a.batch = B;
-  a.n_qtiles = (int32_t)nt;
   a.scale_log2 = scale_log2;
   a.n_split = n_used;
   if (n_used > 1) {

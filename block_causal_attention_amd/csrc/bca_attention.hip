@@ -8,10 +8,12 @@
 // visible (kv_end); this kernel walks key tiles [0, kv_end), masks only the tiles that cross a
 // row limit, and never loads the rest.  Decode is the same kernel with no mask except the tail.
 //
-// Work decomposition.  One workgroup = kWaves waves = one tile of kBlockM query rows of one
-// (batch, head); a wave owns kQueryBlocks blocks of 32 rows.  Per key tile of kBlockN keys (32
-// in the prefill and the bf16-cache decode, which then fit 3 waves per SIMD; 64 in the
-// FP8-cache decode, at 2 waves per SIMD):
+// Work decomposition.  One workgroup = kW waves = one tile of 32 kW query rows of one (batch,
+// head); a wave owns kQueryBlocks blocks of 32 rows.  The prefill and the bf16-cache decode run
+// 12 waves (384 rows, one workgroup per CU at 3 waves per SIMD, so each K/V tile in LDS serves
+// 384 rows; a small decode grid runs 4), the FP8-cache decode 4.  Per key tile of kBlockN keys
+// (32 in the prefill and the bf16-cache decode; 64 in the FP8-cache decode, at 2 waves per
+// SIMD):
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q rows held in VGPRs.
 //                 The accumulator gives each lane ONE query (lane % 32) and 16 keys, so the row
 //                 max is an in-lane reduction plus one swap of the two 32-lane halves.
@@ -29,12 +31,13 @@
 // while tile j is computed.  Two ways to fill the ring (template parameter kDirect):
 //   register staging (FP8-cache decode): 16-byte global loads into VGPRs, dequantised and
 //                 written to LDS one tile later;
-//   direct (prefill, bf16-cache decode): buffer_load_dwordx4 ... lds writes each wave's 1 KB
-//                 straight into LDS, with a fixed per-lane offset and the tile's position in the
-//                 descriptor.
+//   direct (prefill, bf16-cache decode): buffer_load_dwordx4 ... lds writes 1 KB (4 rows)
+//                 straight into LDS per instruction, the tile's fills dealt round-robin over the
+//                 waves, with a fixed per-lane offset and the tile's position in the descriptor.
 // Direct fills write unpadded rows, with an XOR swizzle of their 16-byte chunks (below) that
 // keeps the K reads and the transposed V reads free of bank conflicts; staged fills write padded
 // rows.
+#include <atomic>
 #include <type_traits>
 
 #include "bca_internal.h"
@@ -52,16 +55,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The bf16-cache decode through the register-staged path instead of direct fills (build
-// option; measured 4% slower).
-#ifndef BCA_DECODE_STAGED_BF16
-#define BCA_DECODE_STAGED_BF16 0
-#endif
 // While a wave issues its score or PV MFMAs it runs at raised priority, so the SIMD's arbiter
-// prefers waves that can feed the matrix core and the others fill the gaps with softmax work
-// (+2% on both kernels, interleaved A/B).
+// prefers waves that can feed the matrix core and the others fill the gaps with softmax work.
+// Measured per kernel (interleaved A/B): +2% for the prefill and the FP8-cache decode; the
+// bf16-cache decode with 12-wave workgroups runs 4% faster without it.
 #ifndef BCA_MFMA_PRIO
 #define BCA_MFMA_PRIO 1
+#endif
+#ifndef BCA_DECODE_DIRECT_MFMA_PRIO
+#define BCA_DECODE_DIRECT_MFMA_PRIO 0
+#endif
+#ifndef BCA_SKIP_DEAD_WAVES
+#define BCA_SKIP_DEAD_WAVES 0
 #endif
 #ifndef BCA_V_PAD
 #define BCA_V_PAD 16
@@ -75,8 +80,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define BCA_EXP_POLY 0
 #endif
 constexpr bool kStageSwizzle = BCA_STAGE_SWIZZLE;  // swizzled rows for the staging path too
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerPass = kThreads / 16;  // staging: rows per pass
+
 // A row's running max is raised only when its scores grew by more than kRescaleThreshold (log2
 // units), so p <= 2^16: exact in fp32, within bf16's exponent range, and l, O stay far below
 // fp32 overflow.  A lane's tile sum above kRescaleBound is what sends a wave to the exact path.
@@ -166,22 +170,27 @@ __device__ inline u32x2 quantize_row8(u32x4 x, float* scale_out) {
   return u32x2{(uint32_t)w0, (uint32_t)w1};
 }
 
-// The body of both kernels.  kBlockN keys per key tile (32 or 64) is chosen per call, and so is
-// the occupancy (set on the kernels below): the prefill runs 32-key tiles at 3 waves per SIMD,
-// the decode 64-key tiles at 2.
-template <bool kDecode, bool kDirect, int kFmt, int kBlockN>
+// The body of all the kernels.  kBlockN keys per key tile (32 or 64) and kW waves per workgroup
+// are chosen per kernel, and so is the occupancy (set on the kernels below).
+template <bool kDecode, bool kDirect, int kFmt, int kBlockN, int kW>
 __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
-  constexpr int kKeyBlocks = kBlockN / 32;                            // 32-key MFMA blocks
-  constexpr int kChunksPerThread = kBlockN * kHeadDim / 8 / kThreads;  // staging: 16 B chunks
-  constexpr int kDmaRowsPerWave = kBlockN / kWaves;                    // direct: rows per wave
-  constexpr int kDmaInstr = kDmaRowsPerWave / 4;                       // direct: 4 rows per instr
+  constexpr int kThreads = 64 * kW;
+  constexpr int kRows = 32 * kQueryBlocks * kW;  // query rows per workgroup
+  constexpr int kRowsPerPass = kThreads / 16;    // staging: rows per pass
+  constexpr int kKeyBlocks = kBlockN / 32;       // 32-key MFMA blocks
+  // staging: 16-byte chunks per thread (the last pass may be partial where the direct-fill
+  // kernels copy cache rows out of LDS this way)
+  constexpr int kChunksPerThread = (kBlockN * kHeadDim / 8 + kThreads - 1) / kThreads;
   static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
-  static_assert(kBlockN * kHeadDim / 8 % kThreads == 0, "whole 16-byte chunks per thread");
-  static_assert(kDmaRowsPerWave % 4 == 0, "direct loads: each wave fills whole 4-row groups");
+  static_assert(kDirect || kBlockN * kHeadDim / 8 % kThreads == 0,
+                "staged fills: whole 16-byte chunks per thread");
   // The prefill stores a quantised cache; the decode reads one (its first key source).
   constexpr bool kKq = kFmt == kCacheFp8KV;
   constexpr bool kVq = kFmt != kCacheBf16;
-  constexpr bool kPrio = BCA_MFMA_PRIO > 0;  // raise wave priority while issuing MFMAs
+  // wave priority while issuing MFMAs (0: never raised)
+  constexpr int kPrioLevel =
+      kDecode && kDirect && kW == kDecodeDirectWaves ? BCA_DECODE_DIRECT_MFMA_PRIO : BCA_MFMA_PRIO;
+  constexpr bool kPrio = kPrioLevel > 0;
   constexpr bool kKqSrc = kDecode && kKq;
   constexpr bool kVqSrc = kDecode && kVq;
   static_assert(!(kDirect && (kKqSrc || kVqSrc)), "direct loads move bf16 rows only");
@@ -203,13 +212,14 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBlockN * kVStride];
   __shared__ __attribute__((aligned(16))) __bf16 k_pair[2][kBlockN * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 v_pair[2][kBlockN * kVStride];
-  // Buffer `buf`: an int, or a std::integral_constant that names it at compile time.
+  // Buffer `buf`: an int, or a std::integral_constant that names it at compile time (the only
+  // form the separate arrays take).
   auto k_lds = [](auto buf) -> __bf16* {
-    if constexpr (kConstBuf) return buf ? k_lds1 : k_lds0;
+    if constexpr (kConstBuf) return decltype(buf)::value ? k_lds1 : k_lds0;
     else return k_pair[buf];
   };
   auto v_lds = [](auto buf) -> __bf16* {
-    if constexpr (kConstBuf) return buf ? v_lds1 : v_lds0;
+    if constexpr (kConstBuf) return decltype(buf)::value ? v_lds1 : v_lds0;
     else return v_pair[buf];
   };
 
@@ -242,7 +252,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // The tile's sequence (prefill plans may hold several): its first tensor row, the tile's first
   // local row, its length and where its row limits start.  Rows, keys and limits below are local
   // to the sequence; the decode has one sequence of n_q query rows over kv_len keys.
-  int seq_row0 = 0, row0 = tile * kBlockM, n_rows = a.n_q, rl_off = 0;
+  int seq_row0 = 0, row0 = tile * kRows, n_rows = a.n_q, rl_off = 0;
   int kv_end = a.kv_len, kv_full = a.kv_len;
   if constexpr (!kDecode) {
     const int32_t* td = a.tiles + tile * kTileInts;
@@ -258,6 +268,10 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const int split_tiles = a.split_units * (kSplitUnit / kBlockN);
   const int j_begin = n_split > 1 ? split * split_tiles : 0;
   const int j_end = n_split > 1 ? min(ntiles, j_begin + split_tiles) : ntiles;
+
+  // does any of this wave's query rows exist (wave-uniform)
+  const bool live = row0 + wave * 32 * kQueryBlocks < n_rows;
+  constexpr bool kSkipDead = BCA_SKIP_DEAD_WAVES;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
   int lim[kQueryBlocks];
@@ -388,7 +402,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // 16 consecutive threads write one whole 256-byte row, so the swizzle costs no conflicts here.
   // Rows ld_row + kRowsPerPass r share ld_row's swizzle (kRowsPerPass is a multiple of 16).
   const int st_col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(ld_row)) : ld_col;
-  static_assert(kRowsPerPass % 16 == 0, "staging passes keep the swizzle phase");
+  static_assert(kDirect || kRowsPerPass % 16 == 0, "staging passes keep the swizzle phase");
   // Rows of a quantised source (keys below split) are dequantised on the way into LDS.
   auto stage_write = [&](auto quant_c, __bf16* lds, int stride, const u32x4* st, int n0) {
     constexpr bool kQ = decltype(quant_c)::value;
@@ -414,42 +428,49 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   };
 
   // ---- filling the ring: direct loads ----------------------------------------------------------
-  // Wave w fills tile rows [w kDmaRowsPerWave, (w + 1) kDmaRowsPerWave), 4 rows per instruction:
-  // lane L writes LDS chunk L % 16 of row L / 16 of the instruction's 4-row group, so it fetches
-  // logical chunk (L % 16) ^ swz(row) of that key.
-  // The common case (whole tile from one source, nothing past kv_end) adds a tile-uniform base
-  // to per-lane offsets; a tile straddling the cache/target split or the end resolves each row.
+  // A tile is kFills load instructions of one 4-row group (4 x 256 bytes): K's kGroups groups,
+  // then V's.  Instruction n is issued by wave n % kW as that wave's fill n / kW.  Lane L writes
+  // LDS chunk L % 16 of row L / 16 of the group, so it fetches logical chunk (L % 16) ^ swz(row)
+  // of that key.  With kW a multiple of 4 every group a wave fills is congruent to the wave mod 4,
+  // so all its fills share one swizzle phase and the lane's offset inside a group is one VGPR per
+  // source stride.  The group's first row is added to it (prefill: its descriptor ends at the
+  // sequence's last row, and rows past it load as zero, which takes the whole offset inside the
+  // range check) or goes in the scalar offset (decode whole tiles, all in range; the scalar
+  // offset is outside the range check).
+  // The common case (whole tile from one source, nothing past kv_end) goes through a tile-wide
+  // descriptor; a decode tile straddling the cache/target split or the end resolves each row.
+  constexpr int kGroups = kBlockN / 4;
+  constexpr int kFills = 2 * kGroups;
+  constexpr int kFillsPerWave = (kFills + kW - 1) / kW;
+  static_assert(!kDirect || (kW % 4 == 0 && kGroups % 4 == 0), "one swizzle phase per wave");
   const int dma_r = lane >> 4;
   const int dma_p = lane & 15;
-  const int dma_row0 = wave * kDmaRowsPerWave + dma_r;  // + 4 i
-  // swz(row) for row = dma_row0 + 4 i: (row & 3) = dma_r and ((row >> 2) & 3) =
-  // (first row of the wave's slice / 4 + i) & 3, since the slice starts at a multiple of 4.
-  auto dma_col = [&](int i) {
-    return 8 * (dma_p ^ ((dma_r << 2) | ((wave * (kDmaRowsPerWave / 4) + i) & 3)));
+  auto fill_n = [&](int i) { return wave + kW * i; };  // wave-uniform
+  auto fill_is_v = [&](int i) { return fill_n(i) >= kGroups; };
+  auto fill_g = [&](int i) { return fill_is_v(i) ? fill_n(i) - kGroups : fill_n(i); };
+  auto fill_row = [&](int i) { return 4 * fill_g(i) + dma_r; };
+  // swz(row) = ((row & 3) << 2) | ((row >> 2) & 3) with row & 3 = dma_r and row >> 2 = the group
+  const int fill_col = 8 * (dma_p ^ ((dma_r << 2) | (wave & 3)));
+  // byte offset of this lane inside a 4-row group with row stride ss (elements)
+  auto lane_off = [&](int64_t ss) {
+    uint32_t off = ((uint32_t)dma_r * (uint32_t)ss + (uint32_t)fill_col) * 2u;
+    asm volatile("" : "+v"(off));
+    return off;
   };
-  // Prefill: buffer loads.  A lane's byte offset inside a tile is fixed (row and swizzled chunk),
-  // the tile's first key moves the descriptor base (scalar work only), and the descriptor ends
-  // at the last key row of the sequence, so rows past it read as zero: those keys lie at or past
-  // every row's limit and are masked.
-  // (The decode also keeps offsets for its second source, the target.)
-  uint32_t dma_koff[kDmaInstr], dma_voff[kDmaInstr], dma_k2off[kDmaInstr], dma_v2off[kDmaInstr];
+  // This wave's fills of a whole tile from descriptors kr and vr (row strides kss, vss; lane
+  // offsets koff, voff).
+  auto fill_whole = [&](__amdgpu_buffer_rsrc_t kr, int64_t kss, uint32_t koff,
+                        __amdgpu_buffer_rsrc_t vr, int64_t vss, uint32_t voff, auto buf) {
 #pragma unroll
-  for (int i = 0; i < kDmaInstr; ++i) {
-    const uint32_t row = (uint32_t)(dma_row0 + 4 * i), col = (uint32_t)dma_col(i);
-    dma_koff[i] = (row * (uint32_t)a.k_ss + col) * 2u;
-    dma_voff[i] = (row * (uint32_t)a.v_ss + col) * 2u;
-    dma_k2off[i] = (row * (uint32_t)a.k2_ss + col) * 2u;
-    dma_v2off[i] = (row * (uint32_t)a.v2_ss + col) * 2u;
-  }
-  auto dma_whole = [&](const uint16_t* kb, int64_t kss, const uint16_t* vb, int64_t vss,
-                       const uint32_t* koff, const uint32_t* voff, int buf) {
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kb, kss * 2);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vb, vss * 2);
-#pragma unroll
-    for (int i = 0; i < kDmaInstr; ++i) {
-      const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds(buf)[dst], 16, koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds(buf)[dst], 16, voff[i], 0, 0, 0);
+    for (int i = 0; i < kFillsPerWave; ++i) {
+      if (kFills % kW != 0 && fill_n(i) >= kFills) break;
+      const int r0 = 4 * fill_g(i);
+      const bool v = fill_is_v(i);
+      const uint32_t rows_off = (uint32_t)(r0 * (v ? vss : kss) * 2);
+      const uint32_t vo = kDecode ? (v ? voff : koff) : (v ? voff : koff) + rows_off;
+      const uint32_t so = kDecode ? rows_off : 0u;
+      __bf16* dst = (v ? v_lds(buf) : k_lds(buf)) + r0 * kHeadDim;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v ? vr : kr, (lds_void*)dst, 16, vo, so, 0, 0);
     }
   };
   auto dma_rsrc = [&](const uint16_t* base, int64_t ss, int n0) {
@@ -457,46 +478,44 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)n0 * ss), (short)0,
                                              (int)(uint32_t)bytes, kBufferWord3);
   };
-  auto dma_tile = [&](int n0, int buf) {
+  const uint32_t dma_k = kDirect ? lane_off(a.k_ss) : 0u, dma_v = kDirect ? lane_off(a.v_ss) : 0u;
+  const uint32_t dma_k2 = kDirect && kDecode ? lane_off(a.k2_ss) : 0u;
+  const uint32_t dma_v2 = kDirect && kDecode ? lane_off(a.v2_ss) : 0u;
+  auto dma_tile = [&](int n0, auto buf) {
     if constexpr (!kDecode) {
-      const __amdgpu_buffer_rsrc_t kr = dma_rsrc(k_base, a.k_ss, n0);
-      const __amdgpu_buffer_rsrc_t vr = dma_rsrc(v_base, a.v_ss, n0);
-#pragma unroll
-      for (int i = 0; i < kDmaInstr; ++i) {
-        const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&k_lds(buf)[dst], 16, dma_koff[i], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&v_lds(buf)[dst], 16, dma_voff[i], 0, 0, 0);
-      }
+      fill_whole(dma_rsrc(k_base, a.k_ss, n0), a.k_ss, dma_k, dma_rsrc(v_base, a.v_ss, n0), a.v_ss,
+                 dma_v, buf);
       return;
     }
     const bool in_end = n0 + kBlockN <= kv_end;
-    const bool src1 = !kDecode || n0 + kBlockN <= a.split;
-    const bool src2 = kDecode && n0 >= a.split;
+    const bool src1 = n0 + kBlockN <= a.split;
+    const bool src2 = n0 >= a.split;
     // decode: whole tiles from one source through buffer loads, the rest row by row below
     if (in_end && src1) {
-      dma_whole(k_base + (int64_t)n0 * a.k_ss, a.k_ss, v_base + (int64_t)n0 * a.v_ss, a.v_ss,
-                dma_koff, dma_voff, buf);
+      fill_whole(tile_rsrc(k_base + (int64_t)n0 * a.k_ss, a.k_ss * 2), a.k_ss, dma_k,
+                 tile_rsrc(v_base + (int64_t)n0 * a.v_ss, a.v_ss * 2), a.v_ss, dma_v, buf);
       return;
     }
     if (in_end && src2) {
-      dma_whole(k2_base + (int64_t)(n0 - a.split) * a.k2_ss, a.k2_ss,
-                v2_base + (int64_t)(n0 - a.split) * a.v2_ss, a.v2_ss, dma_k2off, dma_v2off, buf);
+      fill_whole(tile_rsrc(k2_base + (int64_t)(n0 - a.split) * a.k2_ss, a.k2_ss * 2), a.k2_ss,
+                 dma_k2, tile_rsrc(v2_base + (int64_t)(n0 - a.split) * a.v2_ss, a.v2_ss * 2),
+                 a.v2_ss, dma_v2, buf);
       return;
     }
 #pragma unroll
-    for (int i = 0; i < kDmaInstr; ++i) {
-      const int row = dma_row0 + 4 * i;
-      const int col = dma_col(i);
+    for (int i = 0; i < kFillsPerWave; ++i) {
+      if (kFills % kW != 0 && fill_n(i) >= kFills) break;
+      const bool v = fill_is_v(i);
       // keys past the end fetch row kv_end - 1 (masked, finite)
-      const int key = min(n0 + row, kv_end - 1);
+      const int key = min(n0 + fill_row(i), kv_end - 1);
       const bool first = key < a.split;
-      const uint16_t* kp = (first ? k_base + (int64_t)key * a.k_ss
-                                  : k2_base + (int64_t)(key - a.split) * a.k2_ss) + col;
-      const uint16_t* vp = (first ? v_base + (int64_t)key * a.v_ss
-                                  : v2_base + (int64_t)(key - a.split) * a.v2_ss) + col;
-      const int dst = (wave * kDmaRowsPerWave + 4 * i) * kHeadDim;
-      __builtin_amdgcn_global_load_lds((const void*)kp, (lds_void*)&k_lds(buf)[dst], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)vp, (lds_void*)&v_lds(buf)[dst], 16, 0, 0);
+      const uint16_t* p = v ? (first ? v_base + (int64_t)key * a.v_ss
+                                     : v2_base + (int64_t)(key - a.split) * a.v2_ss)
+                            : (first ? k_base + (int64_t)key * a.k_ss
+                                     : k2_base + (int64_t)(key - a.split) * a.k2_ss);
+      const int dst = 4 * fill_g(i) * kHeadDim;
+      __builtin_amdgcn_global_load_lds((const void*)(p + fill_col),
+                                       (lds_void*)&(v ? v_lds(buf) : k_lds(buf))[dst], 16, 0, 0);
     }
   };
 
@@ -505,7 +524,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // tiles; they are copied out of the LDS tile while it is resident, so no K/V row is fetched
   // twice.
   const int cache_lo = row0;
-  const int cache_hi = kDecode || a.kc == nullptr ? 0 : min(cache_lo + kBlockM, a.cache_len);
+  const int cache_hi = kDecode || a.kc == nullptr ? 0 : min(cache_lo + kRows, a.cache_len);
   // One 8-value chunk of cache row `key`: a bf16 copy, or (quantised tensor) 8 codes plus, from
   // the row's first lane, the row scale.  The quantised form reduces over the row's 16 lanes, so
   // every lane runs it; only the stores depend on `in`.
@@ -524,19 +543,24 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
                                 h * sh + ld_col) = x;
     }
   };
-  auto store_row = [&](int n0, int buf, int r) {
-    const int row = ld_row + kRowsPerPass * r;
+  // Chunk tid + kThreads r of the tile: row (tid >> 4) + kRowsPerPass r, chunk tid % 16.  In a
+  // partial last pass the rows past the tile re-read its last row and store nothing (whole
+  // 16-lane groups, so the quantiser's row reduction stays inside one row).
+  auto store_row = [&](int n0, auto buf, int r) {
+    const int row_raw = ld_row + kRowsPerPass * r;
+    const int row = min(row_raw, kBlockN - 1);
     const int key = n0 + row;
-    const bool in = key >= cache_lo && key < cache_hi;
+    const bool in = row_raw < kBlockN && key >= cache_lo && key < cache_hi;
     if (!(kKq || kVq) && !in) return;
-    const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds(buf)[row * kKStride + st_col]);
-    const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds(buf)[row * kVStride + st_col]);
+    const int col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(row)) : ld_col;
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds(buf)[row * kKStride + col]);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds(buf)[row * kVStride + col]);
     put_chunk(std::integral_constant<bool, kKq>{}, kx, a.kc, a.kc_ss, a.kc_sb, a.kc_sh, a.kcs,
               a.kcs_ss, a.kcs_sb, a.kcs_sh, key, in);
     put_chunk(std::integral_constant<bool, kVq>{}, vx, a.vc, a.vc_ss, a.vc_sb, a.vc_sh, a.vcs,
               a.vcs_ss, a.vcs_sb, a.vcs_sh, key, in);
   };
-  auto store_cache = [&](int n0, int buf) {
+  auto store_cache = [&](int n0, auto buf) {
     if (kDecode || n0 >= cache_hi || n0 + kBlockN <= cache_lo) return;
     // n0 made opaque: otherwise the compiler keeps this rare store's row pointers live across
     // the whole loop and advances them every tile
@@ -623,17 +647,27 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const float c2 = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // ---- prologue: the first tile resident in its buffer; the next one on its way ------------------
+  // ---- prologue ----------------------------------------------------------------------------------
+  // Tile j lives in buffer (j - j_begin) % 2.  Direct fills: the first two tiles resident.
+  // Staging: the first tile resident, the next one in registers.
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
   if constexpr (kDirect) {
-    dma_tile(j_begin * kBlockN, j_begin & 1);
-    if (j_begin + 1 < j_end) dma_tile((j_begin + 1) * kBlockN, (j_begin + 1) & 1);
+    auto prime = [&](int t, auto buf) {
+      if (j_begin + t < j_end) {
+        if constexpr (kConstBuf) dma_tile((j_begin + t) * kBlockN, buf);
+        else dma_tile((j_begin + t) * kBlockN, (int)decltype(buf)::value);
+      }
+    };
+    prime(0, Buf0{});
+    prime(1, Buf1{});
     __builtin_amdgcn_s_waitcnt(0);
   } else {
     const int first = j_begin * kBlockN;
     stage_k(first);
     stage_v(first);
-    write_k(k_lds(j_begin & 1), first);
-    write_v(v_lds(j_begin & 1), first);
+    write_k(k_lds(0), first);
+    write_v(v_lds(0), first);
     if (j_begin + 1 < j_end) {
       stage_k(first + kBlockN);
       stage_v(first + kBlockN);
@@ -641,118 +675,125 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   }
   __syncthreads();
 
-  // One key tile j from buffer cur = j & 1.  kMasked: the tile crosses some row's key limit.  Full
-  // tiles run in a loop of their own, with no mask code between the score MFMAs and the
-  // softmax, so the compiler can overlap the two inside one wave.
+  // One key tile j from buffer cur.  kMasked: the tile crosses some row's key limit.  Full tiles
+  // run in a loop of their own, with no mask code between the score MFMAs and the softmax, so the
+  // compiler can overlap the two inside one wave.
   auto tile_step = [&](auto masked_c, int j, auto cur) {
     constexpr bool kMasked = decltype(masked_c)::value;
     const int n0 = j * kBlockN;
     store_cache(n0, cur);
+    // A wave whose query rows all lie past the end (in a partial last tile) only fills and
+    // synchronises.
+    if (!kSkipDead || live) {
 
-    // ---- S^T = K Q^T
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(BCA_MFMA_PRIO);
-    f32x16 s[kQueryBlocks][kKeyBlocks];
+      // ---- S^T = K Q^T
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPrioLevel);
+      f32x16 s[kQueryBlocks][kKeyBlocks];
 #pragma unroll
-    for (int kb = 0; kb < kKeyBlocks; ++kb) {
+      for (int kb = 0; kb < kKeyBlocks; ++kb) {
 #pragma unroll
-      for (int qb = 0; qb < kQueryBlocks; ++qb) s[qb][kb] = f32x16{};
+        for (int qb = 0; qb < kQueryBlocks; ++qb) s[qb][kb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8 ka = k_read(cur, c, kb);
+        for (int c = 0; c < 8; ++c) {
+          const bf16x8 ka = k_read(cur, c, kb);
+#pragma unroll
+          for (int qb = 0; qb < kQueryBlocks; ++qb)
+            s[qb][kb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[qb][kb], 0, 0, 0);
+        }
+      }
+
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+      // ---- mask: only tiles that cross some row's limit.  Accumulator element i of key block kb
+      // holds key n0 + 32 kb + 8 (i / 4) + 4 half + i % 4.
+      if (kMasked) {
 #pragma unroll
         for (int qb = 0; qb < kQueryBlocks; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[qb][kb], 0, 0, 0);
-      }
-    }
-
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
-    // ---- mask: only tiles that cross some row's limit.  Accumulator element i of key block kb
-    // holds key n0 + 32 kb + 8 (i / 4) + 4 half + i % 4.
-    if (kMasked) {
 #pragma unroll
-      for (int qb = 0; qb < kQueryBlocks; ++qb)
+          for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+              if (key >= lim[qb]) s[qb][kb][i] = -__builtin_inff();
+            }
+      }
+
+      // ---- p = 2^(s c2 - m) against the running max m of earlier tiles, as bf16 P^T operands
+      // (chunks of 16 keys), plus this tile's row-sum share.  A row whose scores grew past
+      // m + kRescaleThreshold (or any row on its first tile, where m = -inf) shows a lane sum
+      // above 2^threshold (or inf); only then does the wave take the exact path: per-row max, raise
+      // and rescale for rows that grew by more than the threshold, and p recomputed.  Rows that do
+      // not raise recompute the same values, so each row still depends on its own scores alone.
+      bf16x8 pb[kQueryBlocks][2 * kKeyBlocks];
+      float tsum[kQueryBlocks];
+      auto exp_tile = [&](int qb) {
+        const float mneg = -m_run[qb];
+        float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= lim[qb]) s[qb][kb][i] = -__builtin_inff();
+          for (int i = 0; i < 16; i += 2) {
+            const float x0 = __builtin_fmaf(s[qb][kb][i], c2, mneg);
+            const float x1 = __builtin_fmaf(s[qb][kb][i + 1], c2, mneg);
+            const float p0 = BCA_EXP_POLY == 1 ? exp2_fma(x0) : __builtin_amdgcn_exp2f(x0);
+            const float p1 = BCA_EXP_POLY != 0 ? exp2_fma(x1) : __builtin_amdgcn_exp2f(x1);
+            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+            pb[qb][2 * kb + (i >> 3)][i & 7] = pp[0];
+            pb[qb][2 * kb + (i >> 3)][(i & 7) + 1] = pp[1];
+            if (i & 2)
+              acc1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc1, false);
+            else
+              acc0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc0, false);
           }
-    }
-
-    // ---- p = 2^(s c2 - m) against the running max m of earlier tiles, as bf16 P^T operands
-    // (chunks of 16 keys), plus this tile's row-sum share.  A row whose scores grew past
-    // m + kRescaleThreshold (or any row on its first tile, where m = -inf) shows a lane sum
-    // above 2^threshold (or inf); only then does the wave take the exact path: per-row max, raise
-    // and rescale for rows that grew by more than the threshold, and p recomputed.  Rows that do
-    // not raise recompute the same values, so each row still depends on its own scores alone.
-    bf16x8 pb[kQueryBlocks][2 * kKeyBlocks];
-    float tsum[kQueryBlocks];
-    auto exp_tile = [&](int qb) {
-      const float mneg = -m_run[qb];
-      float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float x0 = __builtin_fmaf(s[qb][kb][i], c2, mneg);
-          const float x1 = __builtin_fmaf(s[qb][kb][i + 1], c2, mneg);
-          const float p0 = BCA_EXP_POLY == 1 ? exp2_fma(x0) : __builtin_amdgcn_exp2f(x0);
-          const float p1 = BCA_EXP_POLY != 0 ? exp2_fma(x1) : __builtin_amdgcn_exp2f(x1);
-          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          pb[qb][2 * kb + (i >> 3)][i & 7] = pp[0];
-          pb[qb][2 * kb + (i >> 3)][(i & 7) + 1] = pp[1];
-          if (i & 2)
-            acc1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc1, false);
-          else
-            acc0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc0, false);
-        }
-      tsum[qb] = acc0 + acc1;
-    };
-    bool redo = false;
-#pragma unroll
-    for (int qb = 0; qb < kQueryBlocks; ++qb) {
-      exp_tile(qb);
-      redo = redo || !(tsum[qb] <= kRescaleBound);
-    }
-    if (__builtin_amdgcn_ballot_w64(redo)) {
+        tsum[qb] = acc0 + acc1;
+      };
+      bool redo = false;
 #pragma unroll
       for (int qb = 0; qb < kQueryBlocks; ++qb) {
-        float mx = s[qb][0][0];
-#pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-        mx = halves_max(mx);
-        const float m_cand = fmaxf(m_run[qb], mx * c2);
-        const bool raise = m_cand > m_run[qb] + kRescaleThreshold;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[qb] - m_cand) : 1.0f;  // 0 at first
-        m_run[qb] = raise ? m_cand : m_run[qb];
-        l_part[qb] *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) o[qb][d] *= alpha;
         exp_tile(qb);
+        redo = redo || !(tsum[qb] <= kRescaleBound);
       }
-    }
+      if (__builtin_amdgcn_ballot_w64(redo)) {
 #pragma unroll
-    for (int qb = 0; qb < kQueryBlocks; ++qb) l_part[qb] += tsum[qb];
-
-    // ---- O^T += V^T P^T
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(BCA_MFMA_PRIO);
+        for (int qb = 0; qb < kQueryBlocks; ++qb) {
+          float mx = s[qb][0][0];
 #pragma unroll
-    for (int kc = 0; kc < 2 * kKeyBlocks; ++kc) {
+          for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x4 lo = v_read(cur, 0, d, kc);
-        const bf16x4 hi = v_read(cur, 1, d, kc);
-        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+          mx = halves_max(mx);
+          const float m_cand = fmaxf(m_run[qb], mx * c2);
+          const bool raise = m_cand > m_run[qb] + kRescaleThreshold;
+          // (0 on the first tile)
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[qb] - m_cand) : 1.0f;
+          m_run[qb] = raise ? m_cand : m_run[qb];
+          l_part[qb] *= alpha;
 #pragma unroll
-        for (int qb = 0; qb < kQueryBlocks; ++qb)
-          o[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kc], o[qb][d], 0, 0, 0);
+          for (int d = 0; d < 4; ++d) o[qb][d] *= alpha;
+          exp_tile(qb);
+        }
       }
+#pragma unroll
+      for (int qb = 0; qb < kQueryBlocks; ++qb) l_part[qb] += tsum[qb];
+
+      // ---- O^T += V^T P^T
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPrioLevel);
+#pragma unroll
+      for (int kc = 0; kc < 2 * kKeyBlocks; ++kc) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x4 lo = v_read(cur, 0, d, kc);
+          const bf16x4 hi = v_read(cur, 1, d, kc);
+          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int qb = 0; qb < kQueryBlocks; ++qb)
+            o[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kc], o[qb][d], 0, 0, 0);
+        }
+      }
+
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     }
 
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     // ---- refill.  Staging: write tile j+1 into the other buffer (its tile j-1 was consumed
     // before the last barrier) and start fetching tile j+2.  Direct: tile j+1 was issued one
     // iteration ago; wait for it, then after the barrier reuse this buffer for tile j+2.
@@ -776,11 +817,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const int n_full = min(j_end, kv_full / kBlockN);
   if constexpr (kConstBuf) {
     // two tiles per trip, buffer 0 then buffer 1, so that each copy names its buffer by a constant
-    using Buf0 = std::integral_constant<int, 0>;
-    using Buf1 = std::integral_constant<int, 1>;
     auto run = [&](auto masked_c, int lo, int hi) {
       int j = lo;
-      if (j < hi && (j & 1)) tile_step(masked_c, j++, Buf1{});
+      if (j < hi && ((j - j_begin) & 1)) tile_step(masked_c, j++, Buf1{});
       for (; j + 1 < hi; j += 2) {
         tile_step(masked_c, j, Buf0{});
         tile_step(masked_c, j + 1, Buf1{});
@@ -790,8 +829,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     run(std::false_type{}, j_begin, n_full);
     run(std::true_type{}, max(j_begin, n_full), j_end);
   } else {
-    for (int j = j_begin; j < n_full; ++j) tile_step(std::false_type{}, j, j & 1);
-    for (int j = max(j_begin, n_full); j < j_end; ++j) tile_step(std::true_type{}, j, j & 1);
+    for (int j = j_begin; j < n_full; ++j) tile_step(std::false_type{}, j, (j - j_begin) & 1);
+    for (int j = max(j_begin, n_full); j < j_end; ++j)
+      tile_step(std::true_type{}, j, (j - j_begin) & 1);
   }
 
   // ---- split epilogue: this key range's unnormalised O, running max m (scaled, base 2) and row
@@ -875,27 +915,45 @@ __global__ __launch_bounds__(256) void split_combine(const AttnArgs a) {
 
 // Prefill: block-causal, direct-to-LDS fills, optional prefix-cache store in format kFmt.
 template <int kFmt>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(64 * kPrefillWaves)
 __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
 void attn_prefill(const AttnArgs a) {
-  attn_fwd<false, true, kFmt, kPrefillBlockN>(a);
+  attn_fwd<false, true, kFmt, kPrefillBlockN, kPrefillWaves>(a);
 }
 
 // Decode over [prefix cache in format kFmt ; target], register-staged fills: the FP8 caches,
 // which are dequantised on their way into LDS.
 template <int kFmt>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(64 * kStagedWaves)
 __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd, kDecodeWavesPerSimd)))
 void attn_decode(const AttnArgs a) {
-  attn_fwd<true, false, kFmt, kDecodeBlockN>(a);
+  attn_fwd<true, false, kFmt, kDecodeBlockN, kStagedWaves>(a);
 }
 
 // Decode over a bf16 cache: direct-to-LDS fills like the prefill's, 32-key tiles at 3 waves per
-// SIMD.
-__global__ __launch_bounds__(kThreads)
+// SIMD, kW waves per workgroup.
+template <int kW>
+__global__ __launch_bounds__(64 * kW)
 __attribute__((amdgpu_waves_per_eu(kDecodeDirectWavesPerSimd, kDecodeDirectWavesPerSimd)))
 void attn_decode_direct(const AttnArgs a) {
-  attn_fwd<true, true, kCacheBf16, kDecodeDirectBlockN>(a);
+  attn_fwd<true, true, kCacheBf16, kDecodeDirectBlockN, kW>(a);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 
@@ -903,28 +961,40 @@ void attn_decode_direct(const AttnArgs a) {
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
+  const dim3 block(64 * kPrefillWaves);
   switch (a.cache_fmt) {
-    case kCacheBf16: hipLaunchKernelGGL(attn_prefill<kCacheBf16>, grid, dim3(kThreads), 0, stream, a); break;
-    case kCacheFp8V: hipLaunchKernelGGL(attn_prefill<kCacheFp8V>, grid, dim3(kThreads), 0, stream, a); break;
-    case kCacheFp8KV: hipLaunchKernelGGL(attn_prefill<kCacheFp8KV>, grid, dim3(kThreads), 0, stream, a); break;
+    case kCacheBf16: hipLaunchKernelGGL(attn_prefill<kCacheBf16>, grid, block, 0, stream, a); break;
+    case kCacheFp8V: hipLaunchKernelGGL(attn_prefill<kCacheFp8V>, grid, block, 0, stream, a); break;
+    case kCacheFp8KV: hipLaunchKernelGGL(attn_prefill<kCacheFp8KV>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
+  AttnArgs a = args;
   const int n_split = a.n_split > 1 ? a.n_split : 1;
-  const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads * n_split);
+  const int64_t heads = (int64_t)a.batch * a.heads * n_split;
+  auto tiles = [&](int waves) {
+    const int rows = 32 * kQueryBlocks * waves;
+    return (a.n_q + rows - 1) / rows;
+  };
+  auto launch = [&](auto kernel, int waves) {
+    a.n_qtiles = tiles(waves);
+    const dim3 grid((unsigned)(a.n_qtiles * heads));
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream, a);
+  };
   switch (a.cache_fmt) {
     case kCacheBf16:
-#if BCA_DECODE_STAGED_BF16
-      hipLaunchKernelGGL(attn_decode<kCacheBf16>, grid, dim3(kThreads), 0, stream, a);
-#else
-      hipLaunchKernelGGL(attn_decode_direct, grid, dim3(kThreads), 0, stream, a);
-#endif
+      if (BCA_DECODE_STAGED_BF16)
+        launch(attn_decode<kCacheBf16>, kStagedWaves);
+      else if (tiles(kDecodeDirectWaves) * heads >= 2 * (int64_t)device_cus())
+        launch(attn_decode_direct<kDecodeDirectWaves>, kDecodeDirectWaves);
+      else
+        launch(attn_decode_direct<kDecodeDirectSmallWaves>, kDecodeDirectSmallWaves);
       break;
-    case kCacheFp8V: hipLaunchKernelGGL(attn_decode<kCacheFp8V>, grid, dim3(kThreads), 0, stream, a); break;
-    case kCacheFp8KV: hipLaunchKernelGGL(attn_decode<kCacheFp8KV>, grid, dim3(kThreads), 0, stream, a); break;
+    case kCacheFp8V: launch(attn_decode<kCacheFp8V>, kStagedWaves); break;
+    case kCacheFp8KV: launch(attn_decode<kCacheFp8KV>, kStagedWaves); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

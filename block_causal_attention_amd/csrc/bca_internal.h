@@ -10,21 +10,26 @@
 
 namespace bca {
 
-// Tile shape.  A wave owns kQueryBlocks blocks of 32 query rows; a workgroup has kWaves waves.
+// Tile shape.  A wave owns kQueryBlocks blocks of 32 query rows, and a workgroup's query rows
+// form one tile.  Per kernel: waves per workgroup, keys per key tile (32 or 64) and waves per
+// SIMD.  The prefill and the bf16-cache decode are filled by direct loads and run 32-key tiles
+// at 3 waves per SIMD; their workgroups have 12 waves (one workgroup per CU), so each K/V tile
+// loaded into LDS serves 384 query rows.  A decode whose 12-wave grid would not give every CU
+// two workgroups runs 4-wave ones instead.  The decode over an FP8 cache dequantises through
+// registers and keeps 4 waves, 64-key tiles and 2 waves per SIMD (measured fastest for each).
 #ifndef BCA_QUERY_BLOCKS
 #define BCA_QUERY_BLOCKS 1
 #endif
-#ifndef BCA_WAVES
-#define BCA_WAVES 4
+#ifndef BCA_PREFILL_WAVES
+#define BCA_PREFILL_WAVES 12
 #endif
-constexpr int kHeadDim = 128;  // the only head width the kernels are built for
-constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
-constexpr int kWaves = BCA_WAVES;
-constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup (= plan tile)
-// Keys per key tile (32 or 64) and waves per SIMD, per kernel.  32-key tiles need fewer registers
-// and half the LDS, which lets the prefill and the bf16-cache decode (both filled by direct loads)
-// run 3 waves per SIMD; the decode over an FP8 cache, which dequantises through registers, keeps
-// 64-key tiles at 2 waves per SIMD (measured fastest for each).
+#ifndef BCA_DECODE_DIRECT_WAVES
+#define BCA_DECODE_DIRECT_WAVES 12
+#endif
+// The bf16-cache decode through the staged kernel instead of the direct one (for comparisons).
+#ifndef BCA_DECODE_STAGED_BF16
+#define BCA_DECODE_STAGED_BF16 0
+#endif
 #ifndef BCA_PREFILL_BLOCK_N
 #define BCA_PREFILL_BLOCK_N 32
 #endif
@@ -43,6 +48,15 @@ constexpr int kBlockM = 32 * kQueryBlocks * kWaves;  // query rows per workgroup
 #ifndef BCA_DECODE_DIRECT_WAVES_PER_SIMD
 #define BCA_DECODE_DIRECT_WAVES_PER_SIMD 3
 #endif
+constexpr int kHeadDim = 128;  // the only head width the kernels are built for
+constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
+constexpr int kPrefillWaves = BCA_PREFILL_WAVES;
+constexpr int kDecodeDirectWaves = BCA_DECODE_DIRECT_WAVES;  // large decode grids
+constexpr int kDecodeDirectSmallWaves = 4;                     // small decode grids
+constexpr int kStagedWaves = 4;
+constexpr int kBlockM = 32 * kQueryBlocks * kPrefillWaves;  // prefill query tile (= plan tile)
+// Fewest query rows any decode workgroup takes (bounds the decode's grid).
+constexpr int kDecodeMinBlockM = 32 * kQueryBlocks * 4;
 constexpr int kPrefillBlockN = BCA_PREFILL_BLOCK_N;
 constexpr int kPrefillWavesPerSimd = BCA_PREFILL_WAVES_PER_SIMD;
 constexpr int kDecodeBlockN = BCA_DECODE_BLOCK_N;  // register-staged decode (FP8 caches)
@@ -90,7 +104,7 @@ struct AttnArgs {
   int32_t split;     // first key taken from the second source
   int32_t heads;
   int32_t batch;
-  int32_t n_qtiles;  // ceil(n_q / kBlockM)
+  int32_t n_qtiles;  // ceil(n_q / query rows per workgroup); launch_decode sets it itself
   float scale_log2;  // softmax scale * log2(e)
   // Prefill only (NULL for decode): per-row key limit and per-tile ranges / order.
   const int32_t* row_limit;
