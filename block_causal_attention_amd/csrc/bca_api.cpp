@@ -166,8 +166,16 @@ bca_kv_cache bf16_cache(const bca_tensor* k_cache, const bca_tensor* v_cache) {
   return c;
 }
 
+// A launch of `groups` workgroups of `threads` work-items: a dispatch counts at most 2^32 - 1
+// work-items per grid dimension.
+bool grid_fits(int64_t groups, int64_t threads) {
+  return groups >= 0 && groups <= (int64_t)UINT32_MAX / threads;
+}
+// The attention grids: tiles * B * H workgroups of the prefill's size, the largest any
+// attention kernel uses.
 bool grid_fits(int64_t tiles, int32_t B, int32_t H) {
-  return tiles * (int64_t)B * (int64_t)H <= (int64_t)INT32_MAX;
+  return tiles <= (int64_t)INT32_MAX / ((int64_t)B * H) &&
+         grid_fits(tiles * B * H, 64 * bca::kPrefillWaves);
 }
 
 }  // namespace
@@ -319,7 +327,10 @@ bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, floa
   if ((s = check_extent(k, "k", hp.seq_len)) != BCA_OK) return s;
   if ((s = check_extent(v, "v", hp.seq_len)) != BCA_OK) return s;
   const int64_t nt = (int64_t)hp.kv_end.size();
-  if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles exceeds 2^31 - 1");
+  if (!grid_fits(nt, B, H)) return fail(BCA_ERR_ARG, "B * H * query tiles is too large a grid");
+  if (store && cache->format != BCA_CACHE_BF16 &&
+      !grid_fits(((int64_t)B * hp.prefix_len * H + 15) / 16, 256))
+    return fail(BCA_ERR_ARG, "B * P * H is too large for the cache quantisation grid");
   if ((s = check_launchable(plan)) != BCA_OK) return s;
 
   bca::AttnArgs a{};
@@ -348,16 +359,47 @@ bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, floa
   a.order = plan->d_order;
   a.tiles = plan->d_tiles;
   a.cache_fmt = BCA_CACHE_BF16;
+  // The attention kernel stores the cache's bf16 tensors from its on-chip tiles; a quantised
+  // tensor is written afterwards, on the same stream, from the same k / v rows.
+  const bool kq = store && cache->format == BCA_CACHE_FP8_KV;
+  const bool vq = store && cache->format != BCA_CACHE_BF16;
   if (store) {
-    a.kc = cache->k.data;
-    a.kc_sb = cache->k.stride_b; a.kc_ss = cache->k.stride_s; a.kc_sh = cache->k.stride_h;
-    a.vc = cache->v.data;
-    a.vc_sb = cache->v.stride_b; a.vc_ss = cache->v.stride_s; a.vc_sh = cache->v.stride_h;
+    if (!kq) {
+      a.kc = cache->k.data;
+      a.kc_sb = cache->k.stride_b; a.kc_ss = cache->k.stride_s; a.kc_sh = cache->k.stride_h;
+    }
+    if (!vq) {
+      a.vc = cache->v.data;
+      a.vc_sb = cache->v.stride_b; a.vc_ss = cache->v.stride_s; a.vc_sh = cache->v.stride_h;
+    }
     a.cache_len = (int32_t)hp.prefix_len;
-    set_cache_args(cache, &a);
   }
   hipError_t e = bca::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  if (kq || vq) {
+    bca::QuantArgs qa{};
+    qa.k = static_cast<const uint16_t*>(k->data);
+    qa.k_sb = k->stride_b; qa.k_ss = k->stride_s; qa.k_sh = k->stride_h;
+    qa.v = static_cast<const uint16_t*>(v->data);
+    qa.v_sb = v->stride_b; qa.v_ss = v->stride_s; qa.v_sh = v->stride_h;
+    if (kq) {
+      qa.ko = static_cast<uint8_t*>(cache->k.data);
+      qa.ko_sb = cache->k.stride_b; qa.ko_ss = cache->k.stride_s; qa.ko_sh = cache->k.stride_h;
+      qa.ks = static_cast<float*>(cache->k_scale.data);
+      qa.ks_sb = cache->k_scale.stride_b; qa.ks_ss = cache->k_scale.stride_s;
+      qa.ks_sh = cache->k_scale.stride_h;
+    }
+    qa.vo = static_cast<uint8_t*>(cache->v.data);
+    qa.vo_sb = cache->v.stride_b; qa.vo_ss = cache->v.stride_s; qa.vo_sh = cache->v.stride_h;
+    qa.vs = static_cast<float*>(cache->v_scale.data);
+    qa.vs_sb = cache->v_scale.stride_b; qa.vs_ss = cache->v_scale.stride_s;
+    qa.vs_sh = cache->v_scale.stride_h;
+    qa.rows = (int64_t)B * hp.prefix_len * H;
+    qa.prefix = (int32_t)hp.prefix_len;
+    qa.heads = H;
+    e = bca::launch_quantize(qa, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cache quantisation launch");
+  }
   return BCA_OK;
 }
 
@@ -386,7 +428,7 @@ bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale
   if ((s = check_extent(k, "k", hp.rows)) != BCA_OK) return s;
   if ((s = check_extent(v, "v", hp.rows)) != BCA_OK) return s;
   const int64_t nt = (int64_t)hp.kv_end.size();
-  if (!grid_fits(nt, 1, H)) return fail(BCA_ERR_ARG, "H * query tiles exceeds 2^31 - 1");
+  if (!grid_fits(nt, 1, H)) return fail(BCA_ERR_ARG, "H * query tiles is too large a grid");
   if ((s = check_launchable(plan)) != BCA_OK) return s;
 
   bca::AttnArgs a{};
@@ -488,7 +530,7 @@ bca_status decode_impl(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
                                      " bytes, " + std::to_string(need) + " needed");
     }
   }
-  if (!grid_fits(nt * n_used, B, H)) return fail(BCA_ERR_ARG, "the grid exceeds 2^31 - 1");
+  if (!grid_fits(nt * n_used, B, H)) return fail(BCA_ERR_ARG, "the decode grid is too large");
   if ((s = check_launchable(plan)) != BCA_OK) return s;
 
   bca::AttnArgs a{};
@@ -630,7 +672,7 @@ bca_status bca_cache_dequantize(int32_t B, int64_t P, int32_t H, int32_t D,
   if ((s = check_tensor(k_out, "k_out", 2)) != BCA_OK) return s;
   if ((s = check_tensor(v_out, "v_out", 2)) != BCA_OK) return s;
   const int64_t rows = (int64_t)B * P * H;
-  if ((rows + 15) / 16 > (int64_t)UINT32_MAX) return fail(BCA_ERR_ARG, "B * P * H is too large");
+  if (!grid_fits((rows + 15) / 16, 256)) return fail(BCA_ERR_ARG, "B * P * H is too large");
   bca::DequantArgs a{};
   a.k = cache->k.data;
   a.k_sb = cache->k.stride_b; a.k_ss = cache->k.stride_s; a.k_sh = cache->k.stride_h;

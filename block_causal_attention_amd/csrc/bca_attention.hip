@@ -68,6 +68,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef BCA_SKIP_DEAD_WAVES
 #define BCA_SKIP_DEAD_WAVES 0
 #endif
+// Reads kept in flight ahead of the MFMAs (in steps of one MFMA) in the score and PV phases, or
+// 0 to leave the order to the compiler.  Measured (interleaved A/B, 12-wave kernels): 3 and 4
+// give the prefill +2.7% and the decode +0.5% over the compiler's own order; 2 and 2 or 2 and 4
+// the same within noise; 4 and 6 less on the prefill.
+#ifndef BCA_SCHED_K_DEPTH
+#define BCA_SCHED_K_DEPTH 3
+#endif
+#ifndef BCA_SCHED_V_DEPTH
+#define BCA_SCHED_V_DEPTH 4
+#endif
+constexpr int kSchedKDepth = BCA_SCHED_K_DEPTH;
+constexpr int kSchedVDepth = BCA_SCHED_V_DEPTH;
 #ifndef BCA_V_PAD
 #define BCA_V_PAD 16
 #endif
@@ -95,6 +107,26 @@ constexpr int kBufferWord3 = 0x00020000;
 // -> 16 distinct chunks) and sends the 4-chunk group of one 32-column block in 4 aligned rows to
 // 4 distinct groups (transposed V reads: 32 lanes read 4 rows x 64 B).
 __device__ inline int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Scheduling of one MFMA phase: kSteps steps, each kReads LDS operand reads feeding kMfmas
+// MFMAs.  With kDepth > 0 the reads of step i + kDepth are issued right after step i's MFMAs,
+// so kDepth steps' reads are always in flight ahead of their MFMAs (instead of the order the
+// compiler's scheduler picks, which in some loop shapes waits for each read right before its
+// MFMA).  Placed after the phase's code, in the same basic block.
+template <int kSteps, int kReads, int kMfmas, int kDepth>
+__device__ __forceinline__ void pipeline_reads() {
+  if constexpr (kDepth > 0) {
+    constexpr int kMfmaMask = 0x008, kDsReadMask = 0x100;
+    constexpr int kLead = kDepth < kSteps ? kDepth : kSteps;
+    __builtin_amdgcn_sched_group_barrier(kDsReadMask, kReads * kLead, 0);
+#pragma unroll
+    for (int i = 0; i + kLead < kSteps; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfmaMask, kMfmas, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsReadMask, kReads, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfmaMask, kMfmas * kLead, 0);
+  }
+}
 
 // Reduce across the two 32-lane halves of the wave: after v_permlane32_swap(x, x) every lane
 // holds {x[lane % 32], x[lane % 32 + 32]} in the same order, so both halves get identical bits.
@@ -145,31 +177,6 @@ __device__ inline u32x4 dequant(u32x4 x) {
   return __builtin_bit_cast(u32x4, r);
 }
 
-// Quantises this lane's 8 bf16 values of a 128-wide row held by 16 consecutive lanes (8 values
-// each): the row's amax comes from a 16-lane max, scale = max(amax / 448, 2^-126) (1 if amax is
-// 0) and codes = E4M3(x * (1 / scale)), all divisions correctly rounded and the conversion
-// round-to-nearest-even.  Returns the 8 codes; *scale_out gets the row scale.
-__device__ inline u32x2 quantize_row8(u32x4 x, float* scale_out) {
-  const bf16x8 xb = __builtin_bit_cast(bf16x8, x);
-  float f[8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    f[i] = (float)xb[i];
-    amax = fmaxf(amax, fabsf(f[i]));
-  }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  const float scale = amax > 0.0f ? fmaxf(amax / 448.0f, 0x1p-126f) : 1.0f;
-  const float inv = 1.0f / scale;
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv, f[1] * inv, 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv, f[3] * inv, w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * inv, f[5] * inv, 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * inv, f[7] * inv, w1, true);
-  *scale_out = scale;
-  return u32x2{(uint32_t)w0, (uint32_t)w1};
-}
-
 // The body of all the kernels.  kBlockN keys per key tile (32 or 64) and kW waves per workgroup
 // are chosen per kernel, and so is the occupancy (set on the kernels below).
 template <bool kDecode, bool kDirect, int kFmt, int kBlockN, int kW>
@@ -184,15 +191,14 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
   static_assert(kDirect || kBlockN * kHeadDim / 8 % kThreads == 0,
                 "staged fills: whole 16-byte chunks per thread");
-  // The prefill stores a quantised cache; the decode reads one (its first key source).
-  constexpr bool kKq = kFmt == kCacheFp8KV;
-  constexpr bool kVq = kFmt != kCacheBf16;
+  // The decode may read a quantised cache (its first key source); the prefill stores bf16 only.
+  static_assert(kDecode || kFmt == kCacheBf16, "the prefill stores the cache's bf16 tensors");
   // wave priority while issuing MFMAs (0: never raised)
   constexpr int kPrioLevel =
       kDecode && kDirect && kW == kDecodeDirectWaves ? BCA_DECODE_DIRECT_MFMA_PRIO : BCA_MFMA_PRIO;
   constexpr bool kPrio = kPrioLevel > 0;
-  constexpr bool kKqSrc = kDecode && kKq;
-  constexpr bool kVqSrc = kDecode && kVq;
+  constexpr bool kKqSrc = kDecode && kFmt == kCacheFp8KV;
+  constexpr bool kVqSrc = kDecode && kFmt != kCacheBf16;
   static_assert(!(kDirect && (kKqSrc || kVqSrc)), "direct loads move bf16 rows only");
   // LDS rows: unpadded (256 B) with their 16-byte chunks swizzled, or padded (272 B / 288 B).
   constexpr bool kSwizzle = kDirect || kStageSwizzle;
@@ -200,12 +206,12 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // Padded V rows: 288 B.  (320 B rows make the transposed reads bank-conflict-free on 64 banks,
   // BCA_V_PAD = 32, but measured no faster: the decode is not bound by LDS conflicts.)
   constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + BCA_V_PAD;
-  // The two ring buffers.  The bf16 prefill (swizzled tiles, read by buffer constants: its tile
-  // loop is unrolled by two below) keeps them in separate arrays: reads of one are then provably
-  // independent of the direct loads in flight into the other, so the compiler adds no vmcnt wait
-  // before them (the ring's own waits and barrier order the buffers).  The other calls index one
-  // array of two at run time (an unrolled FP8 prefill runs out of registers in its quantiser).
-  constexpr bool kConstBuf = kSwizzle && kFmt == kCacheBf16;
+  // The two ring buffers.  The direct-fill kernels (swizzled tiles, read by buffer constants:
+  // their tile loop is unrolled by two below) keep them in separate arrays: reads of one are then
+  // provably independent of the direct loads in flight into the other, so the compiler adds no
+  // vmcnt wait before them (the ring's own waits and barrier order the buffers).  The staged
+  // decode indexes one array of two at run time.
+  constexpr bool kConstBuf = kSwizzle;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBlockN * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBlockN * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kBlockN * kVStride];
@@ -522,57 +528,34 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // ---- prefix-K/V cache (prefill only) ----------------------------------------------------------
   // This workgroup owns cache rows [cache_lo, cache_hi), which lie inside its own diagonal key
   // tiles; they are copied out of the LDS tile while it is resident, so no K/V row is fetched
-  // twice.
+  // twice.  Either tensor may be absent (NULL): a quantised one is written by its own pass.
   const int cache_lo = row0;
-  const int cache_hi = kDecode || a.kc == nullptr ? 0 : min(cache_lo + kRows, a.cache_len);
-  // One 8-value chunk of cache row `key`: a bf16 copy, or (quantised tensor) 8 codes plus, from
-  // the row's first lane, the row scale.  The quantised form reduces over the row's 16 lanes, so
-  // every lane runs it; only the stores depend on `in`.
-  auto put_chunk = [&](auto quant_c, u32x4 x, void* base, int64_t ss, int64_t sb, int64_t sh,
-                       float* sbase, int64_t sss, int64_t ssb, int64_t ssh, int key, bool in) {
-    if constexpr (decltype(quant_c)::value) {
-      float sc;
-      const u32x2 c = quantize_row8(x, &sc);
-      if (in) {
-        *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(base) + b * sb + (int64_t)key * ss +
-                                  h * sh + ld_col) = c;
-        if ((tid & 15) == 0) sbase[b * ssb + (int64_t)key * sss + h * ssh] = sc;
-      }
-    } else if (in) {
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + b * sb + (int64_t)key * ss +
-                                h * sh + ld_col) = x;
-    }
-  };
-  // Chunk tid + kThreads r of the tile: row (tid >> 4) + kRowsPerPass r, chunk tid % 16.  In a
-  // partial last pass the rows past the tile re-read its last row and store nothing (whole
-  // 16-lane groups, so the quantiser's row reduction stays inside one row).
+  const int cache_hi =
+      kDecode || (a.kc == nullptr && a.vc == nullptr) ? 0 : min(cache_lo + kRows, a.cache_len);
+  // Chunk tid + kThreads r of the tile: row (tid >> 4) + kRowsPerPass r, chunk tid % 16 (a
+  // partial last pass stores nothing past the tile).
   auto store_row = [&](int n0, auto buf, int r) {
-    const int row_raw = ld_row + kRowsPerPass * r;
-    const int row = min(row_raw, kBlockN - 1);
+    const int row = ld_row + kRowsPerPass * r;
     const int key = n0 + row;
-    const bool in = row_raw < kBlockN && key >= cache_lo && key < cache_hi;
-    if (!(kKq || kVq) && !in) return;
+    if (row >= kBlockN || key < cache_lo || key >= cache_hi) return;
     const int col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(row)) : ld_col;
-    const u32x4 kx = *reinterpret_cast<const u32x4*>(&k_lds(buf)[row * kKStride + col]);
-    const u32x4 vx = *reinterpret_cast<const u32x4*>(&v_lds(buf)[row * kVStride + col]);
-    put_chunk(std::integral_constant<bool, kKq>{}, kx, a.kc, a.kc_ss, a.kc_sb, a.kc_sh, a.kcs,
-              a.kcs_ss, a.kcs_sb, a.kcs_sh, key, in);
-    put_chunk(std::integral_constant<bool, kVq>{}, vx, a.vc, a.vc_ss, a.vc_sb, a.vc_sh, a.vcs,
-              a.vcs_ss, a.vcs_sb, a.vcs_sh, key, in);
+    const int64_t at = (int64_t)key;
+    if (a.kc != nullptr)
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kc) + b * a.kc_sb + at * a.kc_ss +
+                                h * a.kc_sh + ld_col) =
+          *reinterpret_cast<const u32x4*>(&k_lds(buf)[row * kKStride + col]);
+    if (a.vc != nullptr)
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.vc) + b * a.vc_sb + at * a.vc_ss +
+                                h * a.vc_sh + ld_col) =
+          *reinterpret_cast<const u32x4*>(&v_lds(buf)[row * kVStride + col]);
   };
   auto store_cache = [&](int n0, auto buf) {
     if (kDecode || n0 >= cache_hi || n0 + kBlockN <= cache_lo) return;
     // n0 made opaque: otherwise the compiler keeps this rare store's row pointers live across
     // the whole loop and advances them every tile
     asm volatile("" : "+s"(n0));
-    if constexpr (kKq || kVq) {
-      // one row pass at a time: the quantiser's registers stay few next to the accumulators
-#pragma unroll 1
-      for (int r = 0; r < kChunksPerThread; ++r) store_row(n0, buf, r);
-    } else {
 #pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r) store_row(n0, buf, r);
-    }
+    for (int r = 0; r < kChunksPerThread; ++r) store_row(n0, buf, r);
   };
 
   // ---- per-lane LDS read addresses (byte offsets inside one buffer) ------------------------------
@@ -702,6 +685,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[qb][kb], 0, 0, 0);
         }
       }
+      pipeline_reads<8 * kKeyBlocks, 1, kQueryBlocks, kSchedKDepth>();
 
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
       // ---- mask: only tiles that cross some row's limit.  Accumulator element i of key block kb
@@ -790,6 +774,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
             o[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kc], o[qb][d], 0, 0, 0);
         }
       }
+      pipeline_reads<8 * kKeyBlocks, 2, kQueryBlocks, kSchedVDepth>();
 
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     }
@@ -913,12 +898,11 @@ __global__ __launch_bounds__(256) void split_combine(const AttnArgs a) {
   *reinterpret_cast<f32x4*>(op + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
 }
 
-// Prefill: block-causal, direct-to-LDS fills, optional prefix-cache store in format kFmt.
-template <int kFmt>
+// Prefill: block-causal, direct-to-LDS fills, optional store of the prefix cache's bf16 tensors.
 __global__ __launch_bounds__(64 * kPrefillWaves)
 __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
 void attn_prefill(const AttnArgs a) {
-  attn_fwd<false, true, kFmt, kPrefillBlockN, kPrefillWaves>(a);
+  attn_fwd<false, true, kCacheBf16, kPrefillBlockN, kPrefillWaves>(a);
 }
 
 // Decode over [prefix cache in format kFmt ; target], register-staged fills: the FP8 caches,
@@ -962,12 +946,7 @@ int device_cus() {
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);
   const dim3 block(64 * kPrefillWaves);
-  switch (a.cache_fmt) {
-    case kCacheBf16: hipLaunchKernelGGL(attn_prefill<kCacheBf16>, grid, block, 0, stream, a); break;
-    case kCacheFp8V: hipLaunchKernelGGL(attn_prefill<kCacheFp8V>, grid, block, 0, stream, a); break;
-    case kCacheFp8KV: hipLaunchKernelGGL(attn_prefill<kCacheFp8KV>, grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(attn_prefill, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -986,12 +965,14 @@ hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   };
   switch (a.cache_fmt) {
     case kCacheBf16:
-      if (BCA_DECODE_STAGED_BF16)
-        launch(attn_decode<kCacheBf16>, kStagedWaves);
-      else if (tiles(kDecodeDirectWaves) * heads >= 2 * (int64_t)device_cus())
+#if BCA_DECODE_STAGED_BF16
+      launch(attn_decode<kCacheBf16>, kStagedWaves);
+#else
+      if (tiles(kDecodeDirectWaves) * heads >= 2 * (int64_t)device_cus())
         launch(attn_decode_direct<kDecodeDirectWaves>, kDecodeDirectWaves);
       else
         launch(attn_decode_direct<kDecodeDirectSmallWaves>, kDecodeDirectSmallWaves);
+#endif
       break;
     case kCacheFp8V: launch(attn_decode<kCacheFp8V>, kStagedWaves); break;
     case kCacheFp8KV: launch(attn_decode<kCacheFp8KV>, kStagedWaves); break;

@@ -1,11 +1,13 @@
-// Prefix-cache expansion for gfx950: a cache stored as FP8 E4M3 codes with one fp32 scale per
-// (token, head) (the 10100.com Qwen-Image 2.1 article, FP8 part) written back as bf16, once per
-// layer, so that the cached step can run the bf16 decode.  The value of a code is its E4M3 value
-// times the row scale, formed in fp32 and rounded to bf16 (RNE): the same rule the decode applies
-// when it dequantises while staging, so both paths see bitwise the same K and V.
-//
-// Sixteen lanes per 128-value row, eight values per lane: 8 code bytes (or 16 bf16 bytes) in,
-// 16 bytes out.  HBM-bound.
+// Prefix-cache format conversions for gfx950.  The FP8 cache stores E4M3 codes with one fp32
+// scale per (token, head) (the 10100.com Qwen-Image 2.1 article, FP8 part).
+//   cache_quantize: the prefill's prefix K/V rows written as codes and scales.  The prefill
+//     kernel itself stores only the cache's bf16 tensors: quantising inside its key-tile loop
+//     cost the loop registers it needs for its operand reads.
+//   cache_dequant: a cache written back as bf16, once per layer, so that the cached step can run
+//     the bf16 decode.  The value of a code is its E4M3 value times the row scale, formed in fp32
+//     and rounded to bf16 (RNE): the same rule the decode applies when it dequantises while
+//     staging, so both paths see bitwise the same K and V.
+// Sixteen lanes per 128-value row, eight values per lane.  HBM-bound.
 #include "bca_internal.h"
 
 namespace bca {
@@ -39,6 +41,61 @@ __device__ inline u32x4 load8(const void* base, int64_t sb, int64_t ss, int64_t 
   return *reinterpret_cast<const u32x4*>(src);
 }
 
+// Quantises this lane's 8 bf16 values of a 128-wide row held by 16 consecutive lanes (8 values
+// each): the row's amax comes from a 16-lane max, scale = max(amax / 448, 2^-126) (1 if amax is
+// 0) and codes = E4M3(x * (1 / scale)), all divisions correctly rounded and the conversion
+// round-to-nearest-even.  Returns the 8 codes; *scale_out gets the row scale.
+__device__ inline u32x2 quantize_row8(u32x4 x, float* scale_out) {
+  const bf16x8 xb = __builtin_bit_cast(bf16x8, x);
+  float f[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[i] = (float)xb[i];
+    amax = fmaxf(amax, fabsf(f[i]));
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float scale = amax > 0.0f ? fmaxf(amax / 448.0f, 0x1p-126f) : 1.0f;
+  const float inv = 1.0f / scale;
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv, f[1] * inv, 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv, f[3] * inv, w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * inv, f[5] * inv, 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * inv, f[7] * inv, w1, true);
+  *scale_out = scale;
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+
+// One tensor's row chunk (b, p, h, d0 .. d0 + 7) quantised: codes to `out`, the row scale (from
+// the row's first lane) to `sout`.
+__device__ inline void quantize8(const uint16_t* src, int64_t sb, int64_t ss, int64_t sh,
+                                 uint8_t* out, int64_t ob, int64_t os, int64_t oh, float* sout,
+                                 int64_t sob, int64_t sos, int64_t soh, int64_t b, int64_t p,
+                                 int64_t h, int d0, bool first_lane) {
+  const u32x4 x = *reinterpret_cast<const u32x4*>(src + b * sb + p * ss + h * sh + d0);
+  float sc;
+  const u32x2 c = quantize_row8(x, &sc);
+  *reinterpret_cast<u32x2*>(out + b * ob + p * os + h * oh + d0) = c;
+  if (first_lane) sout[b * sob + p * sos + h * soh] = sc;
+}
+
+__global__ __launch_bounds__(256) void cache_quantize(const QuantArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= a.rows) return;  // whole 16-lane groups: the row max stays inside one group
+  const int d0 = 8 * (threadIdx.x & 15);
+  const bool first = (threadIdx.x & 15) == 0;
+  const int64_t h = row % a.heads;
+  const int64_t bp = row / a.heads;
+  const int64_t p = bp % a.prefix;
+  const int64_t b = bp / a.prefix;
+  if (a.ko != nullptr)
+    quantize8(a.k, a.k_sb, a.k_ss, a.k_sh, a.ko, a.ko_sb, a.ko_ss, a.ko_sh, a.ks, a.ks_sb,
+              a.ks_ss, a.ks_sh, b, p, h, d0, first);
+  if (a.vo != nullptr)
+    quantize8(a.v, a.v_sb, a.v_ss, a.v_sh, a.vo, a.vo_sb, a.vo_ss, a.vo_sh, a.vs, a.vs_sb,
+              a.vs_ss, a.vs_sh, b, p, h, d0, first);
+}
+
 __global__ __launch_bounds__(256) void cache_dequant(const DequantArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (row >= a.rows) return;  // whole 16-lane groups; no cross-lane exchange
@@ -55,6 +112,12 @@ __global__ __launch_bounds__(256) void cache_dequant(const DequantArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
+  const int64_t blocks = (a.rows + 15) / 16;
+  hipLaunchKernelGGL(cache_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
   const int64_t blocks = (a.rows + 15) / 16;

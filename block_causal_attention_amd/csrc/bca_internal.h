@@ -91,9 +91,9 @@ struct AttnArgs {
   int64_t v2_sb, v2_ss, v2_sh;
   float* o;
   int64_t o_sb, o_ss, o_sh;
-  // Prefill only: prefix-K/V cache [B, cache_len, H, D] receiving K/V rows [0, cache_len), or
-  // NULL.  The workgroup of query tile t writes rows [t kBlockM, (t + 1) kBlockM) of it.  In a
-  // quantised format the quantised tensor holds uint8 codes.
+  // Prefill only: bf16 prefix-cache tensors [B, cache_len, H, D] receiving K/V rows
+  // [0, cache_len), or NULL (no cache, or a quantised tensor, which launch_quantize writes).
+  // The workgroup of query tile t writes rows [t kBlockM, (t + 1) kBlockM) of them.
   void* kc;
   int64_t kc_sb, kc_ss, kc_sh;
   void* vc;
@@ -115,13 +115,12 @@ struct AttnArgs {
   // offset of the sequence's row limits, kv_full, kv_end, 0, 0}; row_limit and the key bounds
   // are local to the sequence.
   const int32_t* tiles;
-  // Scales [B, cache_len, H] of the quantised cache tensors: written by the prefill, read by the
-  // decode (NULL for a bf16 tensor).
+  // Decode only: scales [B, cache_len, H] of the quantised cache tensors (NULL for a bf16 one).
   float* kcs;
   int64_t kcs_sb, kcs_ss, kcs_sh;
   float* vcs;
   int64_t vcs_sb, vcs_ss, vcs_sh;
-  int32_t cache_fmt;  // kCacheBf16 / kCacheFp8V / kCacheFp8KV
+  int32_t cache_fmt;  // decode only: kCacheBf16 / kCacheFp8V / kCacheFp8KV
   // Decode only: key ranges of split_units x kSplitUnit keys each, n_split of them (1 = no
   // split), whose partial results go to part_o [n_split][B][N][H][D] and part_ml
   // [n_split][B][N][H][2] (m, l) and are merged into o by a second kernel.
@@ -173,8 +172,31 @@ struct DequantArgs {
   int32_t fmt;   // kCacheBf16 / kCacheFp8V / kCacheFp8KV
 };
 
+// Cache quantisation: prefix rows [0, P) of bf16 K and V [B, S, H, D] written as E4M3 codes
+// [B, P, H, D] plus one fp32 scale per (b, p, h) for each tensor with a code pointer (ko, vo;
+// NULL: that tensor is not quantised).  The rule is the cache format's (scale = max(amax / 448,
+// 2^-126), 1 for an all-zero row; codes = E4M3(x * (1 / scale)), RNE).
+struct QuantArgs {
+  const uint16_t* k;
+  int64_t k_sb, k_ss, k_sh;
+  const uint16_t* v;
+  int64_t v_sb, v_ss, v_sh;
+  uint8_t* ko;
+  int64_t ko_sb, ko_ss, ko_sh;
+  float* ks;
+  int64_t ks_sb, ks_ss, ks_sh;
+  uint8_t* vo;
+  int64_t vo_sb, vo_ss, vo_sh;
+  float* vs;
+  int64_t vs_sb, vs_ss, vs_sh;
+  int64_t rows;  // B * P * H
+  int32_t prefix;
+  int32_t heads;
+};
+
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 

@@ -222,8 +222,10 @@ typedef struct bca_kv_cache {
 /*
  * bca_prefill_ex -- bca_prefill with the prefix cache given as a descriptor of any format (NULL:
  * no cache).  The attention itself always uses the bf16 k and v; only the stored cache is
- * quantised, by the rule above, in the same kernel that reads those rows.  Ownership, errors and
- * the other arguments are those of bca_prefill; an unknown format is BCA_ERR_ARG.
+ * quantised, by the rule above: the attention kernel stores the cache's bf16 tensors, and a second
+ * kernel on the same stream quantises rows [0, P) of k and v into the code and scale tensors.
+ * Ownership, errors and the other arguments are those of bca_prefill; an unknown format is
+ * BCA_ERR_ARG.
  */
 bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
                           const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
