@@ -397,7 +397,7 @@ def main():
         dom, key, achieved = ("decode: attn_decode_direct<12> (bf16 cache), B=2", "decode_cfg_b2",
                               dec_tf)
     else:
-        dom, key, achieved = ("prefill: attn_prefill<0> (writes the bf16 prefix cache), B=1",
+        dom, key, achieved = ("prefill: attn_prefill (writes the bf16 prefix cache), B=1",
                               "prefill_b1", pre_tf)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
