@@ -276,7 +276,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const int j_end = n_split > 1 ? min(ntiles, j_begin + split_tiles) : ntiles;
 
   // does any of this wave's query rows exist (wave-uniform)
-  const bool live = row0 + wave * 32 * kQueryBlocks < n_rows;
+  const int wave_row0 = row0 + wave * 32 * kQueryBlocks;
+  const bool live = wave_row0 + 32 * kQueryBlocks > 0 && wave_row0 < n_rows;
   constexpr bool kSkipDead = BCA_SKIP_DEAD_WAVES;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
@@ -286,7 +287,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
 #pragma unroll
   for (int qb = 0; qb < kQueryBlocks; ++qb) {
     const int row = row0 + (wave * kQueryBlocks + qb) * 32 + qn;
-    row_ok[qb] = row < n_rows;
+    row_ok[qb] = row >= 0 && row < n_rows;  // a prefill tile's first rows may be padding
     lim[qb] = kDecode ? a.kv_len : a.row_limit[rl_off + (row_ok[qb] ? row : n_rows - 1)];
     const uint16_t* qp = a.q + b * a.q_sb + (int64_t)(seq_row0 + (row_ok[qb] ? row : 0)) * a.q_ss +
                          h * a.q_sh + 8 * half;

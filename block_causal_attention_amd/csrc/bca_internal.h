@@ -93,7 +93,7 @@ struct AttnArgs {
   int64_t o_sb, o_ss, o_sh;
   // Prefill only: bf16 prefix-cache tensors [B, cache_len, H, D] receiving K/V rows
   // [0, cache_len), or NULL (no cache, or a quantised tensor, which launch_quantize writes).
-  // The workgroup of query tile t writes rows [t kBlockM, (t + 1) kBlockM) of them.
+  // The workgroup of a query tile writes the tile's own rows of them.
   void* kc;
   int64_t kc_sb, kc_ss, kc_sh;
   void* vc;
@@ -111,7 +111,8 @@ struct AttnArgs {
   const int32_t* kv_full;
   const int32_t* kv_end;
   const int32_t* order;
-  // Prefill only: per query tile {sequence's first tensor row, first local row, sequence length,
+  // Prefill only: per query tile {sequence's first tensor row, first local row (negative for a
+  // partial first tile, whose rows below 0 are padding), sequence length,
   // offset of the sequence's row limits, kv_full, kv_end, 0, 0}; row_limit and the key bounds
   // are local to the sequence.
   const int32_t* tiles;

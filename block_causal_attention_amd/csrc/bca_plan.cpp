@@ -62,15 +62,24 @@ int build_host_plan(const int32_t* ids, int64_t S, int block_m, HostPlan* out, s
   }
   p.useful_pairs = 0;
   for (int32_t x : p.row_limit) p.useful_pairs += x;
-  // per query tile: first row's limit is the minimum, last row's the maximum
+  // Query tiles end at the sequence's end: tile t covers rows [S - (nt - t) block_m,
+  // S - (nt - 1 - t) block_m), so a partial tile is the first one, whose rows see the fewest
+  // keys (hi never decreases), and its rows below 0 are padding.  Per tile the first real row's
+  // limit is the minimum and the last row's the maximum.
   const int64_t nt = (S + block_m - 1) / block_m;
   p.kv_full.resize((size_t)nt);
   p.kv_end.resize((size_t)nt);
+  p.tiles.assign((size_t)nt * kTileInts, 0);
   for (int64_t t = 0; t < nt; ++t) {
-    const int64_t first = t * block_m;
-    const int64_t last = std::min<int64_t>(S, first + block_m) - 1;
-    p.kv_full[(size_t)t] = p.row_limit[(size_t)first];
+    const int64_t first = S - (nt - t) * block_m;
+    const int64_t last = first + block_m - 1;
+    p.kv_full[(size_t)t] = p.row_limit[(size_t)std::max<int64_t>(first, 0)];
     p.kv_end[(size_t)t] = p.row_limit[(size_t)last];
+    int32_t* d = &p.tiles[(size_t)t * kTileInts];
+    d[1] = (int32_t)first;
+    d[2] = (int32_t)S;
+    d[4] = p.kv_full[(size_t)t];
+    d[5] = p.kv_end[(size_t)t];
   }
   // heavy-first: kv_end descending, ties by tile index ascending
   p.order.resize((size_t)nt);
@@ -82,14 +91,6 @@ int build_host_plan(const int32_t* ids, int64_t S, int block_m, HostPlan* out, s
   p.target_len = S - p.prefix_len;
   p.decode_ok = p.segments[3 * (nseg - 1) + 2] >= 0 ? 1 : 0;
   p.block_m = block_m;
-  p.tiles.assign((size_t)nt * kTileInts, 0);
-  for (int64_t t = 0; t < nt; ++t) {
-    int32_t* d = &p.tiles[(size_t)t * kTileInts];
-    d[1] = (int32_t)(t * block_m);
-    d[2] = (int32_t)S;
-    d[4] = p.kv_full[(size_t)t];
-    d[5] = p.kv_end[(size_t)t];
-  }
   p.rows = S;
   *out = std::move(p);
   return kPlanOk;
@@ -153,7 +154,7 @@ int build_varlen_plan(const int32_t* ids, const int64_t* lengths, const int64_t*
     for (size_t t = 0; t < nt; ++t) {
       p.kv_full.push_back(one.kv_full[t]);
       p.kv_end.push_back(one.kv_end[t]);
-      const int32_t d[kTileInts] = {(int32_t)start[(size_t)b], (int32_t)(t * block_m),
+      const int32_t d[kTileInts] = {(int32_t)start[(size_t)b], one.tiles[t * kTileInts + 1],
                                     (int32_t)lengths[b], (int32_t)off, one.kv_full[t],
                                     one.kv_end[t], 0, 0};
       p.tiles.insert(p.tiles.end(), d, d + kTileInts);

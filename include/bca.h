@@ -89,8 +89,10 @@ enum { BCA_PLAN_HOST_ONLY = 1u };
  * with hi(i) = i + 1 for text and the end of its block for image rows.  For text this is the
  * bottom-right aligned causal triangle of a segment whose query count is below its key count
  * (10100.com article, piecewise-attention part: mask = ones(q_len, kv_len).tril(kv_len - q_len)).
- * Per query tile t of block_m rows it stores kv_full[t] (min hi: key tiles below it need no mask)
- * and kv_end[t] (max hi: key tiles at or past it are skipped), and a heavy-first tile order.
+ * The rows are cut into n_qtiles tiles of block_m rows that end at the last row: tile t holds
+ * rows [S - (n_qtiles - t) block_m, S - (n_qtiles - 1 - t) block_m) clipped at 0, so only tile 0
+ * may be partial.  Per tile it stores kv_full[t] (min hi over its rows: key tiles below it need no
+ * mask) and kv_end[t] (max hi: key tiles at or past it are skipped), and a heavy-first order.
  *
  * flags: 0, or BCA_PLAN_HOST_ONLY to skip the device upload (such a plan can be inspected but
  * not launched).  Without it, the plan owns small int32 device arrays on the current device

@@ -242,10 +242,14 @@ def row_key_limits(ids: Sequence[int]) -> np.ndarray:
 def plan_from_mask(ids: Sequence[int], block_m: int) -> Dict[str, np.ndarray]:
     """Per-query-tile key ranges derived from the mask, for bit-exact comparison with a planner.
 
-    For query tile t (rows [t*block_m, min(S, (t+1)*block_m))): kv_full[t] = min hi over its
-    rows (every key below it is visible to every row of the tile), kv_end[t] = max hi (no row
-    sees a key at or beyond it).  ``order`` lists the tiles by kv_end descending, ties by tile
-    index ascending.  ``segments`` are the maximal equal-id runs (start, end, id).
+    The pages fix no partition of the queries into tiles; the reading taken here (and by the
+    planner) is that the nt = ceil(S / block_m) tiles end at the sequence's end, so only the
+    first one may be partial: tile t holds rows [max(0, S - (nt-t)*block_m), S - (nt-1-t)*block_m)
+    (``tile_first`` gives S - (nt-t)*block_m, negative for a partial first tile).  Then
+    kv_full[t] = min hi over its rows (every key below it is visible to every row of the tile),
+    kv_end[t] = max hi (no row sees a key at or beyond it).  ``order`` lists the tiles by kv_end
+    descending, ties by tile index ascending.  ``segments`` are the maximal equal-id runs
+    (start, end, id).
     """
     a = validate_block_ids(ids)
     S = a.size
@@ -253,8 +257,11 @@ def plan_from_mask(ids: Sequence[int], block_m: int) -> Dict[str, np.ndarray]:
     nt = -(-S // block_m)
     kv_full = np.empty(nt, dtype=np.int64)
     kv_end = np.empty(nt, dtype=np.int64)
+    tile_first = np.empty(nt, dtype=np.int64)
     for t in range(nt):
-        seg = hi[t * block_m:min(S, (t + 1) * block_m)]
+        first = S - (nt - t) * block_m
+        seg = hi[max(0, first):first + block_m]
+        tile_first[t] = first
         kv_full[t] = seg.min()
         kv_end[t] = seg.max()
     order = np.array(sorted(range(nt), key=lambda t: (-kv_end[t], t)), dtype=np.int64)
@@ -264,6 +271,7 @@ def plan_from_mask(ids: Sequence[int], block_m: int) -> Dict[str, np.ndarray]:
         "row_limit": hi,
         "kv_full": kv_full,
         "kv_end": kv_end,
+        "tile_first": tile_first,
         "order": order,
         "prefix_len": np.int64(P),
         "target_len": np.int64(N),

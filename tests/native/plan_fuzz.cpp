@@ -13,6 +13,8 @@
 
 #include "bca_plan.h"
 
+#include <algorithm>
+
 static int fail(const char* what, int64_t S) {
   std::fprintf(stderr, "FAIL %s (S=%lld)\n", what, (long long)S);
   return 1;
@@ -52,14 +54,20 @@ int main(int argc, char** argv) {
     const int64_t nt = (S + block_m - 1) / block_m;
     if ((int64_t)p.kv_full.size() != nt || (int64_t)p.order.size() != nt) return fail("tiles", S);
     std::vector<int> seen((size_t)nt, 0);
+    int64_t next_row = 0;  // tiles cover rows [0, S) in order, each once; only the first is partial
     for (int64_t t = 0; t < nt; ++t) {
       const int32_t o = p.order[(size_t)t];
       if (o < 0 || o >= nt || seen[(size_t)o]++) return fail("order permutation", S);
       if (t && p.kv_end[(size_t)p.order[(size_t)t - 1]] < p.kv_end[(size_t)o]) return fail("heavy first", S);
-      for (int64_t r = t * block_m; r < S && r < (t + 1) * block_m; ++r)
+      const int64_t first = p.tiles[(size_t)t * bca::kTileInts + 1];
+      if (first + block_m <= 0 || (t > 0 && first < 0) || std::max<int64_t>(first, 0) != next_row)
+        return fail("tile partition", S);
+      next_row = first + block_m;
+      for (int64_t r = std::max<int64_t>(first, 0); r < first + block_m; ++r)
         if (p.row_limit[(size_t)r] < p.kv_full[(size_t)t] || p.row_limit[(size_t)r] > p.kv_end[(size_t)t])
           return fail("tile range", S);
     }
+    if (next_row != S) return fail("tile partition end", S);
     const size_t nseg = p.segments.size() / 3;
     if (p.prefix_len != p.segments[3 * (nseg - 1)] || p.prefix_len + p.target_len != S)
       return fail("prefix", S);
@@ -100,7 +108,9 @@ int main(int argc, char** argv) {
       const int64_t s0 = packed ? off : starts[(size_t)b];
       for (int64_t t = 0; t < (n + 127) / 128; ++t, ++tiles) {
         const int32_t* d = &p.tiles[(size_t)tiles * bca::kTileInts];
-        if (d[0] != s0 || d[1] != t * 128 || d[2] != n || d[3] != off) return fail("descriptor", n);
+        const int64_t nt = (n + 127) / 128;
+        if (d[0] != s0 || d[1] != n - (nt - t) * 128 || d[2] != n || d[3] != off)
+          return fail("descriptor", n);
         if (d[4] < 1 || d[4] > d[5] || d[5] > n) return fail("descriptor bounds", n);
       }
       for (int64_t i = 0; i < n; ++i) {

@@ -323,13 +323,20 @@ def test_plan_from_mask_brute_force():
             hi = np.array([1 + max(j for j in range(S) if wm[i, j]) for i in range(S)])
             assert np.array_equal(plan["row_limit"], hi)
             nt = (S + bm - 1) // bm
+            # tiles end at the sequence's end: only the first may be partial, and together they
+            # cover every row once
+            covered = []
             for t in range(nt):
-                rows = range(t * bm, min(S, (t + 1) * bm))
+                rows = range(max(0, S - (nt - t) * bm), S - (nt - 1 - t) * bm)
+                assert plan["tile_first"][t] == S - (nt - t) * bm
+                assert len(rows) == bm or (t == 0 and 0 < len(rows) < bm)
+                covered.extend(rows)
                 full = min(hi[r] for r in rows)
                 end = max(hi[r] for r in rows)
                 assert plan["kv_full"][t] == full and plan["kv_end"][t] == end
                 # every key below kv_full is visible to every row; none at or past kv_end is
                 assert all(wm[r, :full].all() and not wm[r, end:].any() for r in rows)
+            assert covered == list(range(S))
             keys = [(-plan["kv_end"][t], t) for t in plan["order"]]
             assert keys == sorted(keys) and sorted(plan["order"]) == list(range(nt))
             assert plan["useful_pairs"] == wm.sum()
