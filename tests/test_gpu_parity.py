@@ -297,3 +297,24 @@ def test_strided_inputs_and_side_stream():
     s.synchronize()
     assert torch.equal(out, o_ref)
     assert torch.count_nonzero(big[:, :, 0]) == 0
+
+
+def test_decode_workgroup_widths_agree_bitwise():
+    """The bf16 decode runs 12-wave workgroups on large grids and 4-wave ones on small grids
+    (B = 2 and B = 1 at N = 4,096, H = 32).  A row's arithmetic and key order do not depend on
+    the width, so batch item 0 of the B = 2 decode equals the B = 1 decode of the same inputs
+    bit for bit (sampled against the oracle too, through the CFG test)."""
+    lay = W.EDIT_2REF
+    ids = lay.block_ids()
+    S, H = lay.seq_len, lay.heads
+    plan = bca.Plan(ids)
+    P, N = plan.info.prefix_len, plan.info.target_len
+    qb, kb, vb = W.qkv(W.SEEDS["edit_2ref_cfg"], 2, S, H, scaled=False)
+    q, k, v = to_dev(qb[:, P:]), to_dev(kb[:, P:]), to_dev(vb[:, P:])
+    kc, vc = to_dev(kb[:, :P]), to_dev(vb[:, :P])
+    say(f"case: decode widths B=2 vs B=1, N={N}")
+    both = bca.decode(plan, q, kc, vc, k, v)
+    one = bca.decode(plan, q[:1].contiguous(), kc[:1].contiguous(), vc[:1].contiguous(),
+                     k[:1].contiguous(), v[:1].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(both[:1], one)
