@@ -11,7 +11,7 @@
 // Work decomposition.  One workgroup = kW waves = one tile of 32 kW query rows of one (batch,
 // head); a wave owns kQueryBlocks blocks of 32 rows.  The prefill and the bf16-cache decode run
 // 12 waves (384 rows, one workgroup per CU at 3 waves per SIMD, so each K/V tile in LDS serves
-// 384 rows; a small decode grid runs 4), the FP8-cache decode 4.  Per key tile of kBlockN keys
+// 384 rows; a small decode grid runs 4), the FP8-cache decode 8 (4 on a small grid).  Per key tile of kBlockN keys
 // (32 in the prefill and the bf16-cache decode; 64 in the FP8-cache decode, at 2 waves per
 // SIMD):
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q rows held in VGPRs.
@@ -189,8 +189,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // kernels copy cache rows out of LDS this way)
   constexpr int kChunksPerThread = (kBlockN * kHeadDim / 8 + kThreads - 1) / kThreads;
   static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
-  static_assert(kDirect || kBlockN * kHeadDim / 8 % kThreads == 0,
-                "staged fills: whole 16-byte chunks per thread");
+  // staging passes past the tile's rows (a partial last pass) load and store nothing
+  constexpr bool kPartialPass = kBlockN * kHeadDim / 8 % kThreads != 0;
   // The decode may read a quantised cache (its first key source); the prefill stores bf16 only.
   static_assert(kDecode || kFmt == kCacheBf16, "the prefill stores the cache's bf16 tensors");
   // wave priority while issuing MFMAs (0: never raised)
@@ -337,10 +337,13 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       const int voff = ((int)ld_row * (int)ss + ld_col) * 2;
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r)
-        st[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss * 2), 0);
+        if (!kPartialPass || ld_row + kRowsPerPass * r < kBlockN)
+          st[r] =
+              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss * 2), 0);
     } else {
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r) {
+        if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
         const int key = n0 + ld_row + kRowsPerPass * r;
         const bool valid = key < kv_end;
         const int kc = valid ? key : kv_end - 1;
@@ -368,7 +371,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       const int soff = (int)ld_row * (int)sss1 * 4;
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r) {
-        const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(rc, voff, (int)(kRowsPerPass * r * ss1), 0);
+        if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
+        const u32x2 c =
+            __builtin_amdgcn_raw_buffer_load_b64(rc, voff, (int)(kRowsPerPass * r * ss1), 0);
         const uint32_t sc =
             __builtin_amdgcn_raw_buffer_load_b32(rsc, soff, (int)(kRowsPerPass * r * sss1 * 4), 0);
         st[r] = u32x4{c[0], c[1], sc, 0u};
@@ -378,10 +383,13 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       const int voff = ((int)ld_row * (int)ss2 + ld_col) * 2;
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r)
-        st[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss2 * 2), 0);
+        if (!kPartialPass || ld_row + kRowsPerPass * r < kBlockN)
+          st[r] =
+              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss2 * 2), 0);
     } else {
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r) {
+        if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
         const int key = n0 + ld_row + kRowsPerPass * r;
         const bool valid = key < kv_end;
         const int kc = valid ? key : kv_end - 1;
@@ -417,6 +425,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const bool some_q = kQ && n0 < a.split;
 #pragma unroll
     for (int r = 0; r < kChunksPerThread; ++r) {
+      // (a row past the tile would land in the next buffer)
+      if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
       u32x4 x = st[r];
       if (kQ && all_q) {
         x = dequant(x);
@@ -908,11 +918,11 @@ void attn_prefill(const AttnArgs a) {
 
 // Decode over [prefix cache in format kFmt ; target], register-staged fills: the FP8 caches,
 // which are dequantised on their way into LDS.
-template <int kFmt>
-__global__ __launch_bounds__(64 * kStagedWaves)
+template <int kFmt, int kW>
+__global__ __launch_bounds__(64 * kW)
 __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd, kDecodeWavesPerSimd)))
 void attn_decode(const AttnArgs a) {
-  attn_fwd<true, false, kFmt, kDecodeBlockN, kStagedWaves>(a);
+  attn_fwd<true, false, kFmt, kDecodeBlockN, kW>(a);
 }
 
 // Decode over a bf16 cache: direct-to-LDS fills like the prefill's, 32-key tiles at 3 waves per
@@ -964,19 +974,28 @@ hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
     const dim3 grid((unsigned)(a.n_qtiles * heads));
     hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream, a);
   };
+  // the wider workgroup where its grid gives every CU at least two, else the narrower one
+  auto wide = [&](int waves) { return tiles(waves) * heads >= 2 * (int64_t)device_cus(); };
+  auto staged = [&](auto fmt_c) {
+    constexpr int kF = decltype(fmt_c)::value;
+    if (wide(kStagedWaves))
+      launch(attn_decode<kF, kStagedWaves>, kStagedWaves);
+    else
+      launch(attn_decode<kF, kStagedSmallWaves>, kStagedSmallWaves);
+  };
   switch (a.cache_fmt) {
     case kCacheBf16:
 #if BCA_DECODE_STAGED_BF16
-      launch(attn_decode<kCacheBf16>, kStagedWaves);
+      staged(std::integral_constant<int, kCacheBf16>{});
 #else
-      if (tiles(kDecodeDirectWaves) * heads >= 2 * (int64_t)device_cus())
+      if (wide(kDecodeDirectWaves))
         launch(attn_decode_direct<kDecodeDirectWaves>, kDecodeDirectWaves);
       else
         launch(attn_decode_direct<kDecodeDirectSmallWaves>, kDecodeDirectSmallWaves);
 #endif
       break;
-    case kCacheFp8V: launch(attn_decode<kCacheFp8V>, kStagedWaves); break;
-    case kCacheFp8KV: launch(attn_decode<kCacheFp8KV>, kStagedWaves); break;
+    case kCacheFp8V: staged(std::integral_constant<int, kCacheFp8V>{}); break;
+    case kCacheFp8KV: staged(std::integral_constant<int, kCacheFp8KV>{}); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -16,7 +16,8 @@ namespace bca {
 // at 3 waves per SIMD; their workgroups have 12 waves (one workgroup per CU), so each K/V tile
 // loaded into LDS serves 384 query rows.  A decode whose 12-wave grid would not give every CU
 // two workgroups runs 4-wave ones instead.  The decode over an FP8 cache dequantises through
-// registers and keeps 4 waves, 64-key tiles and 2 waves per SIMD (measured fastest for each).
+// registers and runs 64-key tiles at 2 waves per SIMD in 8-wave workgroups (4 on small grids)
+// (measured fastest for each).
 #ifndef BCA_QUERY_BLOCKS
 #define BCA_QUERY_BLOCKS 1
 #endif
@@ -53,7 +54,13 @@ constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
 constexpr int kPrefillWaves = BCA_PREFILL_WAVES;
 constexpr int kDecodeDirectWaves = BCA_DECODE_DIRECT_WAVES;  // large decode grids
 constexpr int kDecodeDirectSmallWaves = 4;                     // small decode grids
-constexpr int kStagedWaves = 4;
+// Waves per workgroup of the register-staged decode (FP8 caches): 8 on large grids (one
+// workgroup per CU at 2 waves per SIMD), 4 on grids under two such workgroups per CU.
+#ifndef BCA_STAGED_WAVES
+#define BCA_STAGED_WAVES 8
+#endif
+constexpr int kStagedWaves = BCA_STAGED_WAVES;
+constexpr int kStagedSmallWaves = 4;
 constexpr int kBlockM = 32 * kQueryBlocks * kPrefillWaves;  // prefill query tile (= plan tile)
 // Fewest query rows any decode workgroup takes (bounds the decode's grid).
 constexpr int kDecodeMinBlockM = 32 * kQueryBlocks * 4;

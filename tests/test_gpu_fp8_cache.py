@@ -185,6 +185,16 @@ def test_cfg_fp8_full_size(fname, fmt):
     ref = O.decode_cached(f32(qt[:, :, heads]), oc, f32(kt[:, :, heads]), f32(vt[:, :, heads]),
                           rows=rows)
     check(got, ref, "fresh-step decode over FP8 cache vs oracle")
+    # Heads are independent: two of them as strided views make a grid small enough for the
+    # 4-wave decode (the full one runs 8-wave workgroups); a row's arithmetic is the same.
+    two = slice(0, 2)
+    sub = bca.KVCache(fmt, cache.k[:, :, two], cache.v[:, :, two],
+                      None if cache.k_scale is None else cache.k_scale[:, :, two],
+                      None if cache.v_scale is None else cache.v_scale[:, :, two])
+    od2 = bca.decode_ex(plan, to_dev(qt)[:, :, two], sub, to_dev(kt)[:, :, two],
+                        to_dev(vt)[:, :, two])
+    torch.cuda.synchronize()
+    assert torch.equal(od[:, :, two], od2)
 
 
 def test_fp8_strided_cache_views():
