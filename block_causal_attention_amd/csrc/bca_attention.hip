@@ -1,12 +1,14 @@
 // Block-causal flash attention for gfx950 (MI355X): prefill (plan-driven) and prefix-cached
-// decode (mask-free over [cache ; target]); the prefill also writes the prefix-K/V cache.
+// decode (mask-free over [cache ; target]); the prefill also writes the prefix-K/V cache's bf16
+// tensors (an FP8 cache's quantised ones come from cache_quantize, bca_cache.hip).
 //
 // The rule ("Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo", section
 // "Block-causal attention is the cache-enabling boundary") makes every mask row a prefix of the
-// keys: row i sees exactly keys [0, hi(i)).  The planner turns that into, per tile of kBlockM
-// query rows, a key bound below which no mask is needed (kv_full) and one past which no key is
-// visible (kv_end); this kernel walks key tiles [0, kv_end), masks only the tiles that cross a
-// row limit, and never loads the rest.  Decode is the same kernel with no mask except the tail.
+// keys: row i sees exactly keys [0, hi(i)).  The planner turns that into, per query tile (the
+// prefill's workgroup), a key bound below which no mask is needed (kv_full) and one past which
+// no key is visible (kv_end); this kernel walks key tiles [0, kv_end), masks only the tiles that
+// cross a row limit, and never loads the rest.  Decode is the same kernel with no mask except
+// the tail.
 //
 // Work decomposition.  One workgroup = kW waves = one tile of 32 kW query rows of one (batch,
 // head); a wave owns kQueryBlocks blocks of 32 rows.  The prefill and the bf16-cache decode run
