@@ -377,3 +377,18 @@ def test_split_workspace_sizing_and_errors():
     assert call(4, ctypes.c_void_p(0x100000), 1 << 30) == _lib.BCA_ERR_ARG     # host-only plan
     assert b"HOST_ONLY" in lib.bca_last_error()
     assert call(1, None, 0) == _lib.BCA_ERR_ARG and b"HOST_ONLY" in lib.bca_last_error()
+
+
+def test_grid_guards_count_work_items():
+    """Launch-size checks count work-items (at most 2^32 - 1 per grid dimension), before any
+    device call: a host-only plan and fake pointers reach them."""
+    lib = _lib.load()
+    p = plan_host(W.TINY.block_ids())
+    # 12-wave prefill tiles: tiles * B * H * 768 work-items
+    assert call_prefill(p.handle, B=1 << 20, H=32) == _lib.BCA_ERR_ARG
+    assert b"grid" in lib.bca_last_error()
+    # the cache expansion: ceil(B * P * H / 16) blocks of 256
+    r = ctypes.byref
+    rc = lib.bca_cache_dequantize(1 << 22, 82, 32, 128, r(_cache(2)), r(_t()), r(_t()), None)
+    assert rc == _lib.BCA_ERR_ARG and b"too large" in lib.bca_last_error()
+    p.free()
