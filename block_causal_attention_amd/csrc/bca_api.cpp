@@ -466,8 +466,12 @@ bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale
 
 namespace {
 
-// Key ranges of a split decode: the requested count (0 = enough workgroups for about four per
-// CU, each range at least 8 units of 64 keys), at most one per unit, and no empty range.
+// Key ranges of a split decode: the requested count, or (0) the library's choice; at most one
+// range per unit, and no empty range.  The choice leaves a grid of at least 768 four-wave
+// workgroups (three per CU on 256 CUs) as it is.  A smaller grid is split into n ranges of at
+// least 8 units, n minimising ceil(base n / 768) / n + n / 100: whole rounds of 768 workgroups,
+// each range a 1/n of the keys, plus a small charge per range for the partial results and the
+// merge.  (The 512^2-target step, 256 workgroups unsplit, gets 3 ranges: one round.)
 void split_shape(const bca::HostPlan& hp, int32_t B, int32_t H, int32_t n_split,
                  int32_t* n_used, int32_t* tiles_per) {
   // in units of kSplitUnit keys, the same for every cache format
@@ -476,9 +480,17 @@ void split_shape(const bca::HostPlan& hp, int32_t B, int32_t H, int32_t n_split,
   const int64_t nt = (hp.target_len + 127) / 128;
   int64_t want = n_split;
   if (want == 0) {
+    constexpr int64_t kSlots = 768;
     const int64_t base = nt * B * H;
-    want = (1024 + base - 1) / base;
-    want = std::min<int64_t>(want, std::max<int64_t>(1, ktiles / 8));
+    const int64_t most = std::max<int64_t>(1, ktiles / 8);
+    want = 1;
+    if (base < kSlots) {
+      double best = 2.0;  // above any split's cost
+      for (int64_t n = 1; n <= most && n <= 4 * kSlots; ++n) {
+        const double cost = (double)((base * n + kSlots - 1) / kSlots) / (double)n + n / 100.0;
+        if (cost < best) best = cost, want = n;
+      }
+    }
   }
   want = std::max<int64_t>(1, std::min<int64_t>(want, ktiles));
   const int64_t per = (ktiles + want - 1) / want;

@@ -311,9 +311,11 @@ bca_status bca_qk_prologue(int32_t B, int64_t S, int32_t H, int32_t D, float eps
  * which is the same softmax up to rounding.
  *
  * bca_decode_split_workspace -- HOST.  *bytes = workspace bytes for (plan, B, H, n_split);
- * n_split = 0 lets the library choose (enough workgroups for about four per CU, ranges of at
- * least 8 units of 64 keys; at most one range per unit); *n_split_used (may be NULL) = the number
- * of ranges it will use (1 = plain decode, bytes = 0).  Neither depends on the cache format.  The plan's last block must be an image block (else BCA_ERR_NO_DECODE).
+ * n_split = 0 lets the library choose: one range where the unsplit decode already has 768
+ * workgroups of 128 query rows per (batch, head) tile (three per CU on 256 CUs), else the count n
+ * that best fills whole rounds of 768 workgroups (minimising ceil(768-unit rounds) / n + n / 100),
+ * with ranges of at least 8 units of 64 keys; at most one range per unit.  *n_split_used (may be
+ * NULL) = the number of ranges it will use (1 = plain decode, bytes = 0).  Neither depends on the cache format.  The plan's last block must be an image block (else BCA_ERR_NO_DECODE).
  *
  * bca_decode_split -- as bca_decode_ex, plus n_split (>= 0) and a DEVICE workspace of at least
  * that many bytes, 16-byte aligned, owned by the caller and not used by anything else while the

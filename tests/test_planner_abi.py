@@ -348,9 +348,11 @@ def test_cache_dequantize_argument_errors():
 def test_split_workspace_sizing_and_errors():
     lib = _lib.load()
     p = plan_host(W.EDIT_2REF_T512.block_ids())            # P = 8,304, N = 1,024
-    # B = 1, H = 32: 8 query tiles x 32 heads = 256 workgroups -> 4 ranges of 37 key tiles
+    # B = 1, H = 32: 8 query tiles x 32 heads = 256 workgroups -> 3 ranges (768 workgroups: one
+    # round of three per CU); 16 heads -> 6 ranges
     nbytes, used = bca.split_workspace(p, 1, 32)
-    assert used == 4 and nbytes == 4 * 1 * 1024 * 32 * 130 * 4
+    assert used == 3 and nbytes == 3 * 1 * 1024 * 32 * 130 * 4
+    assert bca.split_workspace(p, 1, 16)[1] == 6
     assert bca.split_workspace(p, 1, 32, 1) == (0, 1)      # one range: the plain decode
     assert bca.split_workspace(p, 1, 32, 146) == (146 * 1024 * 32 * 520, 146)
     assert bca.split_workspace(p, 1, 32, 500)[1] == 146    # at most one range per key tile
