@@ -280,6 +280,14 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // does any of this wave's query rows exist (wave-uniform)
   const int wave_row0 = row0 + wave * 32 * kQueryBlocks;
   const bool live = wave_row0 + 32 * kQueryBlocks > 0 && wave_row0 < n_rows;
+  // Prefill: the largest key limit among this wave's real rows (wave-uniform: limits never
+  // decrease along a sequence, so it is the last real row's).  A key tile starting at or past it
+  // is invisible to the whole wave, whose part of that tile then adds exact zeros.
+  int wave_lim = a.kv_len;
+  if constexpr (!kDecode) {
+    const int last = min(wave_row0 + 32 * kQueryBlocks - 1, n_rows - 1);
+    wave_lim = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : a.row_limit[rl_off + last]);
+  }
   constexpr bool kSkipDead = BCA_SKIP_DEAD_WAVES;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
@@ -678,9 +686,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     constexpr bool kMasked = decltype(masked_c)::value;
     const int n0 = j * kBlockN;
     store_cache(n0, cur);
-    // A wave whose query rows all lie past the end (in a partial last tile) only fills and
-    // synchronises.
-    if (!kSkipDead || live) {
+    // A wave that sees no key of a masked tile, or (option) whose query rows all lie past the
+    // end, only fills and synchronises: its share of the tile is exactly zero.
+    if ((!kSkipDead || live) && !(kMasked && !kDecode && n0 >= wave_lim)) {
 
       // ---- S^T = K Q^T
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPrioLevel);
