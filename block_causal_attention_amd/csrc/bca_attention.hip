@@ -288,7 +288,10 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const int last = min(wave_row0 + 32 * kQueryBlocks - 1, n_rows - 1);
     wave_lim = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : a.row_limit[rl_off + last]);
   }
-  constexpr bool kSkipDead = BCA_SKIP_DEAD_WAVES;
+  // (on for the 4-wave bf16 decode: measured +5% there, from its code generation rather than
+  // from the rare dead waves; the 12-wave kernels run 4% slower with it)
+  constexpr bool kSkipDead =
+      BCA_SKIP_DEAD_WAVES || (kDecode && kDirect && kW == kDecodeDirectSmallWaves);
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
   int lim[kQueryBlocks];
