@@ -318,3 +318,44 @@ def test_decode_workgroup_widths_agree_bitwise():
                      k[:1].contiguous(), v[:1].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(both[:1], one)
+
+
+def test_max_extent_strided():
+    """K/V at the ABI's extent limit: rows * stride_s just below 2^31 elements (4 GiB of bf16 per
+    tensor), through views with stride_s = 16,384 into padded buffers (one head of 128 values per
+    16,384-element row).  The prefill over S = 131,071 positions and the cached step over the same
+    buffers (cache = rows [0, P), target = rows [P, S)) are checked against the oracle on sampled
+    rows."""
+    stride = 16384
+    S = (2**31 - 128) // stride  # 131,071: S * stride + 128 <= 2^31 - 1
+    ids = np.concatenate([np.full(35, -1), np.full(65536, 0), np.full(100, -1),
+                          np.full(S - 35 - 65536 - 100, 1)]).astype(np.int32)
+    assert len(ids) == S and S * stride + 128 < 2**31
+    say(f"case: max extent S={S} stride_s={stride}")
+    qb, kb, vb = W.qkv(21, 1, S, 1, scaled=False)
+    views = []
+    for bits in (qb, kb, vb):
+        big = torch.empty((1, S, stride // 128, 128), dtype=torch.bfloat16, device=DEV)
+        view = big[:, :, :1]
+        view.copy_(to_dev(bits))
+        views.append(view)
+    q, k, v = views
+    assert q.stride(1) == stride
+    plan = bca.Plan(ids)
+    o = bca.prefill(plan, q, k, v)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, S, 2731), [34, 35, 65570, 65571, 65671, S - 1]]))
+    got = o[:, torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    ref = O.attention(f32(qb), f32(kb), f32(vb), ids, rows=rows)
+    check(got, ref, f"prefill, {len(rows)} rows")
+    P, N = plan.info.prefix_len, plan.info.target_len
+    assert P + N == S and P * stride + 128 < 2**31
+    od = bca.decode(plan, q[:, P:], k[:, :P], v[:, :P], k[:, P:], v[:, P:])
+    torch.cuda.synchronize()
+    drows = np.unique(np.concatenate([np.arange(0, N, 1999), [N - 1]]))
+    got = od[:, torch.from_numpy(drows).to(DEV)].cpu().numpy()
+    ref = O.decode(f32(qb[:, P:]), f32(kb[:, :P]), f32(vb[:, :P]), f32(kb[:, P:]), f32(vb[:, P:]),
+                   rows=drows)
+    check(got, ref, f"decode, {len(drows)} rows")
+    del views, q, k, v
+    torch.cuda.empty_cache()
