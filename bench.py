@@ -8,6 +8,12 @@ A step is one pass of the whole path on the 2-reference 1024^2 edit shape:
 The plan is built once before timing (it serves all layers and steps).  Inputs are resident in
 HBM before the timed region.  Useful work = 4 * D flops per visible (query, key) pair.
 
+Beside the step (side keys of the same JSON line, not part of `value`): the text-to-image 1024^2
+prefill (S = 4,352) and the four-reference 2048^2-target prefill (S = 32,912); the 49 cached
+steps of one generation, each with its own fresh target Q/K/V, timed call by call; the plan's
+build time split into host planning, device upload and first launches; the FP8 cache, Q/K
+prologue, varlen and split-decode calls.
+
 Prints ONE JSON line on stdout.  Diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -40,23 +46,63 @@ def to_dev(torch, bits, dev):
 
 KERNEL_SOURCE = os.path.join(ROOT, "block_causal_attention_amd", "csrc", "bca_attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
+
+
+def kernel_source_sha256():
+    import hashlib
+    try:
+        with open(KERNEL_SOURCE, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+
+
+def profile_entry(path, kernel):
+    """The committed rocprofv3 summary of `kernel` in `path` (a JSON file under profiles/), or
+    None when it was taken on a different kernel source than the one being benchmarked."""
+    try:
+        with open(path) as f:
+            entry = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return entry
 
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes (already scaled by the copy calibration), or None when those counters were taken on
     a different kernel source than the one being benchmarked."""
+    entry = profile_entry(TRAFFIC_FILE, kernel)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def mfma_utilisation():
+    """MFMA busy fractions per kernel from the committed rocprofv3 SQ-counter pass
+    (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles and over busy-CU cycles), for the kernel source
+    being benchmarked only."""
+    out = {}
+    for key in ("prefill_b1", "decode_cfg_b2"):
+        e = profile_entry(SQ_FILE, key)
+        if e is not None:
+            out[key] = {k: e[k] for k in ("kernel", "mfma_busy_of_simd_cycles",
+                                          "mfma_busy_of_busy_cu_cycles", "cu_busy_of_dispatch")
+                        if k in e}
+    return out or None
+
+
+def cpu_model():
     try:
-        import hashlib
-        with open(KERNEL_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        with open(TRAFFIC_FILE) as f:
-            entry = json.load(f).get(kernel)
-    except (OSError, ValueError):
-        return None
-    if not entry or entry.get("kernel_source_sha256") != sha:
-        return None
-    return entry.get("bytes_per_launch")
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
 
 
 def cpu_baseline(W, lay, ids, P, N, budget_rows, heads):
@@ -86,6 +132,7 @@ def cpu_baseline(W, lay, ids, P, N, budget_rows, heads):
     value = (flops_pre + flops_dec) / (t_pre + t_dec) / 1e12
     return {
         "value": value, "unit": "TFLOP/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+        "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
         "sample": (f"float64 NumPy oracle, batch 0, heads 0..{heads - 1}: {rows.size} prefill rows "
                    f"of the S={S} block-causal layout ({t_pre:.2f} s) + all {N} target rows of one "
                    f"cached decode over {P + N} keys ({t_dec:.2f} s); value = useful flops / time"),
@@ -269,6 +316,93 @@ def split_decode_timing(torch, bca, W, dev, iters=20):
     return out
 
 
+def prefill_timing(torch, bca, W, name, dev, iters=10):
+    """One prefill shape on its own (B = 1, H = 32, writing its prefix cache): ms per call (mean
+    and median of event-timed calls) and useful TFLOP/s from the median."""
+    lay = W.WORKLOADS[name]
+    ids = lay.block_ids()
+    S, H = lay.seq_len, lay.heads
+    plan = bca.Plan(ids)
+    P = plan.info.prefix_len
+    q, k, v = (to_dev(torch, x, dev) for x in W.qkv(W.SEEDS[name], 1, S, H))
+    o = torch.empty((1, S, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    kc = torch.empty((1, P, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+
+    def call():
+        bca.prefill(plan, q, k, v, out=o, k_cache=kc, v_cache=vc)
+    settle(torch, call, SETTLE["extra_ms"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record()
+    for i in range(iters):
+        call()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+    flops = 4.0 * HEAD_DIM * H * plan.info.useful_pairs
+    tf = flops / (np.median(ms) * 1e-3) / 1e12
+    log(f"prefill {name} S={S}: {ms.mean():.3f} ms (median {np.median(ms):.3f}) = {tf:.1f} TFLOP/s")
+    plan.free()
+    return {"workload": f"{lay.name}, S={S} (P={P}, N={S - P}), B=1, H={H}, writes the prefix cache",
+            "ms": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
+            "useful_tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "useful_gflop": round(flops / 1e9, 1)}
+
+
+def decode_generation_timing(torch, bca, plan, kc2, vc2, od, Bd, N, H, flops_dec, dev,
+                             steps=49, base_seed=4000):
+    """The cached steps of one generation (50 denoising steps = one prefill + 49 cached steps):
+    49 decode calls over the same CFG-pair prefix cache, each with its own fresh target Q/K/V,
+    all drawn and resident before timing, each call timed with its own event pair.  The fresh
+    inputs are drawn on the device (torch's Philox generator seeded base_seed + step,
+    N(0,1)/sqrt(128) in fp32, rounded to bf16), so that 49 x 201 MB of inputs take no host time."""
+    sets = []
+    for s in range(1, steps + 1):
+        g = torch.Generator(device=dev)
+        g.manual_seed(base_seed + s)
+        sets.append(tuple((torch.randn((Bd, N, H, HEAD_DIM), generator=g, device=dev,
+                                       dtype=torch.float32) * (1.0 / np.sqrt(HEAD_DIM)))
+                          .to(torch.bfloat16) for _ in range(3)))
+    settle(torch, lambda: bca.decode(plan, *sets[0][:1], kc2, vc2, *sets[0][1:], out=od),
+           SETTLE["extra_ms"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i, (qt, kt, vt) in enumerate(sets):
+        bca.decode(plan, qt, kc2, vc2, kt, vt, out=od)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    del sets
+    tf = flops_dec / (np.median(ms) * 1e-3) / 1e12
+    log(f"49 cached steps: median {np.median(ms):.3f} ms, mean {ms.mean():.3f}, total "
+        f"{ms.sum():.2f} ms = {tf:.1f} TFLOP/s (median)")
+    return {"workload": f"49 cached CFG steps, B={Bd}, N={N}, {H} heads, fresh target Q/K/V per "
+                        "step (device-drawn, seeds 4001..4049)",
+            "steps": steps, "ms_median": round(float(np.median(ms)), 4),
+            "ms_mean": round(float(ms.mean()), 4), "ms_total": round(float(ms.sum()), 3),
+            "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4),
+            "useful_tflops_median": round(tf, 2),
+            "frac_peak_median": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def plan_timing(torch, bca, ids, dev):
+    """Where the plan's build time goes: host planning alone (a host-only plan), the full build
+    (host planning + one device allocation and copy) twice, the first one in the process paying
+    the runtime's first-use costs."""
+    out = {}
+    t0 = time.perf_counter()
+    h = bca.Plan(ids, host_only=True)
+    out["host_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+    h.free()
+    for key in ("full_first_ms", "full_again_ms"):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p = bca.Plan(ids)
+        out[key] = round((time.perf_counter() - t0) * 1e3, 3)
+        p.free()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,6 +450,7 @@ def main():
     cfg = W.EDIT_2REF_CFG
     ids = pre.block_ids()
     S, H = pre.seq_len, pre.heads
+    plan_split = plan_timing(torch, bca, ids, dev)
     t0 = time.perf_counter()
     plan = bca.Plan(ids)
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -335,13 +470,25 @@ def main():
     kc2 = torch.empty((Bd, P, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
     vc2 = torch.empty_like(kc2)
     o2 = torch.empty((Bd, S, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    # the process's first launch (module load and first-dispatch costs; wall clock)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     bca.prefill(plan, q2, k2, v2, out=o2, k_cache=kc2, v_cache=vc2)
+    torch.cuda.synchronize()
+    plan_split["first_prefill_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
     del q2, k2, v2, o2
     sets = [tuple(to_dev(torch, x, dev) for x in W.decode_step_qkv(s + 1, Bd, N, H))
             for s in range(N_DECODE_SETS)]
     od = torch.empty((Bd, N, H, HEAD_DIM), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    log(f"setup done: S={S} P={P} N={N} useful pairs/head={pairs} plan {plan_ms:.2f} ms")
+    # the process's first decode launch (wall clock)
+    t0 = time.perf_counter()
+    bca.decode(plan, *sets[0][:1], kc2, vc2, *sets[0][1:], out=torch.empty(
+        (Bd, N, H, HEAD_DIM), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    plan_split["first_decode_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+    log(f"setup done: S={S} P={P} N={N} useful pairs/head={pairs} plan {plan_ms:.2f} ms "
+        f"({plan_split})")
     # no garbage-collector pauses inside a timed loop (a host stall leaves the GPU idle between
     # launches, and that idle time would count)
     gc.collect()
@@ -403,8 +550,11 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(key), "kernel": dom}
 
-    prologue = varlen = split = None
+    prologue = varlen = split = gen = pre_c2 = pre_c5 = None
     if not args.no_extras:
+        gen = decode_generation_timing(torch, bca, plan, kc2, vc2, od, Bd, N, H, flops_dec, dev)
+        pre_c2 = prefill_timing(torch, bca, W, "t2i_1024", dev)
+        pre_c5 = prefill_timing(torch, bca, W, "long_4ref", dev)
         prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
         varlen = varlen_timing(torch, bca, W, dev, H)
         split = split_decode_timing(torch, bca, W, dev)
@@ -437,6 +587,12 @@ def main():
                    "useful_tflops": round(dec_tf, 2), "frac_peak": round(dec_tf / PEAK_BF16_TFLOPS, 4),
                    "useful_gflop": round(flops_dec / 1e9, 1)},
         "plan_ms": round(plan_ms, 3),
+        "plan_build": plan_split,
+        "decode_49_steps": gen,
+        "prefill_t2i_1024": pre_c2,
+        "prefill_long_4ref": pre_c5,
+        "mfma_utilisation": mfma_utilisation(),
+        "kernel_source_sha256": kernel_source_sha256(),
         "fp8_cache": fp8,
         "qk_prologue": prologue,
         "varlen_prefill": varlen,

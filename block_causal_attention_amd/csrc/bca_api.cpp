@@ -15,6 +15,9 @@ struct bca_plan_s {
   bca::HostPlan host;
   int32_t host_only = 1;
   int device = -1;
+  // One device allocation holds every plan array (uploaded with one copy); the pointers below
+  // point into it.
+  void* d_arena = nullptr;
   int32_t* d_row_limit = nullptr;
   int32_t* d_kv_full = nullptr;
   int32_t* d_kv_end = nullptr;
@@ -37,22 +40,35 @@ bca_status hip_fail(hipError_t e, const char* what) {
 }
 
 void free_device(bca_plan_s* p) {
-  int32_t** arrs[] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end, &p->d_order, &p->d_tiles};
-  for (int32_t** a : arrs) {
-    if (*a) (void)hipFree(*a);
-    *a = nullptr;
-  }
+  if (p->d_arena) (void)hipFree(p->d_arena);
+  p->d_arena = nullptr;
+  p->d_row_limit = p->d_kv_full = p->d_kv_end = p->d_order = p->d_tiles = nullptr;
 }
 
-bca_status upload(const std::vector<int32_t>& src, int32_t** dst) {
-  const size_t bytes = src.size() * sizeof(int32_t);
-  hipError_t e = hipMalloc((void**)dst, bytes);
-  if (e != hipSuccess) {
-    *dst = nullptr;
-    return fail(BCA_ERR_ALLOC, std::string("hipMalloc of plan array: ") + hipGetErrorString(e));
+// The plan's device arrays: packed into one host staging buffer (each array starting on a
+// 256-byte boundary), then one hipMalloc and one synchronous hipMemcpy.
+bca_status upload(bca_plan_s* p) {
+  const bca::HostPlan& h = p->host;
+  const std::vector<int32_t>* src[5] = {&h.row_limit, &h.kv_full, &h.kv_end, &h.order, &h.tiles};
+  int32_t** dst[5] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end, &p->d_order, &p->d_tiles};
+  constexpr size_t kAlignInts = 64;
+  size_t off[5], total = 0;
+  for (int i = 0; i < 5; ++i) {
+    off[i] = total;
+    total += (src[i]->size() + kAlignInts - 1) / kAlignInts * kAlignInts;
   }
-  e = hipMemcpy(*dst, src.data(), bytes, hipMemcpyHostToDevice);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpy of plan array");
+  std::vector<int32_t> staging(total, 0);
+  for (int i = 0; i < 5; ++i)
+    std::copy(src[i]->begin(), src[i]->end(), staging.begin() + (ptrdiff_t)off[i]);
+  hipError_t e = hipMalloc(&p->d_arena, total * sizeof(int32_t));
+  if (e != hipSuccess) {
+    p->d_arena = nullptr;
+    return fail(BCA_ERR_ALLOC, std::string("hipMalloc of the plan arrays: ") +
+                                   hipGetErrorString(e));
+  }
+  e = hipMemcpy(p->d_arena, staging.data(), total * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy of the plan arrays");
+  for (int i = 0; i < 5; ++i) *dst[i] = static_cast<int32_t*>(p->d_arena) + off[i];
   return BCA_OK;
 }
 
@@ -233,12 +249,12 @@ bca_status make_plan(uint32_t flags, bca_plan_t* out, Build build) {
       delete p;
       return hip_fail(e, "hipGetDevice");
     }
-    bca_status s = BCA_OK;
-    if (s == BCA_OK) s = upload(p->host.row_limit, &p->d_row_limit);
-    if (s == BCA_OK) s = upload(p->host.kv_full, &p->d_kv_full);
-    if (s == BCA_OK) s = upload(p->host.kv_end, &p->d_kv_end);
-    if (s == BCA_OK) s = upload(p->host.order, &p->d_order);
-    if (s == BCA_OK) s = upload(p->host.tiles, &p->d_tiles);
+    bca_status s;
+    try {
+      s = upload(p);
+    } catch (const std::bad_alloc&) {
+      s = fail(BCA_ERR_ALLOC, "host allocation of the plan's staging buffer failed");
+    }
     if (s != BCA_OK) {
       free_device(p);
       delete p;

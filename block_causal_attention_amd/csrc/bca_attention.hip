@@ -61,39 +61,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 // prefers waves that can feed the matrix core and the others fill the gaps with softmax work.
 // Measured per kernel (interleaved A/B): +2% for the prefill and the FP8-cache decode; the
 // bf16-cache decode with 12-wave workgroups runs 4% faster without it.
-#ifndef BCA_MFMA_PRIO
-#define BCA_MFMA_PRIO 1
-#endif
-#ifndef BCA_DECODE_DIRECT_MFMA_PRIO
-#define BCA_DECODE_DIRECT_MFMA_PRIO 0
-#endif
-#ifndef BCA_SKIP_DEAD_WAVES
-#define BCA_SKIP_DEAD_WAVES 0
-#endif
-// Reads kept in flight ahead of the MFMAs (in steps of one MFMA) in the score and PV phases, or
-// 0 to leave the order to the compiler.  Measured (interleaved A/B, 12-wave kernels): 3 and 4
-// give the prefill +2.7% and the decode +0.5% over the compiler's own order; 2 and 2 or 2 and 4
-// the same within noise; 4 and 6 less on the prefill.
-#ifndef BCA_SCHED_K_DEPTH
-#define BCA_SCHED_K_DEPTH 3
-#endif
-#ifndef BCA_SCHED_V_DEPTH
-#define BCA_SCHED_V_DEPTH 4
-#endif
-constexpr int kSchedKDepth = BCA_SCHED_K_DEPTH;
-constexpr int kSchedVDepth = BCA_SCHED_V_DEPTH;
-#ifndef BCA_V_PAD
-#define BCA_V_PAD 16
-#endif
-#ifndef BCA_STAGE_SWIZZLE
-#define BCA_STAGE_SWIZZLE 0
-#endif
-// Which exponentials of the softmax run on the FMA pipe (exp2_fma below) instead of the
-// transcendental unit: 0 none, 1 all, 2 one of each pair.
-#ifndef BCA_EXP_POLY
-#define BCA_EXP_POLY 0
-#endif
-constexpr bool kStageSwizzle = BCA_STAGE_SWIZZLE;  // swizzled rows for the staging path too
+constexpr int kMfmaPrio = 1;
+constexpr int kDecodeDirectMfmaPrio = 0;
+// Reads kept in flight ahead of the MFMAs (in steps of one MFMA) in the score and PV phases.
+// Measured (interleaved A/B, 12-wave kernels): 3 and 4 give the prefill +2.7% and the decode
+// +0.5% over the compiler's own order; 2 and 2 or 2 and 4 the same within noise; 4 and 6 less on
+// the prefill.
+constexpr int kSchedKDepth = 3;
+constexpr int kSchedVDepth = 4;
+// Padding of the register-staged decode's V rows: 288 B.  (320 B rows make its transposed reads
+// bank-conflict-free on 64 banks but measured no faster: the decode is not bound by LDS
+// conflicts.)
+constexpr int kStagedVPad = 16;
 
 // A row's running max is raised only when its scores grew by more than kRescaleThreshold (log2
 // units), so p <= 2^16: exact in fp32, within bf16's exponent range, and l, O stay far below
@@ -144,24 +123,6 @@ __device__ inline float halves_sum(float x) {
 }
 
 // FP8 prefix cache (E4M3, one fp32 scale per (token, head) row; the exact rule is in bca.h).
-// 2^x on the FMA pipe, for the softmax's p (rounded to bf16 right after, 2^-9 relative): x is
-// clamped to [-127, 64], split into n = rint(x) (the 1.5 * 2^23 rounding trick) and f = x - n in
-// [-0.5, 0.5]; 2^f comes from a cubic fitted for relative error (1.0e-4 at most, constant term
-// exactly 1, so integer x gives an exact power of two) and n is added to its exponent field.  At
-// the clamp floor f = 0 and the sum is exactly +0, so masked scores (-inf) give p = 0; elsewhere
-// below -126 the result is a denormal or 0.  x above 64 (only on a first tile or a rescale, which
-// the caller redoes) saturates at 2^64.
-__device__ inline float exp2_fma(float x) {
-  constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
-  const float xc = __builtin_amdgcn_fmed3f(x, -127.0f, 64.0f);
-  const float t = xc + kRound;
-  const float f = xc - (t - kRound);
-  const float p = __builtin_fmaf(f, __builtin_fmaf(f, __builtin_fmaf(f, 0.05500871f, 0.24221068f),
-                                                   0.69328292f), 1.0f);
-  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) +
-                                       (__builtin_bit_cast(uint32_t, t) << 23));
-}
-
 // A staged row of a quantised tensor travels as {8 code bytes, scale bits, 0}; dequant turns it
 // into the 8 bf16 values E4M3(code) * scale that the LDS tile holds.
 __device__ inline u32x4 dequant(u32x4 x) {
@@ -197,17 +158,15 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   static_assert(kDecode || kFmt == kCacheBf16, "the prefill stores the cache's bf16 tensors");
   // wave priority while issuing MFMAs (0: never raised)
   constexpr int kPrioLevel =
-      kDecode && kDirect && kW == kDecodeDirectWaves ? BCA_DECODE_DIRECT_MFMA_PRIO : BCA_MFMA_PRIO;
+      kDecode && kDirect && kW == kDecodeDirectWaves ? kDecodeDirectMfmaPrio : kMfmaPrio;
   constexpr bool kPrio = kPrioLevel > 0;
   constexpr bool kKqSrc = kDecode && kFmt == kCacheFp8KV;
   constexpr bool kVqSrc = kDecode && kFmt != kCacheBf16;
   static_assert(!(kDirect && (kKqSrc || kVqSrc)), "direct loads move bf16 rows only");
   // LDS rows: unpadded (256 B) with their 16-byte chunks swizzled, or padded (272 B / 288 B).
-  constexpr bool kSwizzle = kDirect || kStageSwizzle;
+  constexpr bool kSwizzle = kDirect;
   constexpr int kKStride = kSwizzle ? kHeadDim : kHeadDim + 8;
-  // Padded V rows: 288 B.  (320 B rows make the transposed reads bank-conflict-free on 64 banks,
-  // BCA_V_PAD = 32, but measured no faster: the decode is not bound by LDS conflicts.)
-  constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + BCA_V_PAD;
+  constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + kStagedVPad;
   // The two ring buffers.  The direct-fill kernels (swizzled tiles, read by buffer constants:
   // their tile loop is unrolled by two below) keep them in separate arrays: reads of one are then
   // provably independent of the direct loads in flight into the other, so the compiler adds no
@@ -288,10 +247,11 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const int last = min(wave_row0 + 32 * kQueryBlocks - 1, n_rows - 1);
     wave_lim = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : a.row_limit[rl_off + last]);
   }
-  // (on for the 4-wave bf16 decode: measured +5% there, from its code generation rather than
-  // from the rare dead waves; the 12-wave kernels run 4% slower with it)
+  // Waves whose rows all lie past the end skip their compute in the 4-wave bf16 decode only
+  // (measured +5% there, from its code generation rather than from the rare dead waves; the
+  // 12-wave kernels run 4% slower with it).
   constexpr bool kSkipDead =
-      BCA_SKIP_DEAD_WAVES || (kDecode && kDirect && kW == kDecodeDirectSmallWaves);
+      kDecode && kDirect && kW == kDecodeDirectSmallWaves;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
   int lim[kQueryBlocks];
@@ -689,8 +649,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     constexpr bool kMasked = decltype(masked_c)::value;
     const int n0 = j * kBlockN;
     store_cache(n0, cur);
-    // A wave that sees no key of a masked tile, or (option) whose query rows all lie past the
-    // end, only fills and synchronises: its share of the tile is exactly zero.
+    // A wave that sees no key of a masked tile, or (4-wave bf16 decode) whose query rows all lie
+    // past the end, only fills and synchronises: its share of the tile is exactly zero.
     if ((!kSkipDead || live) && !(kMasked && !kDecode && n0 >= wave_lim)) {
 
       // ---- S^T = K Q^T
@@ -743,8 +703,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
           for (int i = 0; i < 16; i += 2) {
             const float x0 = __builtin_fmaf(s[qb][kb][i], c2, mneg);
             const float x1 = __builtin_fmaf(s[qb][kb][i + 1], c2, mneg);
-            const float p0 = BCA_EXP_POLY == 1 ? exp2_fma(x0) : __builtin_amdgcn_exp2f(x0);
-            const float p1 = BCA_EXP_POLY != 0 ? exp2_fma(x1) : __builtin_amdgcn_exp2f(x1);
+            const float p0 = __builtin_amdgcn_exp2f(x0);
+            const float p1 = __builtin_amdgcn_exp2f(x1);
             const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
             pb[qb][2 * kb + (i >> 3)][i & 7] = pp[0];
             pb[qb][2 * kb + (i >> 3)][(i & 7) + 1] = pp[1];
@@ -998,14 +958,10 @@ hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   };
   switch (a.cache_fmt) {
     case kCacheBf16:
-#if BCA_DECODE_STAGED_BF16
-      staged(std::integral_constant<int, kCacheBf16>{});
-#else
       if (wide(kDecodeDirectWaves))
         launch(attn_decode_direct<kDecodeDirectWaves>, kDecodeDirectWaves);
       else
         launch(attn_decode_direct<kDecodeDirectSmallWaves>, kDecodeDirectSmallWaves);
-#endif
       break;
     case kCacheFp8V: staged(std::integral_constant<int, kCacheFp8V>{}); break;
     case kCacheFp8KV: staged(std::integral_constant<int, kCacheFp8KV>{}); break;

@@ -18,58 +18,24 @@ namespace bca {
 // two workgroups runs 4-wave ones instead.  The decode over an FP8 cache dequantises through
 // registers and runs 64-key tiles at 2 waves per SIMD in 8-wave workgroups (4 on small grids)
 // (measured fastest for each).
-#ifndef BCA_QUERY_BLOCKS
-#define BCA_QUERY_BLOCKS 1
-#endif
-#ifndef BCA_PREFILL_WAVES
-#define BCA_PREFILL_WAVES 12
-#endif
-#ifndef BCA_DECODE_DIRECT_WAVES
-#define BCA_DECODE_DIRECT_WAVES 12
-#endif
-// The bf16-cache decode through the staged kernel instead of the direct one (for comparisons).
-#ifndef BCA_DECODE_STAGED_BF16
-#define BCA_DECODE_STAGED_BF16 0
-#endif
-#ifndef BCA_PREFILL_BLOCK_N
-#define BCA_PREFILL_BLOCK_N 32
-#endif
-#ifndef BCA_PREFILL_WAVES_PER_SIMD
-#define BCA_PREFILL_WAVES_PER_SIMD 3
-#endif
-#ifndef BCA_DECODE_BLOCK_N
-#define BCA_DECODE_BLOCK_N 64
-#endif
-#ifndef BCA_DECODE_WAVES_PER_SIMD
-#define BCA_DECODE_WAVES_PER_SIMD 2
-#endif
-#ifndef BCA_DECODE_DIRECT_BLOCK_N
-#define BCA_DECODE_DIRECT_BLOCK_N 32
-#endif
-#ifndef BCA_DECODE_DIRECT_WAVES_PER_SIMD
-#define BCA_DECODE_DIRECT_WAVES_PER_SIMD 3
-#endif
 constexpr int kHeadDim = 128;  // the only head width the kernels are built for
-constexpr int kQueryBlocks = BCA_QUERY_BLOCKS;
-constexpr int kPrefillWaves = BCA_PREFILL_WAVES;
-constexpr int kDecodeDirectWaves = BCA_DECODE_DIRECT_WAVES;  // large decode grids
-constexpr int kDecodeDirectSmallWaves = 4;                     // small decode grids
+constexpr int kQueryBlocks = 1;
+constexpr int kPrefillWaves = 12;
+constexpr int kDecodeDirectWaves = 12;      // large decode grids
+constexpr int kDecodeDirectSmallWaves = 4;  // small decode grids
 // Waves per workgroup of the register-staged decode (FP8 caches): 8 on large grids (one
 // workgroup per CU at 2 waves per SIMD), 4 on grids under two such workgroups per CU.
-#ifndef BCA_STAGED_WAVES
-#define BCA_STAGED_WAVES 8
-#endif
-constexpr int kStagedWaves = BCA_STAGED_WAVES;
+constexpr int kStagedWaves = 8;
 constexpr int kStagedSmallWaves = 4;
 constexpr int kBlockM = 32 * kQueryBlocks * kPrefillWaves;  // prefill query tile (= plan tile)
 // Fewest query rows any decode workgroup takes (bounds the decode's grid).
 constexpr int kDecodeMinBlockM = 32 * kQueryBlocks * 4;
-constexpr int kPrefillBlockN = BCA_PREFILL_BLOCK_N;
-constexpr int kPrefillWavesPerSimd = BCA_PREFILL_WAVES_PER_SIMD;
-constexpr int kDecodeBlockN = BCA_DECODE_BLOCK_N;  // register-staged decode (FP8 caches)
-constexpr int kDecodeWavesPerSimd = BCA_DECODE_WAVES_PER_SIMD;
-constexpr int kDecodeDirectBlockN = BCA_DECODE_DIRECT_BLOCK_N;  // direct-fill decode (bf16 cache)
-constexpr int kDecodeDirectWavesPerSimd = BCA_DECODE_DIRECT_WAVES_PER_SIMD;
+constexpr int kPrefillBlockN = 32;
+constexpr int kPrefillWavesPerSimd = 3;
+constexpr int kDecodeBlockN = 64;  // register-staged decode (FP8 caches)
+constexpr int kDecodeWavesPerSimd = 2;
+constexpr int kDecodeDirectBlockN = 32;  // direct-fill decode (bf16 cache)
+constexpr int kDecodeDirectWavesPerSimd = 3;
 // A split decode's key ranges are whole multiples of kSplitUnit keys, whatever the kernel's tile
 // width (which divides it), so the workspace a plan needs does not depend on the cache format.
 constexpr int kSplitUnit = 64;

@@ -7,7 +7,7 @@
  * every image block is bidirectional inside, and blocks are causal in sequence order
  * ("Qwen-Image 2.1: Block-Causal Attention, Prefix KV Cache, and Turbo", section "Block-causal
  * attention is the cache-enabling boundary"; the 10100.com Qwen-Image 2.1 article, Block-Causal
- * mask part, which writes the rule as (query_position >= key_position) or same_image_block).
+ * mask part, which states the same rule as a boolean expression over positions and blocks).
  *
  * Shapes.  Multi-head attention (not GQA) with H heads of width D = 128; Q, K and V are
  * [B, S, H, D] bf16 with D contiguous (same guide, section "One stream for text, reference
@@ -88,7 +88,8 @@ enum { BCA_PLAN_HOST_ONLY = 1u };
  * The plan holds, for every row i, its key limit hi(i): row i sees exactly the keys [0, hi(i)),
  * with hi(i) = i + 1 for text and the end of its block for image rows.  For text this is the
  * bottom-right aligned causal triangle of a segment whose query count is below its key count
- * (10100.com article, piecewise-attention part: mask = ones(q_len, kv_len).tril(kv_len - q_len)).
+ * (10100.com article, piecewise-attention part: a segment of q queries after k - q earlier keys
+ * lets its query r see keys 0 .. k - q + r).
  * The rows are cut into n_qtiles tiles of block_m rows that end at the last row: tile t holds
  * rows [S - (n_qtiles - t) block_m, S - (n_qtiles - 1 - t) block_m) clipped at 0, so only tile 0
  * may be partial.  Per tile it stores kv_full[t] (min hi over its rows: key tiles below it need no
@@ -96,7 +97,7 @@ enum { BCA_PLAN_HOST_ONLY = 1u };
  *
  * flags: 0, or BCA_PLAN_HOST_ONLY to skip the device upload (such a plan can be inspected but
  * not launched).  Without it, the plan owns small int32 device arrays on the current device
- * (hipMalloc + synchronous hipMemcpy, the only allocations in this library).
+ * (one hipMalloc and one synchronous hipMemcpy, the only allocations in this library).
  * *out receives the plan; release it with bca_plan_free.
  */
 bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, bca_plan_t* out);

@@ -101,8 +101,8 @@ def prefix_split(ids: Sequence[int]) -> Tuple[int, int, bool]:
 def visibility_mask(ids: Sequence[int], rows: Optional[np.ndarray] = None) -> np.ndarray:
     """M[i, j] = (i >= j) or (i and j are in the same image block).
 
-    [QI21-article], Block-Causal mask part: visible = (query_position >= key_position) or
-    same_image_block.  Text is -1 and is strictly causal ([QI21-guide], "Block-causal attention
+    [QI21-article], Block-Causal mask part: a query sees a key when the key is not later than the
+    query, or when both belong to one image block.  Text is -1 and is strictly causal ([QI21-guide], "Block-causal attention
     is the cache-enabling boundary"), so "same image block" requires a non-negative id.
     Returns bool [len(rows), S] (all rows when ``rows`` is None).
     """

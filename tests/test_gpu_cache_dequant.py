@@ -11,6 +11,9 @@
   two-reference editing shape at full size (P = 8,304, N = 4,096, H = 32).
 * Strided (non-contiguous) inputs and outputs.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -172,7 +175,19 @@ def test_decode_over_expansion_matches_the_fp8_decode(fmt):
 def test_decode_over_expansion_full_size(fmt):
     lay = W.EDIT_2REF
     say(f"case: decode over expansion, 2-ref edit full size, fmt={fmt}")
-    plan, _, fused, expanded = _fp8_decode_pair(lay.block_ids(), 1, lay.heads, fmt,
-                                                W.SEEDS["edit_2ref"])
-    assert (plan.info.prefix_len, plan.info.target_len) == (8304, 4096)
+    ids = lay.block_ids()
+    plan, (qb, kb, vb), fused, expanded = _fp8_decode_pair(ids, 1, lay.heads, fmt,
+                                                           W.SEEDS["edit_2ref"])
+    P, N, H = plan.info.prefix_len, plan.info.target_len, lay.heads
+    assert (P, N) == (8304, 4096)
     check(expanded.cpu().numpy(), fused.cpu().numpy(), "expanded vs the FP8 decode, full size")
+    # and both against the oracle's decode over the oracle's own FP8 cache, every row and head
+    # (one thread per head: NumPy releases the interpreter lock in its products)
+    oc = O.prefix_cache_fp8(f32(kb), f32(vb), ids, fmt)
+    ockv = O.cache_values(oc)
+    qf, kf, vf = f32(qb[:, P:]), f32(kb[:, P:]), f32(vb[:, P:])
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        parts = list(ex.map(lambda h: O.decode(qf, *ockv, kf, vf, heads=[h]), range(H)))
+    ref = np.concatenate(parts, axis=2)
+    check(expanded.cpu().numpy(), ref, "expanded, bf16 decode vs oracle, full size")
+    check(fused.cpu().numpy(), ref, "FP8 decode vs oracle, full size")

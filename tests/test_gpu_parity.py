@@ -151,7 +151,7 @@ def count_probe_expected(ids, v):
 
 
 @pytest.mark.parametrize("name,H", [("tiny", 2), ("t2i_1024", 4), ("edit_2ref", 32),
-                                    ("long_4ref", 2)])
+                                    ("long_4ref", 32)])
 def test_count_probe_exact(name, H):
     lay = W.WORKLOADS[name]
     ids = lay.block_ids()
@@ -175,7 +175,7 @@ def test_count_probe_exact(name, H):
         assert (np.abs(gd - wd) <= 2 * np.spacing(np.abs(wd).astype(np.float32))).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "edit_2ref"])
+@pytest.mark.parametrize("name", ["tiny", "edit_2ref", "long_4ref"])
 def test_leak_probe_bitwise(name):
     """Overwrite every key/value a row range cannot see; those rows must not change at all."""
     lay = W.WORKLOADS[name]
