@@ -26,7 +26,7 @@ from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
            "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen",
-           "decode_split", "split_workspace", "dequantize_cache"]
+           "decode_split", "split_workspace", "dequantize_cache", "decode_split_noalloc"]
 
 
 class BcaError(RuntimeError):
@@ -476,6 +476,35 @@ def decode_split(plan: Plan, q, cache: Optional[KVCache], k, v, *, n_split: int 
             ctypes.byref(_desc(v, "v", torch.bfloat16)),
             ctypes.byref(_desc(out, "out", torch.float32)), n_split, ws, wsb,
             ctypes.c_void_p(stream)))
+    return out
+
+
+def decode_split_noalloc(plan: Plan, q, cache: Optional[KVCache], k, v, *, n_split: int = 0,
+                         scale: Optional[float] = None, out=None):
+    """Split-KV cached decode whose partial results live in the library's own device scratch
+    (bca_decode_split_noalloc): the library allocates nothing.  `out` is allocated here (by
+    torch) only when not given."""
+    import torch
+
+    B, N, H, D = q.shape
+    P = plan.info.prefix_len
+    if N != plan.info.target_len:
+        raise ValueError(f"target length {N} != plan's {plan.info.target_len}")
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (B, N, H, D):
+            raise ValueError(f"{name} must be [B, {N}, H, D]")
+    if P > 0 and cache is None:
+        raise ValueError("the prefix is not empty: a cache is required")
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+    c = ctypes.byref(cache._struct(B, P, H, D)) if P > 0 else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_decode_split_noalloc(
+            plan.handle, B, H, D, _scale(scale), ctypes.byref(_desc(q, "q", torch.bfloat16)), c,
+            ctypes.byref(_desc(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc(v, "v", torch.bfloat16)),
+            ctypes.byref(_desc(out, "out", torch.float32)), n_split, ctypes.c_void_p(stream)))
     return out
 
 

@@ -28,6 +28,7 @@ struct bca_plan_s {
 namespace {
 
 constexpr int64_t kHeadDimElems = bca::kHeadDim;
+static_assert(BCA_SCRATCH_BYTES == bca::kScratchBytes, "bca.h states the scratch size");
 thread_local std::string g_last_error;
 
 bca_status fail(bca_status s, const std::string& msg) {
@@ -631,6 +632,34 @@ bca_status bca_decode_split(bca_plan_t plan, int32_t B, int32_t H, int32_t D, fl
                             void* stream) {
   return decode_impl(plan, B, H, D, scale, q_tgt, cache, k_tgt, v_tgt, o, true, n_split,
                      workspace, workspace_bytes, stream);
+}
+
+bca_status bca_decode_split_noalloc(bca_plan_t plan, int32_t B, int32_t H, int32_t D,
+                                    float scale, const bca_tensor* q_tgt,
+                                    const bca_kv_cache* cache, const bca_tensor* k_tgt,
+                                    const bca_tensor* v_tgt, const bca_tensor* o, int32_t n_split,
+                                    void* stream) {
+  if (plan == nullptr) return fail(BCA_ERR_ARG, "plan is NULL");
+  if (B < 1 || H < 1) return fail(BCA_ERR_ARG, "B and H must be >= 1");
+  if (n_split < 0) return fail(BCA_ERR_ARG, "n_split must be >= 0 (0 = chosen by the library)");
+  if (!plan->host.decode_ok)
+    return fail(BCA_ERR_NO_DECODE, "the layout's last block is text; cached decode needs the "
+                                   "target image block last");
+  int32_t n_used = 1, per = 0;
+  split_shape(plan->host, B, H, n_split, &n_used, &per);
+  const int64_t need = split_bytes(plan->host, B, H, n_used);
+  if (need > bca::kScratchBytes)
+    return fail(BCA_ERR_ARG, "the split needs " + std::to_string(need) +
+                                 " bytes of partial results; the library's scratch holds " +
+                                 std::to_string(bca::kScratchBytes) +
+                                 " (use bca_decode_split with a caller workspace)");
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = bca::scratch_memory(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address (hipGetSymbolAddress)");
+  }
+  return decode_impl(plan, B, H, D, scale, q_tgt, cache, k_tgt, v_tgt, o, true, n_split, ws,
+                     need > 0 ? bca::kScratchBytes : 0, stream);
 }
 
 bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,

@@ -40,6 +40,7 @@
 // keeps the K reads and the transposed V reads free of bank conflicts; staged fills write padded
 // rows.
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "bca_internal.h"
@@ -925,7 +926,37 @@ int device_cus() {
 }
 
 
+// Library-owned device scratch for the allocation-free split decode (bca_decode_split_noalloc):
+// the partial O, m and l of its key ranges.  One copy per GPU the library runs on, held until the
+// process ends; every call on a GPU shares it.  In host code the array's name is only a
+// stand-in: its device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) static unsigned char scratch[kScratchBytes];
+
 }  // namespace
+
+hipError_t scratch_memory(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    void* p = ptrs[dev].load(std::memory_order_acquire);
+    if (p != nullptr) {
+      *out = p;
+      return hipSuccess;
+    }
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+  if (e != hipSuccess) return e;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  if (dev >= 0 && dev < kMaxDevices) ptrs[dev].store(p, std::memory_order_release);
+  *out = p;
+  return hipSuccess;
+}
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.n_qtiles * a.batch * a.heads);

@@ -168,6 +168,12 @@ struct QuantArgs {
   int32_t heads;
 };
 
+// Device scratch owned by the library for the allocation-free split decode: kScratchBytes per
+// GPU.  scratch_memory returns the current device's copy (its address is looked up once per
+// device); it allocates nothing.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+hipError_t scratch_memory(void** out);
+
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);

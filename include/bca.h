@@ -330,6 +330,26 @@ bca_status bca_decode_split(bca_plan_t plan, int32_t B, int32_t H, int32_t D, fl
                             int32_t n_split, void* workspace, int64_t workspace_bytes,
                             void* stream);
 
+/*
+ * bca_decode_split_noalloc -- for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): bca_decode_split with the
+ * same arguments and result, minus the workspace.  The key ranges' partial results go to a
+ * scratch buffer the library owns: BCA_SCRATCH_BYTES (64 MiB) of device memory per GPU, reserved
+ * when the library is loaded on that GPU and held until the process ends.  This call allocates
+ * nothing (its first call on a device looks up that device's copy of the buffer once).  A split
+ * whose partial results (bca_decode_split_workspace's bytes) exceed BCA_SCRATCH_BYTES is
+ * BCA_ERR_ARG and enqueues nothing; one range (n_split_used = 1) uses no scratch.  Every call on
+ * one GPU shares its scratch, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that may overlap on one GPU (different streams, or threads racing on one)
+ * race on it and must be ordered by the caller.  Enqueues two kernels on stream (one when
+ * unsplit).
+ */
+#define BCA_SCRATCH_BYTES (64ll << 20)
+bca_status bca_decode_split_noalloc(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
+                                    const bca_tensor* q_tgt, const bca_kv_cache* cache,
+                                    const bca_tensor* k_tgt, const bca_tensor* v_tgt,
+                                    const bca_tensor* o, int32_t n_split, void* stream);
+
 /* Static name of a status code ("BCA_OK", ...); "unknown status" for other values. */
 const char* bca_status_str(bca_status status);
 
