@@ -87,11 +87,19 @@ EDIT_2REF_T512 = Layout("2-ref 1024^2 edit, 512^2 target: [t48][ref 4096][t40][r
                         "[target 1024]", _two_ref_edit()[:-1] + (("image", 1024),), batch=1,
                         heads=32)
 
+# Classifier-free guidance with prompts of different lengths: the cond branch is the 2-ref edit
+# above; the uncond branch keeps the references and the target but has a shorter first text
+# segment (8 positions in place of 48, standing for a short negative prompt).  Each branch keeps
+# its own prefix cache.
+EDIT_2REF_UNCOND = Layout("2-ref 1024^2 edit, uncond branch: [t8][ref 4096][t40][ref 4096][t24]"
+                          "[target 4096]", (("text", 8),) + _two_ref_edit()[1:], batch=1, heads=32)
+CFG_VARLEN = (EDIT_2REF, EDIT_2REF_UNCOND)
+
 WORKLOADS = {"tiny": TINY, "t2i_1024": T2I_1024, "edit_2ref": EDIT_2REF,
              "edit_2ref_cfg": EDIT_2REF_CFG, "long_4ref": LONG_4REF,
              "edit_2ref_t512": EDIT_2REF_T512}
 SEEDS = {"tiny": 1001, "t2i_1024": 2001, "edit_2ref": 3001, "edit_2ref_cfg": 4000,
-         "long_4ref": 5001, "edit_2ref_t512": 6001}
+         "long_4ref": 5001, "edit_2ref_t512": 6001, "cfg_varlen": 7001}
 DECODE_STEPS = 49  # 50 denoising steps: one prefill, then 49 cached steps
 
 

@@ -282,6 +282,46 @@ def varlen_timing(torch, bca, W, dev, H, iters=10):
             "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "useful_gflop": round(flops / 1e9, 1)}
 
 
+def cfg_varlen_timing(torch, bca, W, dev, iters=10):
+    """CFG branches whose prompts differ in length, one launch each for the prefill (storing
+    each branch's own prefix cache) and for the cached step over the two caches: the 2-ref edit
+    (S = 12,400) as the cond branch and the same layout with an 8-position prompt (S = 12,360)
+    as the uncond branch, packed, H = 32."""
+    ids_list = [lay.block_ids() for lay in W.CFG_VARLEN]
+    H = W.EDIT_2REF.heads
+    plan = bca.Plan.varlen(ids_list)
+    sq = plan.sequences()
+    R, P, N = int(sq[:, 1].sum()), plan.info.prefix_len, plan.info.target_len
+    q, k, v = (to_dev(torch, x[0], dev) for x in W.qkv(W.SEEDS["cfg_varlen"], 1, R, H))
+    o = torch.empty((R, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    kc = torch.empty((P, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    qt, kt, vt = (to_dev(torch, x[0], dev) for x in W.qkv(W.SEEDS["cfg_varlen"] + 1, 1, N, H))
+    od = torch.empty((N, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    pre = lambda: bca.prefill_varlen(plan, q, k, v, k_cache=kc, v_cache=vc, out=o)
+    dec = lambda: bca.decode_varlen(plan, qt, kc, vc, kt, vt, out=od)
+    out = {"workload": "CFG pair, packed: cond 2-ref edit S=12400 (P=8304) + uncond with an "
+                       f"8-position prompt S=12360 (P=8264), N=4096 each, H={H}"}
+    flops = {"prefill": 4.0 * HEAD_DIM * H * plan.info.useful_pairs,
+             "decode": sum(4.0 * HEAD_DIM * H * int(n) * int(p + n) for p, n in sq[:, 2:4])}
+    for name, fn in (("prefill", pre), ("decode", dec)):
+        settle(torch, fn, SETTLE["extra_ms"])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        tf = flops[name] / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "useful_tflops": round(tf, 2),
+                     "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "useful_gflop": round(flops[name] / 1e9, 1)}
+        log(f"cfg varlen {name}: {ms:.3f} ms = {tf:.1f} TFLOP/s")
+    plan.free()
+    return out
+
+
 def split_decode_timing(torch, bca, W, dev, iters=20):
     """Cached step of the 512^2-target edit (N = 1,024 under P = 8,304, B = 1, H = 32): the
     plain decode (8 x 32 = 256 workgroups) against the split-KV decode (library-chosen ranges)."""
@@ -550,13 +590,14 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(key), "kernel": dom}
 
-    prologue = varlen = split = gen = pre_c2 = pre_c5 = None
+    prologue = varlen = split = gen = pre_c2 = pre_c5 = cfg = None
     if not args.no_extras:
         gen = decode_generation_timing(torch, bca, plan, kc2, vc2, od, Bd, N, H, flops_dec, dev)
         pre_c2 = prefill_timing(torch, bca, W, "t2i_1024", dev)
         pre_c5 = prefill_timing(torch, bca, W, "long_4ref", dev)
         prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
         varlen = varlen_timing(torch, bca, W, dev, H)
+        cfg = cfg_varlen_timing(torch, bca, W, dev)
         split = split_decode_timing(torch, bca, W, dev)
     fp8 = None if args.no_fp8 else fp8_timings(torch, bca, W, plan, q, k, v, o, sets, od,
                                                flops_pre, flops_dec, Bd, S, H, P, dev)
@@ -596,6 +637,7 @@ def main():
         "fp8_cache": fp8,
         "qk_prologue": prologue,
         "varlen_prefill": varlen,
+        "cfg_varlen": cfg,
         "split_decode": split,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -26,7 +26,8 @@ from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
            "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen",
-           "decode_split", "split_workspace", "dequantize_cache", "decode_split_noalloc"]
+           "decode_split", "split_workspace", "dequantize_cache", "decode_split_noalloc",
+           "decode_varlen"]
 
 
 class BcaError(RuntimeError):
@@ -106,6 +107,14 @@ class Plan:
         _check(_lib.load().bca_plan_export(self.handle, p(seg), p(rl), p(kf), p(ke), p(od)))
         return {"segments": seg.reshape(-1, 3), "row_limit": rl, "kv_full": kf, "kv_end": ke,
                 "order": od}
+
+    def sequences(self) -> np.ndarray:
+        """int64 [n_sequences, 6] (bca_plan_sequences): per sequence its first tensor row,
+        length, prefix P_b, target N_b, first cache row c_b and first target row t_b."""
+        out = np.empty((self.info.n_sequences, 6), np.int64)
+        _check(_lib.load().bca_plan_sequences(
+            self.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        return out
 
     def free(self) -> None:
         if self._h:
@@ -409,10 +418,12 @@ def _desc3(t, name: str, dtype) -> BcaTensor:
     return BcaTensor(t.data_ptr(), 0, ss, sh)
 
 
-def prefill_varlen(plan: Plan, q, k, v, *, scale: Optional[float] = None, out=None):
+def prefill_varlen(plan: Plan, q, k, v, *, k_cache=None, v_cache=None,
+                   scale: Optional[float] = None, out=None):
     """Block-causal prefill of every sequence of a varlen plan (bca_prefill_varlen).  q, k, v:
     bf16 [rows, H, D]; returns fp32 [rows, H, D] (rows outside the sequences left untouched:
-    zero when `out` is not given)."""
+    zero when `out` is not given).  k_cache, v_cache (optional, both or neither): bf16
+    [plan.info.prefix_len, H, D], receiving every sequence's prefix rows, packed."""
     import torch
 
     R, H, D = q.shape
@@ -420,15 +431,58 @@ def prefill_varlen(plan: Plan, q, k, v, *, scale: Optional[float] = None, out=No
         raise ValueError("q, k, v must share the shape [rows, H, D]")
     if R < plan.info.rows:
         raise ValueError(f"the plan spans {plan.info.rows} rows, the tensors {R}")
+    if (k_cache is None) != (v_cache is None):
+        raise ValueError("give both k_cache and v_cache, or neither")
+    P = plan.info.prefix_len
+    if k_cache is not None:
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            if tuple(t.shape) != (P, H, D):
+                raise ValueError(f"{name} must be [{P}, H, D]")
     if out is None:
         out = torch.zeros((R, H, D), dtype=torch.float32, device=q.device)
     if tuple(out.shape) != (R, H, D):
         raise ValueError("out has the wrong shape")
+    store = k_cache is not None and P > 0
+    kc = ctypes.byref(_desc3(k_cache, "k_cache", torch.bfloat16)) if store else None
+    vc = ctypes.byref(_desc3(v_cache, "v_cache", torch.bfloat16)) if store else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         _check(_lib.load().bca_prefill_varlen(
             plan.handle, H, D, _scale(scale), ctypes.byref(_desc3(q, "q", torch.bfloat16)),
             ctypes.byref(_desc3(k, "k", torch.bfloat16)),
+            ctypes.byref(_desc3(v, "v", torch.bfloat16)),
+            ctypes.byref(_desc3(out, "out", torch.float32)), kc, vc, ctypes.c_void_p(stream)))
+    return out
+
+
+def decode_varlen(plan: Plan, q, k_cache, v_cache, k, v, *, scale: Optional[float] = None,
+                  out=None):
+    """Cached step of every sequence of a varlen plan in one launch (bca_decode_varlen).  q, k, v:
+    bf16 [plan.info.target_len, H, D] (the sequences' targets, packed); k_cache, v_cache: bf16
+    [plan.info.prefix_len, H, D] as prefill_varlen stores them.  Returns fp32 like q."""
+    import torch
+
+    N, H, D = q.shape
+    P = plan.info.prefix_len
+    if N != plan.info.target_len:
+        raise ValueError(f"{N} target rows != the plan's {plan.info.target_len}")
+    checks = [("k", k, N), ("v", v, N)]
+    if P > 0 or k_cache is not None or v_cache is not None:
+        checks += [("k_cache", k_cache, P), ("v_cache", v_cache, P)]
+    for name, t, n in checks:
+        if t is None or tuple(t.shape) != (n, H, D):
+            raise ValueError(f"{name} must be [{n}, H, D]")
+    if out is None:
+        out = torch.empty((N, H, D), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (N, H, D):
+        raise ValueError("out has the wrong shape")
+    kc = ctypes.byref(_desc3(k_cache, "k_cache", torch.bfloat16)) if P > 0 else None
+    vc = ctypes.byref(_desc3(v_cache, "v_cache", torch.bfloat16)) if P > 0 else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        _check(_lib.load().bca_decode_varlen(
+            plan.handle, H, D, _scale(scale), ctypes.byref(_desc3(q, "q", torch.bfloat16)),
+            kc, vc, ctypes.byref(_desc3(k, "k", torch.bfloat16)),
             ctypes.byref(_desc3(v, "v", torch.bfloat16)),
             ctypes.byref(_desc3(out, "out", torch.float32)), ctypes.c_void_p(stream)))
     return out

@@ -24,7 +24,8 @@ EXPORTED = ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export",
             "bca_decode", "bca_prefill_ex", "bca_decode_ex", "bca_rope_positions", "bca_rope_table",
             "bca_qk_prologue", "bca_plan_varlen", "bca_prefill_varlen",
             "bca_decode_split_workspace", "bca_decode_split", "bca_cache_dequantize",
-            "bca_decode_split_noalloc", "bca_status_str", "bca_last_error")
+            "bca_decode_split_noalloc", "bca_plan_sequences", "bca_decode_varlen",
+            "bca_status_str", "bca_last_error")
 BCA_SCRATCH_BYTES = 64 << 20
 
 
@@ -85,7 +86,10 @@ def load() -> ctypes.CDLL:
     lib.bca_plan_varlen.argtypes = [i32p, i64p, i64p, ctypes.c_int32, ctypes.c_uint32,
                                     ctypes.POINTER(P)]
     lib.bca_prefill_varlen.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
-                                       T, T, T, T, P]
+                                       T, T, T, T, T, T, P]
+    lib.bca_plan_sequences.argtypes = [P, i64p]
+    lib.bca_decode_varlen.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                      T, T, T, T, T, T, P]
     lib.bca_decode_split_workspace.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                i64p, i32p]
     lib.bca_decode_split.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -103,7 +107,8 @@ def load() -> ctypes.CDLL:
                  "bca_prefill", "bca_decode", "bca_prefill_ex", "bca_decode_ex",
                  "bca_rope_positions", "bca_rope_table", "bca_qk_prologue", "bca_plan_varlen",
                  "bca_prefill_varlen", "bca_decode_split_workspace", "bca_decode_split",
-                 "bca_cache_dequantize", "bca_decode_split_noalloc"):
+                 "bca_cache_dequantize", "bca_decode_split_noalloc", "bca_plan_sequences",
+                 "bca_decode_varlen"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -23,6 +23,7 @@ struct bca_plan_s {
   int32_t* d_kv_end = nullptr;
   int32_t* d_order = nullptr;
   int32_t* d_tiles = nullptr;
+  int32_t* d_seqs = nullptr;
 };
 
 namespace {
@@ -43,23 +44,26 @@ bca_status hip_fail(hipError_t e, const char* what) {
 void free_device(bca_plan_s* p) {
   if (p->d_arena) (void)hipFree(p->d_arena);
   p->d_arena = nullptr;
-  p->d_row_limit = p->d_kv_full = p->d_kv_end = p->d_order = p->d_tiles = nullptr;
+  p->d_row_limit = p->d_kv_full = p->d_kv_end = p->d_order = p->d_tiles = p->d_seqs = nullptr;
 }
 
 // The plan's device arrays: packed into one host staging buffer (each array starting on a
 // 256-byte boundary), then one hipMalloc and one synchronous hipMemcpy.
 bca_status upload(bca_plan_s* p) {
   const bca::HostPlan& h = p->host;
-  const std::vector<int32_t>* src[5] = {&h.row_limit, &h.kv_full, &h.kv_end, &h.order, &h.tiles};
-  int32_t** dst[5] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end, &p->d_order, &p->d_tiles};
+  constexpr int kArrays = 6;
+  const std::vector<int32_t>* src[kArrays] = {&h.row_limit, &h.kv_full, &h.kv_end,
+                                              &h.order,     &h.tiles,   &h.seqs};
+  int32_t** dst[kArrays] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end,
+                            &p->d_order,     &p->d_tiles,   &p->d_seqs};
   constexpr size_t kAlignInts = 64;
-  size_t off[5], total = 0;
-  for (int i = 0; i < 5; ++i) {
+  size_t off[kArrays], total = 0;
+  for (int i = 0; i < kArrays; ++i) {
     off[i] = total;
     total += (src[i]->size() + kAlignInts - 1) / kAlignInts * kAlignInts;
   }
   std::vector<int32_t> staging(total, 0);
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < kArrays; ++i)
     std::copy(src[i]->begin(), src[i]->end(), staging.begin() + (ptrdiff_t)off[i]);
   hipError_t e = hipMalloc(&p->d_arena, total * sizeof(int32_t));
   if (e != hipSuccess) {
@@ -69,7 +73,7 @@ bca_status upload(bca_plan_s* p) {
   }
   e = hipMemcpy(p->d_arena, staging.data(), total * sizeof(int32_t), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy of the plan arrays");
-  for (int i = 0; i < 5; ++i) *dst[i] = static_cast<int32_t*>(p->d_arena) + off[i];
+  for (int i = 0; i < kArrays; ++i) *dst[i] = static_cast<int32_t*>(p->d_arena) + off[i];
   return BCA_OK;
 }
 
@@ -389,7 +393,6 @@ bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, floa
       a.vc = cache->v.data;
       a.vc_sb = cache->v.stride_b; a.vc_ss = cache->v.stride_s; a.vc_sh = cache->v.stride_h;
     }
-    a.cache_len = (int32_t)hp.prefix_len;
   }
   hipError_t e = bca::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -433,10 +436,13 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
 
 bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
                               const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
-                              const bca_tensor* o, void* stream) {
+                              const bca_tensor* o, const bca_tensor* k_cache,
+                              const bca_tensor* v_cache, void* stream) {
   float scale_log2 = 0.0f;
   bca_status s = check_common(plan, 1, H, D, scale, &scale_log2);
   if (s != BCA_OK) return s;
+  if ((k_cache == nullptr) != (v_cache == nullptr))
+    return fail(BCA_ERR_ARG, "k_cache and v_cache must both be given or both be NULL");
   if ((s = check_tensor(q, "q", 2)) != BCA_OK) return s;
   if ((s = check_tensor(k, "k", 2)) != BCA_OK) return s;
   if ((s = check_tensor(v, "v", 2)) != BCA_OK) return s;
@@ -444,6 +450,13 @@ bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale
   const bca::HostPlan& hp = plan->host;
   if ((s = check_extent(k, "k", hp.rows)) != BCA_OK) return s;
   if ((s = check_extent(v, "v", hp.rows)) != BCA_OK) return s;
+  const bool store = k_cache != nullptr && hp.prefix_len > 0;  // no prefix rows: nothing to store
+  if (store) {
+    if ((s = check_tensor(k_cache, "k_cache", 2)) != BCA_OK) return s;
+    if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
+    if ((s = check_extent(k_cache, "k_cache", hp.prefix_len)) != BCA_OK) return s;
+    if ((s = check_extent(v_cache, "v_cache", hp.prefix_len)) != BCA_OK) return s;
+  }
   const int64_t nt = (int64_t)hp.kv_end.size();
   if (!grid_fits(nt, 1, H)) return fail(BCA_ERR_ARG, "H * query tiles is too large a grid");
   if ((s = check_launchable(plan)) != BCA_OK) return s;
@@ -474,8 +487,23 @@ bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale
   a.order = plan->d_order;
   a.tiles = plan->d_tiles;
   a.cache_fmt = BCA_CACHE_BF16;
+  if (store) {
+    a.kc = k_cache->data;
+    a.kc_ss = k_cache->stride_s; a.kc_sh = k_cache->stride_h;
+    a.vc = v_cache->data;
+    a.vc_ss = v_cache->stride_s; a.vc_sh = v_cache->stride_h;
+  }
   hipError_t e = bca::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return BCA_OK;
+}
+
+bca_status bca_plan_sequences(bca_plan_t plan, int64_t* out) {
+  if (plan == nullptr || out == nullptr) return fail(BCA_ERR_ARG, "plan or out is NULL");
+  const std::vector<int32_t>& sq = plan->host.seqs;
+  const size_t n = sq.size() / bca::kSeqInts;
+  for (size_t b = 0; b < n; ++b)
+    for (int c = 0; c < 6; ++c) out[6 * b + c] = sq[b * bca::kSeqInts + c];
   return BCA_OK;
 }
 
@@ -528,6 +556,8 @@ bca_status decode_impl(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   bca_status s = check_common(plan, B, H, D, scale, &scale_log2);
   if (s != BCA_OK) return s;
   const bca::HostPlan& hp = plan->host;
+  if (hp.n_sequences != 1)
+    return fail(BCA_ERR_ARG, "plan holds several sequences: launch it with bca_decode_varlen");
   if (!hp.decode_ok)
     return fail(BCA_ERR_NO_DECODE, "the layout's last block is text; cached decode needs the "
                                    "target image block last");
@@ -670,6 +700,69 @@ bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float sc
     return bca_decode_ex(plan, B, H, D, scale, q_tgt, nullptr, k_tgt, v_tgt, o, stream);
   const bca_kv_cache c = bf16_cache(k_cache, v_cache);
   return bca_decode_ex(plan, B, H, D, scale, q_tgt, &c, k_tgt, v_tgt, o, stream);
+}
+
+bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
+                             const bca_tensor* q_tgt, const bca_tensor* k_cache,
+                             const bca_tensor* v_cache, const bca_tensor* k_tgt,
+                             const bca_tensor* v_tgt, const bca_tensor* o, void* stream) {
+  float scale_log2 = 0.0f;
+  bca_status s = check_common(plan, 1, H, D, scale, &scale_log2);
+  if (s != BCA_OK) return s;
+  const bca::HostPlan& hp = plan->host;
+  if (!hp.decode_ok)
+    return fail(BCA_ERR_NO_DECODE, "a sequence's last block is text; cached decode needs every "
+                                   "sequence to end in its target image block");
+  if ((s = check_tensor(q_tgt, "q_tgt", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(k_tgt, "k_tgt", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(v_tgt, "v_tgt", 2)) != BCA_OK) return s;
+  if ((s = check_tensor(o, "o", 4)) != BCA_OK) return s;
+  const bool use_cache = hp.prefix_len > 0;
+  if (use_cache) {
+    if (k_cache == nullptr || v_cache == nullptr)
+      return fail(BCA_ERR_ARG, "the prefixes are not empty: k_cache and v_cache are required");
+    if ((s = check_tensor(k_cache, "k_cache", 2)) != BCA_OK) return s;
+    if ((s = check_tensor(v_cache, "v_cache", 2)) != BCA_OK) return s;
+    if ((s = check_extent(k_cache, "k_cache", hp.prefix_len)) != BCA_OK) return s;
+    if ((s = check_extent(v_cache, "v_cache", hp.prefix_len)) != BCA_OK) return s;
+  }
+  if ((s = check_extent(k_tgt, "k_tgt", hp.target_len)) != BCA_OK) return s;
+  if ((s = check_extent(v_tgt, "v_tgt", hp.target_len)) != BCA_OK) return s;
+  int32_t n_max = 0;
+  for (size_t b = 0; b < hp.seqs.size() / bca::kSeqInts; ++b)
+    n_max = std::max(n_max, hp.seqs[b * bca::kSeqInts + 3]);
+  const int64_t nt = (n_max + bca::kDecodeMinBlockM - 1) / bca::kDecodeMinBlockM;
+  if (!grid_fits(nt, hp.n_sequences, H)) return fail(BCA_ERR_ARG, "the decode grid is too large");
+  if ((s = check_launchable(plan)) != BCA_OK) return s;
+
+  bca::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q_tgt->data);
+  a.q_ss = q_tgt->stride_s; a.q_sh = q_tgt->stride_h;
+  a.k2 = static_cast<const uint16_t*>(k_tgt->data);
+  a.k2_ss = k_tgt->stride_s; a.k2_sh = k_tgt->stride_h;
+  a.v2 = static_cast<const uint16_t*>(v_tgt->data);
+  a.v2_ss = v_tgt->stride_s; a.v2_sh = v_tgt->stride_h;
+  a.cache_fmt = BCA_CACHE_BF16;
+  if (use_cache) {
+    a.k = k_cache->data;
+    a.k_ss = k_cache->stride_s; a.k_sh = k_cache->stride_h;
+    a.v = v_cache->data;
+    a.v_ss = v_cache->stride_s; a.v_sh = v_cache->stride_h;
+  } else {  // every key comes from the targets
+    a.k = a.k2; a.k_ss = a.k2_ss; a.k_sh = a.k2_sh;
+    a.v = a.v2; a.v_ss = a.v2_ss; a.v_sh = a.v2_sh;
+  }
+  a.o = static_cast<float*>(o->data);
+  a.o_ss = o->stride_s; a.o_sh = o->stride_h;
+  a.n_q = n_max;
+  a.heads = H;
+  a.batch = hp.n_sequences;
+  a.scale_log2 = scale_log2;
+  a.n_split = 1;
+  a.seqs = plan->d_seqs;
+  hipError_t e = bca::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return BCA_OK;
 }
 
 bca_status bca_qk_prologue(int32_t B, int64_t S, int32_t H, int32_t D, float eps,

@@ -220,8 +220,12 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // The tile's sequence (prefill plans may hold several): its first tensor row, the tile's first
   // local row, its length and where its row limits start.  Rows, keys and limits below are local
   // to the sequence; the decode has one sequence of n_q query rows over kv_len keys.
+  // Keys below kv_split come from the first source, the rest from the second; kv_len in all.
+  // cache_row0: first cache row of the sequence's prefix (stored by the prefill, read by a
+  // decode over a batch of sequences, whose targets start at tensor row seq_row0).
   int seq_row0 = 0, row0 = tile * kRows, n_rows = a.n_q, rl_off = 0;
-  int kv_end = a.kv_len, kv_full = a.kv_len;
+  int kv_len = a.kv_len, kv_split = a.split, kv_end = a.kv_len, kv_full = a.kv_len;
+  int cache_len = 0, cache_row0 = 0;
   if constexpr (!kDecode) {
     const int32_t* td = a.tiles + tile * kTileInts;
     seq_row0 = td[0];
@@ -230,6 +234,18 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     rl_off = td[3];
     kv_full = td[4];
     kv_end = td[5];
+    cache_len = td[6];
+    cache_row0 = td[7];
+  } else if (a.seqs != nullptr) {
+    const int32_t* sd = a.seqs + b * kSeqInts;
+    kv_split = sd[2];
+    n_rows = sd[3];
+    cache_row0 = sd[4];
+    seq_row0 = sd[5];
+    kv_len = kv_end = kv_full = kv_split + n_rows;
+    // the grid spans the longest target: this sequence may have no rows in this tile (the whole
+    // workgroup leaves before any barrier)
+    if (row0 >= n_rows) return;
   }
   const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
   // key tiles this workgroup visits: all of them, or its split's range
@@ -243,7 +259,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // Prefill: the largest key limit among this wave's real rows (wave-uniform: limits never
   // decrease along a sequence, so it is the last real row's).  A key tile starting at or past it
   // is invisible to the whole wave, whose part of that tile then adds exact zeros.
-  int wave_lim = a.kv_len;
+  int wave_lim = kv_len;
   if constexpr (!kDecode) {
     const int last = min(wave_row0 + 32 * kQueryBlocks - 1, n_rows - 1);
     wave_lim = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : a.row_limit[rl_off + last]);
@@ -262,7 +278,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   for (int qb = 0; qb < kQueryBlocks; ++qb) {
     const int row = row0 + (wave * kQueryBlocks + qb) * 32 + qn;
     row_ok[qb] = row >= 0 && row < n_rows;  // a prefill tile's first rows may be padding
-    lim[qb] = kDecode ? a.kv_len : a.row_limit[rl_off + (row_ok[qb] ? row : n_rows - 1)];
+    lim[qb] = kDecode ? kv_len : a.row_limit[rl_off + (row_ok[qb] ? row : n_rows - 1)];
     const uint16_t* qp = a.q + b * a.q_sb + (int64_t)(seq_row0 + (row_ok[qb] ? row : 0)) * a.q_ss +
                          h * a.q_sh + 8 * half;
 #pragma unroll
@@ -274,16 +290,22 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   }
 
   // first key source: bf16, or (decode over a quantised cache) code bytes plus row scales
+  // (prefill: the sequence's own rows; decode: its cache rows, then its target rows)
+  const int64_t src1_row = kDecode ? cache_row0 : seq_row0;
   const uint16_t* k_base =
-      static_cast<const uint16_t*>(a.k) + b * a.k_sb + h * a.k_sh + (int64_t)seq_row0 * a.k_ss;
+      static_cast<const uint16_t*>(a.k) + b * a.k_sb + h * a.k_sh + src1_row * a.k_ss;
   const uint16_t* v_base =
-      static_cast<const uint16_t*>(a.v) + b * a.v_sb + h * a.v_sh + (int64_t)seq_row0 * a.v_ss;
-  const uint8_t* k8_base = static_cast<const uint8_t*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const uint8_t* v8_base = static_cast<const uint8_t*>(a.v) + b * a.v_sb + h * a.v_sh;
-  const float* ks_base = kKqSrc ? a.kcs + b * a.kcs_sb + h * a.kcs_sh : nullptr;
-  const float* vs_base = kVqSrc ? a.vcs + b * a.vcs_sb + h * a.vcs_sh : nullptr;
-  const uint16_t* k2_base = a.k2 + b * a.k2_sb + h * a.k2_sh;
-  const uint16_t* v2_base = a.v2 + b * a.v2_sb + h * a.v2_sh;
+      static_cast<const uint16_t*>(a.v) + b * a.v_sb + h * a.v_sh + src1_row * a.v_ss;
+  const uint8_t* k8_base =
+      static_cast<const uint8_t*>(a.k) + b * a.k_sb + h * a.k_sh + src1_row * a.k_ss;
+  const uint8_t* v8_base =
+      static_cast<const uint8_t*>(a.v) + b * a.v_sb + h * a.v_sh + src1_row * a.v_ss;
+  const float* ks_base =
+      kKqSrc ? a.kcs + b * a.kcs_sb + h * a.kcs_sh + src1_row * a.kcs_ss : nullptr;
+  const float* vs_base =
+      kVqSrc ? a.vcs + b * a.vcs_sb + h * a.vcs_sh + src1_row * a.vcs_ss : nullptr;
+  const uint16_t* k2_base = a.k2 + b * a.k2_sb + h * a.k2_sh + (int64_t)seq_row0 * a.k2_ss;
+  const uint16_t* v2_base = a.v2 + b * a.v2_sb + h * a.v2_sh + (int64_t)seq_row0 * a.v2_ss;
 
   // ---- filling the ring: register staging ----------------------------------------------------
   // Thread t moves the 16-byte chunk at column 8 (t % 16) of tile rows t / 16 + kRowsPerPass r.
@@ -303,9 +325,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   auto stage_tile = [&](int n0, u32x4* st, const uint16_t* base1, int64_t ss1,
                         const uint16_t* base2, int64_t ss2) {
     const bool in_end = n0 + kBlockN <= kv_end;
-    const bool one_src1 = !kDecode || n0 + kBlockN <= a.split;
-    if (in_end && (one_src1 || n0 >= a.split)) {
-      const uint16_t* b = one_src1 ? base1 + (int64_t)n0 * ss1 : base2 + (int64_t)(n0 - a.split) * ss2;
+    const bool one_src1 = !kDecode || n0 + kBlockN <= kv_split;
+    if (in_end && (one_src1 || n0 >= kv_split)) {
+      const uint16_t* b = one_src1 ? base1 + (int64_t)n0 * ss1 : base2 + (int64_t)(n0 - kv_split) * ss2;
       const int64_t ss = one_src1 ? ss1 : ss2;
       const __amdgpu_buffer_rsrc_t rs = tile_rsrc(b, ss * 2);
       const int voff = ((int)ld_row * (int)ss + ld_col) * 2;
@@ -321,9 +343,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
         const int key = n0 + ld_row + kRowsPerPass * r;
         const bool valid = key < kv_end;
         const int kc = valid ? key : kv_end - 1;
-        const bool first = !kDecode || kc < a.split;
+        const bool first = !kDecode || kc < kv_split;
         const uint16_t* p =
-            (first ? base1 + (int64_t)kc * ss1 : base2 + (int64_t)(kc - a.split) * ss2) + ld_col;
+            (first ? base1 + (int64_t)kc * ss1 : base2 + (int64_t)(kc - kv_split) * ss2) + ld_col;
         const u32x4 x = *reinterpret_cast<const u32x4*>(p);
         st[r] = valid ? x : u32x4{0, 0, 0, 0};
       }
@@ -338,7 +360,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       return u32x4{c[0], c[1], __builtin_bit_cast(uint32_t, sc), 0u};
     };
     const bool in_end = n0 + kBlockN <= kv_end;
-    if (in_end && n0 + kBlockN <= a.split) {
+    if (in_end && n0 + kBlockN <= kv_split) {
       const __amdgpu_buffer_rsrc_t rc = tile_rsrc(base1 + (int64_t)n0 * ss1, ss1);
       const __amdgpu_buffer_rsrc_t rsc = tile_rsrc(sbase1 + (int64_t)n0 * sss1, sss1 * 4);
       const int voff = (int)ld_row * (int)ss1 + ld_col;
@@ -352,8 +374,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
             __builtin_amdgcn_raw_buffer_load_b32(rsc, soff, (int)(kRowsPerPass * r * sss1 * 4), 0);
         st[r] = u32x4{c[0], c[1], sc, 0u};
       }
-    } else if (in_end && n0 >= a.split) {
-      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base2 + (int64_t)(n0 - a.split) * ss2, ss2 * 2);
+    } else if (in_end && n0 >= kv_split) {
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base2 + (int64_t)(n0 - kv_split) * ss2, ss2 * 2);
       const int voff = ((int)ld_row * (int)ss2 + ld_col) * 2;
 #pragma unroll
       for (int r = 0; r < kChunksPerThread; ++r)
@@ -368,10 +390,10 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
         const bool valid = key < kv_end;
         const int kc = valid ? key : kv_end - 1;
         u32x4 x;
-        if (kc < a.split)
+        if (kc < kv_split)
           x = load1(kc);
         else
-          x = *reinterpret_cast<const u32x4*>(base2 + (int64_t)(kc - a.split) * ss2 + ld_col);
+          x = *reinterpret_cast<const u32x4*>(base2 + (int64_t)(kc - kv_split) * ss2 + ld_col);
         st[r] = valid ? x : u32x4{0, 0, 0, 0};
       }
     }
@@ -395,8 +417,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // Rows of a quantised source (keys below split) are dequantised on the way into LDS.
   auto stage_write = [&](auto quant_c, __bf16* lds, int stride, const u32x4* st, int n0) {
     constexpr bool kQ = decltype(quant_c)::value;
-    const bool all_q = kQ && n0 + kBlockN <= a.split;
-    const bool some_q = kQ && n0 < a.split;
+    const bool all_q = kQ && n0 + kBlockN <= kv_split;
+    const bool some_q = kQ && n0 < kv_split;
 #pragma unroll
     for (int r = 0; r < kChunksPerThread; ++r) {
       // (a row past the tile would land in the next buffer)
@@ -406,7 +428,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
         x = dequant(x);
       } else if (kQ && some_q) {
         const u32x4 d = dequant(x);
-        x = n0 + ld_row + kRowsPerPass * r < a.split ? d : x;
+        x = n0 + ld_row + kRowsPerPass * r < kv_split ? d : x;
       }
       *reinterpret_cast<u32x4*>(&lds[(ld_row + kRowsPerPass * r) * stride + st_col]) = x;
     }
@@ -479,8 +501,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       return;
     }
     const bool in_end = n0 + kBlockN <= kv_end;
-    const bool src1 = n0 + kBlockN <= a.split;
-    const bool src2 = n0 >= a.split;
+    const bool src1 = n0 + kBlockN <= kv_split;
+    const bool src2 = n0 >= kv_split;
     // decode: whole tiles from one source through buffer loads, the rest row by row below
     if (in_end && src1) {
       fill_whole(tile_rsrc(k_base + (int64_t)n0 * a.k_ss, a.k_ss * 2), a.k_ss, dma_k,
@@ -488,8 +510,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       return;
     }
     if (in_end && src2) {
-      fill_whole(tile_rsrc(k2_base + (int64_t)(n0 - a.split) * a.k2_ss, a.k2_ss * 2), a.k2_ss,
-                 dma_k2, tile_rsrc(v2_base + (int64_t)(n0 - a.split) * a.v2_ss, a.v2_ss * 2),
+      fill_whole(tile_rsrc(k2_base + (int64_t)(n0 - kv_split) * a.k2_ss, a.k2_ss * 2), a.k2_ss,
+                 dma_k2, tile_rsrc(v2_base + (int64_t)(n0 - kv_split) * a.v2_ss, a.v2_ss * 2),
                  a.v2_ss, dma_v2, buf);
       return;
     }
@@ -499,11 +521,11 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       const bool v = fill_is_v(i);
       // keys past the end fetch row kv_end - 1 (masked, finite)
       const int key = min(n0 + fill_row(i), kv_end - 1);
-      const bool first = key < a.split;
+      const bool first = key < kv_split;
       const uint16_t* p = v ? (first ? v_base + (int64_t)key * a.v_ss
-                                     : v2_base + (int64_t)(key - a.split) * a.v2_ss)
+                                     : v2_base + (int64_t)(key - kv_split) * a.v2_ss)
                             : (first ? k_base + (int64_t)key * a.k_ss
-                                     : k2_base + (int64_t)(key - a.split) * a.k2_ss);
+                                     : k2_base + (int64_t)(key - kv_split) * a.k2_ss);
       const int dst = 4 * fill_g(i) * kHeadDim;
       __builtin_amdgcn_global_load_lds((const void*)(p + fill_col),
                                        (lds_void*)&(v ? v_lds(buf) : k_lds(buf))[dst], 16, 0, 0);
@@ -516,7 +538,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // twice.  Either tensor may be absent (NULL): a quantised one is written by its own pass.
   const int cache_lo = row0;
   const int cache_hi =
-      kDecode || (a.kc == nullptr && a.vc == nullptr) ? 0 : min(cache_lo + kRows, a.cache_len);
+      kDecode || (a.kc == nullptr && a.vc == nullptr) ? 0 : min(cache_lo + kRows, cache_len);
   // Chunk tid + kThreads r of the tile: row (tid >> 4) + kRowsPerPass r, chunk tid % 16 (a
   // partial last pass stores nothing past the tile).
   auto store_row = [&](int n0, auto buf, int r) {
@@ -524,7 +546,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const int key = n0 + row;
     if (row >= kBlockN || key < cache_lo || key >= cache_hi) return;
     const int col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(row)) : ld_col;
-    const int64_t at = (int64_t)key;
+    const int64_t at = (int64_t)cache_row0 + key;
     if (a.kc != nullptr)
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kc) + b * a.kc_sb + at * a.kc_ss +
                                 h * a.kc_sh + ld_col) =

@@ -64,14 +64,14 @@ struct AttnArgs {
   int64_t v2_sb, v2_ss, v2_sh;
   float* o;
   int64_t o_sb, o_ss, o_sh;
-  // Prefill only: bf16 prefix-cache tensors [B, cache_len, H, D] receiving K/V rows
-  // [0, cache_len), or NULL (no cache, or a quantised tensor, which launch_quantize writes).
-  // The workgroup of a query tile writes the tile's own rows of them.
+  // Prefill only: bf16 prefix-cache tensors receiving each sequence's K/V rows [0, P) at cache
+  // rows [cache_row, cache_row + P) (both from the tile descriptors), or NULL (no cache, or a
+  // quantised tensor, which launch_quantize writes).  The workgroup of a query tile writes the
+  // tile's own rows of them.
   void* kc;
   int64_t kc_sb, kc_ss, kc_sh;
   void* vc;
   int64_t vc_sb, vc_ss, vc_sh;
-  int32_t cache_len;
   int32_t n_q;       // query rows per (batch, head): S for prefill, N for decode
   int32_t kv_len;    // keys per (batch, head): S for prefill, P + N for decode
   int32_t split;     // first key taken from the second source
@@ -86,9 +86,14 @@ struct AttnArgs {
   const int32_t* order;
   // Prefill only: per query tile {sequence's first tensor row, first local row (negative for a
   // partial first tile, whose rows below 0 are padding), sequence length,
-  // offset of the sequence's row limits, kv_full, kv_end, 0, 0}; row_limit and the key bounds
-  // are local to the sequence.
+  // offset of the sequence's row limits, kv_full, kv_end, prefix length P, first cache row};
+  // row_limit and the key bounds are local to the sequence.
   const int32_t* tiles;
+  // Decode over a batch of sequences (NULL otherwise): per batch entry b, kSeqInts ints of which
+  // [2] = P_b, [3] = N_b, [4] = first cache row, [5] = first target row.  Entry b then takes its
+  // n_q = N_b queries at rows [5] + n of q / o, its keys from cache rows [4] + j (j < P_b) and
+  // target rows [5] + j - P_b; batch strides are unused and n_q is the largest N_b.
+  const int32_t* seqs;
   // Decode only: scales [B, cache_len, H] of the quantised cache tensors (NULL for a bf16 one).
   float* kcs;
   int64_t kcs_sb, kcs_ss, kcs_sh;

@@ -92,6 +92,8 @@ int build_host_plan(const int32_t* ids, int64_t S, int block_m, HostPlan* out, s
   p.decode_ok = p.segments[3 * (nseg - 1) + 2] >= 0 ? 1 : 0;
   p.block_m = block_m;
   p.rows = S;
+  for (int64_t t = 0; t < nt; ++t) p.tiles[(size_t)t * kTileInts + 6] = (int32_t)p.prefix_len;
+  p.seqs = {0, (int32_t)S, (int32_t)p.prefix_len, (int32_t)p.target_len, 0, 0, p.decode_ok, 0};
   *out = std::move(p);
   return kPlanOk;
 }
@@ -140,6 +142,7 @@ int build_varlen_plan(const int32_t* ids, const int64_t* lengths, const int64_t*
   HostPlan p;
   p.block_m = block_m;
   p.n_sequences = batch;
+  p.decode_ok = 1;
   int64_t off = 0;
   for (int32_t b = 0; b < batch; ++b) {
     HostPlan one;
@@ -150,15 +153,24 @@ int build_varlen_plan(const int32_t* ids, const int64_t* lengths, const int64_t*
     }
     for (size_t r = 0; r < one.segments.size(); ++r) p.segments.push_back(one.segments[r]);
     p.row_limit.insert(p.row_limit.end(), one.row_limit.begin(), one.row_limit.end());
+    // this sequence's cache rows and target rows follow those of the sequences before it
+    const int32_t cache_row = (int32_t)p.prefix_len, target_row = (int32_t)p.target_len;
     const size_t nt = one.kv_end.size();
     for (size_t t = 0; t < nt; ++t) {
       p.kv_full.push_back(one.kv_full[t]);
       p.kv_end.push_back(one.kv_end[t]);
       const int32_t d[kTileInts] = {(int32_t)start[(size_t)b], one.tiles[t * kTileInts + 1],
                                     (int32_t)lengths[b], (int32_t)off, one.kv_full[t],
-                                    one.kv_end[t], 0, 0};
+                                    one.kv_end[t], (int32_t)one.prefix_len, cache_row};
       p.tiles.insert(p.tiles.end(), d, d + kTileInts);
     }
+    const int32_t sd[kSeqInts] = {(int32_t)start[(size_t)b], (int32_t)lengths[b],
+                                  (int32_t)one.prefix_len, (int32_t)one.target_len, cache_row,
+                                  target_row, one.decode_ok, 0};
+    p.seqs.insert(p.seqs.end(), sd, sd + kSeqInts);
+    p.prefix_len += one.prefix_len;
+    p.target_len += one.target_len;
+    p.decode_ok &= one.decode_ok;
     p.useful_pairs += one.useful_pairs;
     p.seq_len += lengths[b];
     p.rows = std::max<int64_t>(p.rows, start[(size_t)b] + lengths[b]);
@@ -169,9 +181,6 @@ int build_varlen_plan(const int32_t* ids, const int64_t* lengths, const int64_t*
   std::iota(p.order.begin(), p.order.end(), 0);
   std::stable_sort(p.order.begin(), p.order.end(),
                    [&](int32_t x, int32_t y) { return p.kv_end[(size_t)x] > p.kv_end[(size_t)y]; });
-  p.prefix_len = 0;
-  p.target_len = 0;
-  p.decode_ok = 0;
   *out = std::move(p);
   return kPlanOk;
 }

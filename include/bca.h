@@ -60,14 +60,15 @@ typedef struct bca_tensor {
 
 typedef struct bca_plan_info {
   int64_t seq_len;      /* S */
-  int64_t prefix_len;   /* P: start of the last block (text + reference positions before it) */
-  int64_t target_len;   /* N = S - P */
+  int64_t prefix_len;   /* P: start of the last block (text + reference positions before it);
+                           a bca_plan_varlen plan: the sum of its sequences' P_b */
+  int64_t target_len;   /* N = S - P; a bca_plan_varlen plan: the sum of its sequences' N_b */
   int64_t useful_pairs; /* number of visible (query, key) pairs per (batch, head) = sum of hi(i) */
   int32_t n_segments;   /* maximal runs of equal block id */
   int32_t block_m;      /* query rows per prefill tile */
   int32_t block_n;      /* keys per key tile */
   int32_t n_qtiles;     /* ceil(S / block_m) */
-  int32_t decode_ok;    /* 1 when the last block is an image block (the target) */
+  int32_t decode_ok;    /* 1 when the last block (of every sequence) is an image block */
   int32_t host_only;    /* 1 when built with BCA_PLAN_HOST_ONLY (no device arrays) */
   int32_t n_sequences;  /* 1, or the batch of a bca_plan_varlen plan */
   int32_t reserved;     /* 0 */
@@ -114,13 +115,28 @@ bca_status bca_plan(const int32_t* block_ids, int64_t seq_len, uint32_t flags, b
  * a sequence).  lengths: HOST int64 [batch], each >= 1.  row_start: HOST int64 [batch], the row of
  * the [rows, H, D] tensors where sequence b starts, or NULL for packed (row_start[b] =
  * sum_{c<b} lengths[c]).  Rows of different sequences must not overlap; gaps (padding) are
- * allowed and never read or written.  Such a plan has n_sequences = batch, prefix_len = 0 and
- * decode_ok = 0; it is launched with bca_prefill_varlen.  Exported arrays are concatenated over
- * the sequences (segments and row_limit local to each sequence).
+ * allowed and never read or written.  Exported arrays are concatenated over the sequences
+ * (segments and row_limit local to each sequence).
+ *
+ * Each sequence b has its own prefix P_b (start of its last block) and target N_b = len_b - P_b,
+ * as bca_plan defines them: the guide's section "The prefix cache is a compute-for-memory trade"
+ * keeps one prefix cache per CFG branch, and the cond and uncond prompts differ in length.  The
+ * batch's prefix caches are packed: sequence b's prefix K/V sit at cache rows [c_b, c_b + P_b)
+ * with c_b = sum_{c<b} P_c, and its decode tensors (target Q/K/V and output) at target rows
+ * [t_b, t_b + N_b) with t_b = sum_{c<b} N_c (bca_plan_sequences lists them).  Such a plan has
+ * n_sequences = batch, prefix_len = sum P_b, target_len = sum N_b and decode_ok = 1 when every
+ * sequence ends in an image block; it is launched with bca_prefill_varlen and bca_decode_varlen.
  */
 bca_status bca_plan_varlen(const int32_t* block_ids, const int64_t* lengths,
                            const int64_t* row_start, int32_t batch, uint32_t flags,
                            bca_plan_t* out);
+
+/*
+ * Per sequence of a plan (one row for a bca_plan plan), six int64 written to out[6 b .. 6 b + 5]:
+ * tensor row of its first position, length, prefix length P_b, target length N_b, first cache
+ * row c_b, first target row t_b.  out must hold 6 * n_sequences values.
+ */
+bca_status bca_plan_sequences(bca_plan_t plan, int64_t* out);
 
 /* Releases a plan (host and device arrays).  NULL is accepted and ignored. */
 bca_status bca_plan_free(bca_plan_t plan);
@@ -160,12 +176,15 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
  * bca_prefill_varlen -- block-causal attention of every sequence of a bca_plan_varlen plan (or of
  * the single sequence of a bca_plan plan): q, k, v bf16 and o fp32 are [rows, H, D] tensors
  * (bca_tensor with stride_b unused), sequence b at rows [row_start[b], row_start[b] + len_b).
- * Output rows of a sequence are fully written; rows outside every sequence are not touched.  No
- * prefix cache is stored.  D must be 128.
+ * Output rows of a sequence are fully written; rows outside every sequence are not touched.
+ * k_cache, v_cache: bf16 [sum P_b, H, D] (stride_b unused), or both NULL.  When given, cache rows
+ * [c_b, c_b + P_b) receive copies of sequence b's k and v rows [0, P_b) (its per-branch prefix
+ * cache, packed as bca_plan_varlen describes).  D must be 128.
  */
 bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
                               const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
-                              const bca_tensor* o, void* stream);
+                              const bca_tensor* o, const bca_tensor* k_cache,
+                              const bca_tensor* v_cache, void* stream);
 
 /*
  * bca_decode -- a cached denoising step: the N target queries attend with no mask to the
@@ -179,12 +198,33 @@ bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale
  *
  * q_tgt, k_tgt, v_tgt: bf16 [B, N, H, D]; k_cache, v_cache: bf16 [B, P, H, D] (P, N from the
  * plan); o: fp32 [B, N, H, D].  The plan's last block must be an image block
- * (else BCA_ERR_NO_DECODE).  D must be 128.
+ * (else BCA_ERR_NO_DECODE); a plan of several sequences is BCA_ERR_ARG here (bca_decode_varlen
+ * takes it).  D must be 128.
  */
 bca_status bca_decode(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
                       const bca_tensor* q_tgt, const bca_tensor* k_cache,
                       const bca_tensor* v_cache, const bca_tensor* k_tgt,
                       const bca_tensor* v_tgt, const bca_tensor* o, void* stream);
+
+/*
+ * bca_decode_varlen -- the cached step of every sequence of a bca_plan_varlen plan in one launch
+ * (the guide's section "The prefix cache is a compute-for-memory trade": the cond and uncond CFG
+ * branches each keep their own prefix cache, of their own length).  Sequence b's N_b target
+ * queries attend with no mask to [its cache rows ; its target keys]:
+ *
+ *   o[t_b + n, h, :] = sum_{j < P_b + N_b} softmax_j(scale * q_tgt[t_b + n, h, :] . kk_b[j, h, :])
+ *                      vv_b[j, h, :],
+ *   kk_b[j] = k_cache[c_b + j] for j < P_b, k_tgt[t_b + j - P_b] otherwise (same for vv_b).
+ *
+ * q_tgt, k_tgt, v_tgt: bf16 [sum N_b, H, D]; k_cache, v_cache: bf16 [sum P_b, H, D] (as
+ * bca_prefill_varlen stores them; may be NULL when every P_b is 0); o: fp32 [sum N_b, H, D],
+ * fully written.  stride_b is unused.  Every sequence must end in an image block (else
+ * BCA_ERR_NO_DECODE); a bca_plan plan is accepted (one sequence).  D must be 128.
+ */
+bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
+                             const bca_tensor* q_tgt, const bca_tensor* k_cache,
+                             const bca_tensor* v_cache, const bca_tensor* k_tgt,
+                             const bca_tensor* v_tgt, const bca_tensor* o, void* stream);
 
 /*
  * FP8 prefix cache (10100.com article, FP8 part: the prefix K/V cache may be stored as FP8 E4M3

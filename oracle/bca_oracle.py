@@ -24,8 +24,10 @@ construction, the pages' worked 3x8 example, closed forms (Q = 0), reductions to
 prefix invariance, decode == prefill rows, and the pages' cache-size figures.  The FP8 cache
 functions (tests/test_oracle_fp8_pins.py) are pinned to the E4M3 definition (closed-form codes,
 brute-force nearest value over all 256 codes, tie midpoints), the half-ulp error bound, exact
-round trips and the pages' "V-only saves about a quarter".  No function here is "parity
-unpinned".
+round trips and the pages' "V-only saves about a quarter".  The batch-of-sequences functions
+(tests/test_oracle_varlen_pins.py) are pinned to a dense construction of the rule over the whole
+row axis, and the batched cached step to the prefill rows of each sequence.  No function here is
+"parity unpinned".
 """
 from __future__ import annotations
 
@@ -518,3 +520,48 @@ def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, ids_list: Sequ
 def packed_row_starts(lengths: Sequence[int]) -> np.ndarray:
     """Row of each sequence when the batch is packed without gaps."""
     return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))[:-1]])
+
+
+# ----------------------------------------------------------------------------------------------
+# [QI21-guide], "The prefix cache is a compute-for-memory trade": one prefix cache per CFG branch
+# (the cond and uncond prompts differ, so their prefixes differ in length).  For a batch of
+# sequences, sequence b's prefix is everything before its last block (prefix_split), and the
+# batch's caches are laid end to end along one row axis: sequence b's P_b rows start at
+# c_b = P_0 + ... + P_{b-1}.  Its cached step takes its N_b target rows, which start at
+# t_b = N_0 + ... + N_{b-1} along the row axis of the target tensors.
+def varlen_offsets(ids_list: Sequence[Sequence[int]]) -> Dict[str, np.ndarray]:
+    """Per sequence: P (prefix), N (target), c (first cache row), t (first target row)."""
+    P = np.array([prefix_split(ids)[0] for ids in ids_list], dtype=np.int64)
+    N = np.array([len(ids) for ids in ids_list], dtype=np.int64) - P
+    return {"P": P, "N": N, "c": packed_row_starts(P), "t": packed_row_starts(N)}
+
+
+def prefix_cache_varlen(k: np.ndarray, v: np.ndarray, ids_list: Sequence[Sequence[int]],
+                        row_start: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Copies of every sequence's prefix K/V rows, laid end to end: [sum P_b, H, D] each."""
+    off = varlen_offsets(ids_list)
+    kc = [k[int(row_start[b]):int(row_start[b]) + int(off["P"][b])] for b in range(len(ids_list))]
+    vc = [v[int(row_start[b]):int(row_start[b]) + int(off["P"][b])] for b in range(len(ids_list))]
+    return np.concatenate(kc).copy(), np.concatenate(vc).copy()
+
+
+def decode_varlen(q_t: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, k_t: np.ndarray,
+                  v_t: np.ndarray, ids_list: Sequence[Sequence[int]],
+                  scale: Optional[float] = None, rows_of: Optional[Dict[int, np.ndarray]] = None,
+                  heads: Optional[Sequence[int]] = None) -> Dict[int, np.ndarray]:
+    """Cached step of every sequence of a batch: sequence b's target queries attend with no mask
+    to [its cache rows ; its target keys] (decode, per sequence).  q_t, k_t, v_t are
+    [sum N_b, H, D], the caches [sum P_b, H, D].  Returns {b: float64 [N_b or len(rows_of[b]),
+    H', D]}."""
+    off = varlen_offsets(ids_list)
+    if k_cache.shape[0] != off["P"].sum() or q_t.shape[0] != off["N"].sum():
+        raise OracleInputError("cache or target rows do not match the batch's P_b and N_b")
+    out = {}
+    for b in range(len(ids_list)):
+        c, P = int(off["c"][b]), int(off["P"][b])
+        t, N = int(off["t"][b]), int(off["N"][b])
+        rows = None if rows_of is None else rows_of.get(b)
+        out[b] = decode(q_t[None, t:t + N], k_cache[None, c:c + P], v_cache[None, c:c + P],
+                        k_t[None, t:t + N], v_t[None, t:t + N], scale=scale, rows=rows,
+                        heads=heads)[0]
+    return out

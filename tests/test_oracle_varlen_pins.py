@@ -7,7 +7,9 @@
 * A batch of one is the single-sequence oracle.
 * Sequences are independent: rewriting every row outside sequence b leaves b unchanged, bit for
   bit.
-A planted mistake (the packed batch treated as one sequence) is caught.
+* Per-branch prefix caches laid end to end and the batched cached step: each branch's target
+  rows equal its rows of the dense construction; one branch is the plain cached step.
+Planted mistakes (the packed batch treated as one sequence; a cache read one row off) are caught.
 """
 import numpy as np
 import pytest
@@ -95,3 +97,61 @@ def test_planted_mistake_one_long_sequence_is_caught():
         for b in want:
             np.testing.assert_allclose(wrong[starts[b]:starts[b] + len(ids_list[b])], want[b],
                                        rtol=0, atol=1e-9)
+
+
+def cfg_branches(seed, prompts, target):
+    """Two or more CFG-like branches: [text p][image 6][text 2][image target] with prompts of
+    different lengths, every branch ending in its target image block."""
+    ids_list = [W.block_ids_from_segments((("text", p), ("image", 6), ("text", 2),
+                                           ("image", target))) for p in prompts]
+    lens = [len(i) for i in ids_list]
+    starts = np.cumsum([0] + [n + 2 for n in lens])[:-1]       # a gap of 2 rows between branches
+    R = int(starts[-1] + lens[-1] + 1)
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((R, 2, 128)) for _ in range(3))
+    return q, k, v, ids_list, starts
+
+
+def test_per_branch_caches_and_cached_step_reproduce_the_prefill_rows():
+    """Per-branch caches laid end to end, then the batched cached step: each branch's target rows
+    must equal its prefill rows under the rule built densely over all rows (a target row of the
+    last image block sees every earlier row of its branch and its whole block)."""
+    q, k, v, ids_list, starts = cfg_branches(5, [7, 13, 4], 9)
+    kc, vc = O.prefix_cache_varlen(k, v, ids_list, starts)
+    # the cache rows, position by position
+    r = 0
+    for b, ids in enumerate(ids_list):
+        P = int(np.flatnonzero(np.asarray(ids) != ids[-1]).max()) + 1   # before the last block
+        for j in range(P):
+            assert np.array_equal(kc[r], k[starts[b] + j]) and np.array_equal(vc[r], v[starts[b] + j])
+            r += 1
+    assert r == kc.shape[0]
+    # the targets, packed
+    tgt = [np.arange(starts[b] + len(ids) - 9, starts[b] + len(ids)) for b, ids in enumerate(ids_list)]
+    sel = np.concatenate(tgt)
+    got = O.decode_varlen(q[sel], kc, vc, k[sel], v[sel], ids_list)
+    want = dense_rule_over_rows(q, k, v, ids_list, starts)
+    for b, ids in enumerate(ids_list):
+        np.testing.assert_allclose(got[b], want[b][len(ids) - 9:], rtol=0, atol=1e-12)
+
+
+def test_batched_cached_step_of_one_branch_is_the_plain_cached_step():
+    q, k, v, ids_list, starts = cfg_branches(6, [11], 8)
+    P = len(ids_list[0]) - 8
+    got = O.decode_varlen(q[P:P + 8], k[:P], v[:P], k[P:P + 8], v[P:P + 8], ids_list)[0]
+    want = O.decode(q[None, P:P + 8], k[None, :P], v[None, :P], k[None, P:P + 8], v[None, P:P + 8])[0]
+    assert np.array_equal(got, want)
+
+
+def test_planted_mistake_cache_rows_off_by_one_is_caught():
+    q, k, v, ids_list, starts = cfg_branches(7, [5, 9], 7)
+    kc, vc = O.prefix_cache_varlen(k, v, ids_list, starts)
+    sel = np.concatenate([np.arange(starts[b] + len(i) - 7, starts[b] + len(i))
+                          for b, i in enumerate(ids_list)])
+    want = dense_rule_over_rows(q, k, v, ids_list, starts)
+    # wrong: every cache row read one row off (c_b off by one)
+    wrong = O.decode_varlen(q[sel], np.roll(kc, 1, axis=0), np.roll(vc, 1, axis=0), k[sel], v[sel],
+                            ids_list)
+    with pytest.raises(AssertionError):
+        for b, ids in enumerate(ids_list):
+            np.testing.assert_allclose(wrong[b], want[b][len(ids) - 7:], rtol=0, atol=1e-9)

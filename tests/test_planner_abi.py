@@ -280,7 +280,18 @@ def test_varlen_plan_bit_exact(seed):
     assert np.array_equal(got["segments"].astype(np.int64), segs)
     kv_end = np.concatenate([w["kv_end"] for w in want])
     assert np.array_equal(got["order"], np.argsort(-kv_end, kind="stable"))
-    assert info.n_sequences == len(ids_list) and info.decode_ok == 0 and info.prefix_len == 0
+    assert info.n_sequences == len(ids_list)
+    # per sequence: prefix and target as the oracle splits them, packed cache and target rows
+    split = [O.prefix_split(ids) for ids in ids_list]
+    P = np.array([x[0] for x in split]); N = np.array([x[1] for x in split])
+    assert info.prefix_len == P.sum() and info.target_len == N.sum()
+    assert info.decode_ok == int(all(x[2] for x in split))
+    sq = p.sequences()
+    lens = [len(i) for i in ids_list]
+    assert np.array_equal(sq[:, 0], O.packed_row_starts(lens)) and np.array_equal(sq[:, 1], lens)
+    assert np.array_equal(sq[:, 2], P) and np.array_equal(sq[:, 3], N)
+    assert np.array_equal(sq[:, 4], np.concatenate([[0], np.cumsum(P)[:-1]]))
+    assert np.array_equal(sq[:, 5], np.concatenate([[0], np.cumsum(N)[:-1]]))
     assert info.seq_len == sum(len(i) for i in ids_list) == info.rows
     assert info.useful_pairs == sum(int(w["useful_pairs"]) for w in want)
     assert info.n_qtiles == sum(-(-len(i) // info.block_m) for i in ids_list)
@@ -313,9 +324,27 @@ def test_varlen_plan_errors():
     assert b"bca_prefill_varlen" in lib.bca_last_error()
     r = ctypes.byref
     assert lib.bca_prefill_varlen(ok.handle, 2, 64, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
-                                  None) == _lib.BCA_ERR_UNSUPPORTED
+                                  None, None, None) == _lib.BCA_ERR_UNSUPPORTED
     assert lib.bca_prefill_varlen(ok.handle, 2, 128, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
-                                  None) == _lib.BCA_ERR_ARG             # host-only plan
+                                  None, None, None) == _lib.BCA_ERR_ARG  # host-only plan
+    assert b"HOST_ONLY" in lib.bca_last_error()
+    assert lib.bca_prefill_varlen(ok.handle, 2, 128, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
+                                  r(_t()), None, None) == _lib.BCA_ERR_ARG  # one cache tensor
+    assert b"both" in lib.bca_last_error()
+    # decode over the batch: sequence 1 ends in text
+    assert ok.info.decode_ok == 0
+    assert lib.bca_decode_varlen(ok.handle, 2, 128, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
+                                 r(_t()), r(_t()), None) == _lib.BCA_ERR_NO_DECODE
+    img = bca.Plan.varlen([a, np.array([-1, 0], np.int32)], host_only=True)
+    assert img.info.decode_ok == 1 and img.info.prefix_len == 2 and img.info.target_len == 3
+    assert call_decode(img.handle) == _lib.BCA_ERR_ARG                # several sequences
+    assert b"bca_decode_varlen" in lib.bca_last_error()
+    assert lib.bca_decode_varlen(img.handle, 2, 64, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
+                                 r(_t()), r(_t()), None) == _lib.BCA_ERR_UNSUPPORTED
+    assert lib.bca_decode_varlen(img.handle, 2, 128, 0.0, r(_t()), None, None, r(_t()),
+                                 r(_t()), r(_t()), None) == _lib.BCA_ERR_ARG  # prefix needs caches
+    assert lib.bca_decode_varlen(img.handle, 2, 128, 0.0, r(_t()), r(_t()), r(_t()), r(_t()),
+                                 r(_t()), r(_t()), None) == _lib.BCA_ERR_ARG  # host-only plan
     assert b"HOST_ONLY" in lib.bca_last_error()
 
 
