@@ -11,11 +11,9 @@
 // the tail.
 //
 // Work decomposition.  One workgroup = kW waves = one tile of 32 kW query rows of one (batch,
-// head); a wave owns kQueryBlocks blocks of 32 rows.  The prefill and the bf16-cache decode run
-// 12 waves (384 rows, one workgroup per CU at 3 waves per SIMD, so each K/V tile in LDS serves
-// 384 rows; a small decode grid runs 4), the FP8-cache decode 8 (4 on a small grid).  Per key tile of kBlockN keys
-// (32 in the prefill and the bf16-cache decode; 64 in the FP8-cache decode, at 2 waves per
-// SIMD):
+// head); a wave owns kQueryBlocks blocks of 32 rows.  The prefill and the decode run 12 waves
+// (384 rows, one workgroup per CU at 3 waves per SIMD, so each K/V tile in LDS serves 384 rows;
+// a small decode grid runs 4).  Per key tile of kBlockN = 32 keys:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q rows held in VGPRs.
 //                 The accumulator gives each lane ONE query (lane % 32) and 16 keys, so the row
 //                 max is an in-lane reduction plus one swap of the two 32-lane halves.
@@ -30,15 +28,12 @@
 //                 lane four consecutive keys of one column.  The key order inside one MFMA step
 //                 is permuted identically in A and B, which leaves the sum unchanged.
 // K/V tiles go through a two-buffer LDS ring with one barrier per tile: tile j+1 is in flight
-// while tile j is computed.  Two ways to fill the ring (template parameter kDirect):
-//   register staging (FP8-cache decode): 16-byte global loads into VGPRs, dequantised and
-//                 written to LDS one tile later;
-//   direct (prefill, bf16-cache decode): buffer_load_dwordx4 ... lds writes 1 KB (4 rows)
-//                 straight into LDS per instruction, the tile's fills dealt round-robin over the
-//                 waves, with a fixed per-lane offset and the tile's position in the descriptor.
-// Direct fills write unpadded rows, with an XOR swizzle of their 16-byte chunks (below) that
-// keeps the K reads and the transposed V reads free of bank conflicts; staged fills write padded
-// rows.
+// while tile j is computed.  The ring is filled by direct loads: buffer_load_dwordx4 ... lds
+// writes 1 KB (4 rows) straight into LDS per instruction, the tile's fills dealt round-robin over
+// the waves, with a fixed per-lane offset and the tile's position in the descriptor.  Rows are
+// unpadded, with an XOR swizzle of their 16-byte chunks (below) that keeps the K reads and the
+// transposed V reads free of bank conflicts.  An FP8 prefix cache's code bytes and row scales
+// come in the same way, two tiles ahead, and are turned into the bf16 tile in LDS.
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -60,8 +55,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // While a wave issues its score or PV MFMAs it runs at raised priority, so the SIMD's arbiter
 // prefers waves that can feed the matrix core and the others fill the gaps with softmax work.
-// Measured per kernel (interleaved A/B): +2% for the prefill and the FP8-cache decode; the
-// bf16-cache decode with 12-wave workgroups runs 4% faster without it.
+// Measured per kernel (interleaved A/B): +2% for the prefill; the decode with 12-wave workgroups
+// runs 4% faster without it.
 constexpr int kMfmaPrio = 1;
 constexpr int kDecodeDirectMfmaPrio = 0;
 // Reads kept in flight ahead of the MFMAs (in steps of one MFMA) in the score and PV phases.
@@ -70,10 +65,6 @@ constexpr int kDecodeDirectMfmaPrio = 0;
 // the prefill.
 constexpr int kSchedKDepth = 3;
 constexpr int kSchedVDepth = 4;
-// Padding of the register-staged decode's V rows: 288 B.  (320 B rows make its transposed reads
-// bank-conflict-free on 64 banks but measured no faster: the decode is not bound by LDS
-// conflicts.)
-constexpr int kStagedVPad = 16;
 
 // A row's running max is raised only when its scores grew by more than kRescaleThreshold (log2
 // units), so p <= 2^16: exact in fp32, within bf16's exponent range, and l, O stay far below
@@ -124,8 +115,8 @@ __device__ inline float halves_sum(float x) {
 }
 
 // FP8 prefix cache (E4M3, one fp32 scale per (token, head) row; the exact rule is in bca.h).
-// A staged row of a quantised tensor travels as {8 code bytes, scale bits, 0}; dequant turns it
-// into the 8 bf16 values E4M3(code) * scale that the LDS tile holds.
+// dequant turns {8 code bytes of a row, its scale bits, 0} into the 8 bf16 values
+// E4M3(code) * scale that the LDS tile holds.
 __device__ inline u32x4 dequant(u32x4 x) {
   // (the element goes through a scalar first: hipcc lowers a bit_cast of an ext_vector element
   // operand to a cast of element 0)
@@ -141,54 +132,55 @@ __device__ inline u32x4 dequant(u32x4 x) {
   return __builtin_bit_cast(u32x4, r);
 }
 
-// The body of all the kernels.  kBlockN keys per key tile (32 or 64) and kW waves per workgroup
-// are chosen per kernel, and so is the occupancy (set on the kernels below).
-template <bool kDecode, bool kDirect, int kFmt, int kBlockN, int kW>
+// The body of all the kernels.  kBlockN keys per key tile and kW waves per workgroup are chosen
+// per kernel, and so is the occupancy (set on the kernels below).
+template <bool kDecode, int kFmt, int kBlockN, int kW>
 __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   constexpr int kThreads = 64 * kW;
   constexpr int kRows = 32 * kQueryBlocks * kW;  // query rows per workgroup
-  constexpr int kRowsPerPass = kThreads / 16;    // staging: rows per pass
+  constexpr int kRowsPerPass = kThreads / 16;    // cache copy: rows per pass
   constexpr int kKeyBlocks = kBlockN / 32;       // 32-key MFMA blocks
-  // staging: 16-byte chunks per thread (the last pass may be partial where the direct-fill
-  // kernels copy cache rows out of LDS this way)
+  // cache copy: 16-byte chunks per thread (the last pass may be partial)
   constexpr int kChunksPerThread = (kBlockN * kHeadDim / 8 + kThreads - 1) / kThreads;
   static_assert(kBlockN == 32 || kBlockN == 64, "one or two 32-key MFMA blocks per key tile");
-  // staging passes past the tile's rows (a partial last pass) load and store nothing
+  // cache-copy passes past the tile's rows (a partial last pass) store nothing
   constexpr bool kPartialPass = kBlockN * kHeadDim / 8 % kThreads != 0;
   // The decode may read a quantised cache (its first key source); the prefill stores bf16 only.
   static_assert(kDecode || kFmt == kCacheBf16, "the prefill stores the cache's bf16 tensors");
   // wave priority while issuing MFMAs (0: never raised)
-  constexpr int kPrioLevel =
-      kDecode && kDirect && kW == kDecodeDirectWaves ? kDecodeDirectMfmaPrio : kMfmaPrio;
+  constexpr int kPrioLevel = kDecode && kW == kDecodeDirectWaves ? kDecodeDirectMfmaPrio : kMfmaPrio;
   constexpr bool kPrio = kPrioLevel > 0;
   constexpr bool kKqSrc = kDecode && kFmt == kCacheFp8KV;
   constexpr bool kVqSrc = kDecode && kFmt != kCacheBf16;
-  static_assert(!(kDirect && (kKqSrc || kVqSrc)), "direct loads move bf16 rows only");
-  // LDS rows: unpadded (256 B) with their 16-byte chunks swizzled, or padded (272 B / 288 B).
-  constexpr bool kSwizzle = kDirect;
-  constexpr int kKStride = kSwizzle ? kHeadDim : kHeadDim + 8;
-  constexpr int kVStride = kSwizzle ? kHeadDim : kHeadDim + kStagedVPad;
-  // The two ring buffers.  The direct-fill kernels (swizzled tiles, read by buffer constants:
-  // their tile loop is unrolled by two below) keep them in separate arrays: reads of one are then
-  // provably independent of the direct loads in flight into the other, so the compiler adds no
-  // vmcnt wait before them (the ring's own waits and barrier order the buffers).  The staged
-  // decode indexes one array of two at run time.
-  constexpr bool kConstBuf = kSwizzle;
+  // A decode over a quantised cache brings the code bytes and row scales of the cache rows into
+  // LDS as they are and turns them into the bf16 tile in LDS (convert below).
+  constexpr bool kDirectQ = kKqSrc || kVqSrc;
+  // LDS rows: unpadded (256 B) with their 16-byte chunks swizzled.
+  constexpr int kKStride = kHeadDim;
+  constexpr int kVStride = kHeadDim;
+  // The two ring buffers, in separate arrays named by a constant (the tile loop is unrolled by
+  // two below): reads of one are then provably independent of the direct loads in flight into the
+  // other, so the compiler adds no vmcnt wait before them (the ring's own waits and barrier order
+  // the buffers).  `buf` is a std::integral_constant.
   __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBlockN * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBlockN * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kBlockN * kVStride];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBlockN * kVStride];
-  __shared__ __attribute__((aligned(16))) __bf16 k_pair[2][kBlockN * kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 v_pair[2][kBlockN * kVStride];
-  // Buffer `buf`: an int, or a std::integral_constant that names it at compile time (the only
-  // form the separate arrays take).
-  auto k_lds = [](auto buf) -> __bf16* {
-    if constexpr (kConstBuf) return decltype(buf)::value ? k_lds1 : k_lds0;
-    else return k_pair[buf];
+  auto k_lds = [](auto buf) -> __bf16* { return decltype(buf)::value ? k_lds1 : k_lds0; };
+  auto v_lds = [](auto buf) -> __bf16* { return decltype(buf)::value ? v_lds1 : v_lds0; };
+  // Decode over a quantised cache: a two-tile ring of code bytes (row-major, 128 B a row) and
+  // row scales per quantised tensor, next to the bf16 ring the MFMAs read.
+  constexpr int kCodeBytes = kDirectQ ? kBlockN * kHeadDim : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t kcode0[kKqSrc ? kCodeBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t kcode1[kKqSrc ? kCodeBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t vcode0[kCodeBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vcode1[kCodeBytes];
+  __shared__ __attribute__((aligned(16))) float kscl0[64], kscl1[64], vscl0[64], vscl1[64];
+  auto code_lds = [](bool v, auto buf) -> uint8_t* {
+    return decltype(buf)::value ? (v ? vcode1 : kcode1) : (v ? vcode0 : kcode0);
   };
-  auto v_lds = [](auto buf) -> __bf16* {
-    if constexpr (kConstBuf) return decltype(buf)::value ? v_lds1 : v_lds0;
-    else return v_pair[buf];
+  auto scl_lds = [](bool v, auto buf) -> float* {
+    return decltype(buf)::value ? (v ? vscl1 : kscl1) : (v ? vscl0 : kscl0);
   };
 
   const int tid = threadIdx.x;
@@ -267,8 +259,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // Waves whose rows all lie past the end skip their compute in the 4-wave bf16 decode only
   // (measured +5% there, from its code generation rather than from the rare dead waves; the
   // 12-wave kernels run 4% slower with it).
-  constexpr bool kSkipDead =
-      kDecode && kDirect && kW == kDecodeDirectSmallWaves;
+  constexpr bool kSkipDead = kDecode && kW == kDecodeDirectSmallWaves;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
   int lim[kQueryBlocks];
@@ -307,137 +298,11 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const uint16_t* k2_base = a.k2 + b * a.k2_sb + h * a.k2_sh + (int64_t)seq_row0 * a.k2_ss;
   const uint16_t* v2_base = a.v2 + b * a.v2_sb + h * a.v2_sh + (int64_t)seq_row0 * a.v2_ss;
 
-  // ---- filling the ring: register staging ----------------------------------------------------
-  // Thread t moves the 16-byte chunk at column 8 (t % 16) of tile rows t / 16 + kRowsPerPass r.
-  const int ld_row = tid >> 4;
-  const int ld_col = (tid & 15) * 8;
-  u32x4 kst[kDirect ? 1 : kChunksPerThread], vst[kDirect ? 1 : kChunksPerThread];
-  // Loads one tile (K or V) starting at key n0; keys >= kv_end read as zero.  The common case
-  // (whole tile from one source, nothing past kv_end) uses a tile-uniform base plus a per-thread
-  // offset; only a tile that straddles the cache/target split or the end resolves each row.
-  // Whole tiles from one source use buffer loads: the lane's offset inside the tile is fixed, the
-  // row pass goes in the scalar offset and the tile's first row in the descriptor base.
+  // Descriptor of one whole tile from one source: its first row, 32-bit offsets inside it.
   auto tile_rsrc = [&](const void* first_row, int64_t row_bytes) {
     const int64_t bytes = (int64_t)(kBlockN - 1) * row_bytes + kHeadDim * 2;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(first_row), (short)0,
                                              (int)(uint32_t)bytes, kBufferWord3);
-  };
-  auto stage_tile = [&](int n0, u32x4* st, const uint16_t* base1, int64_t ss1,
-                        const uint16_t* base2, int64_t ss2) {
-    const bool in_end = n0 + kBlockN <= kv_end;
-    const bool one_src1 = !kDecode || n0 + kBlockN <= kv_split;
-    if (in_end && (one_src1 || n0 >= kv_split)) {
-      const uint16_t* b = one_src1 ? base1 + (int64_t)n0 * ss1 : base2 + (int64_t)(n0 - kv_split) * ss2;
-      const int64_t ss = one_src1 ? ss1 : ss2;
-      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(b, ss * 2);
-      const int voff = ((int)ld_row * (int)ss + ld_col) * 2;
-#pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r)
-        if (!kPartialPass || ld_row + kRowsPerPass * r < kBlockN)
-          st[r] =
-              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss * 2), 0);
-    } else {
-#pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r) {
-        if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
-        const int key = n0 + ld_row + kRowsPerPass * r;
-        const bool valid = key < kv_end;
-        const int kc = valid ? key : kv_end - 1;
-        const bool first = !kDecode || kc < kv_split;
-        const uint16_t* p =
-            (first ? base1 + (int64_t)kc * ss1 : base2 + (int64_t)(kc - kv_split) * ss2) + ld_col;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(p);
-        st[r] = valid ? x : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  // The same for a quantised first source: each chunk is 8 code bytes plus its row's scale.
-  auto stage_tile_q = [&](int n0, u32x4* st, const uint8_t* base1, int64_t ss1,
-                          const float* sbase1, int64_t sss1, const uint16_t* base2, int64_t ss2) {
-    auto load1 = [&](int key) {
-      const u32x2 c = *reinterpret_cast<const u32x2*>(base1 + (int64_t)key * ss1 + ld_col);
-      const float sc = sbase1[(int64_t)key * sss1];
-      return u32x4{c[0], c[1], __builtin_bit_cast(uint32_t, sc), 0u};
-    };
-    const bool in_end = n0 + kBlockN <= kv_end;
-    if (in_end && n0 + kBlockN <= kv_split) {
-      const __amdgpu_buffer_rsrc_t rc = tile_rsrc(base1 + (int64_t)n0 * ss1, ss1);
-      const __amdgpu_buffer_rsrc_t rsc = tile_rsrc(sbase1 + (int64_t)n0 * sss1, sss1 * 4);
-      const int voff = (int)ld_row * (int)ss1 + ld_col;
-      const int soff = (int)ld_row * (int)sss1 * 4;
-#pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r) {
-        if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
-        const u32x2 c =
-            __builtin_amdgcn_raw_buffer_load_b64(rc, voff, (int)(kRowsPerPass * r * ss1), 0);
-        const uint32_t sc =
-            __builtin_amdgcn_raw_buffer_load_b32(rsc, soff, (int)(kRowsPerPass * r * sss1 * 4), 0);
-        st[r] = u32x4{c[0], c[1], sc, 0u};
-      }
-    } else if (in_end && n0 >= kv_split) {
-      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base2 + (int64_t)(n0 - kv_split) * ss2, ss2 * 2);
-      const int voff = ((int)ld_row * (int)ss2 + ld_col) * 2;
-#pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r)
-        if (!kPartialPass || ld_row + kRowsPerPass * r < kBlockN)
-          st[r] =
-              __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)(kRowsPerPass * r * ss2 * 2), 0);
-    } else {
-#pragma unroll
-      for (int r = 0; r < kChunksPerThread; ++r) {
-        if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
-        const int key = n0 + ld_row + kRowsPerPass * r;
-        const bool valid = key < kv_end;
-        const int kc = valid ? key : kv_end - 1;
-        u32x4 x;
-        if (kc < kv_split)
-          x = load1(kc);
-        else
-          x = *reinterpret_cast<const u32x4*>(base2 + (int64_t)(kc - kv_split) * ss2 + ld_col);
-        st[r] = valid ? x : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto stage_k = [&](int n0) {
-    if constexpr (kKqSrc)
-      stage_tile_q(n0, kst, k8_base, a.k_ss, ks_base, a.kcs_ss, k2_base, a.k2_ss);
-    else
-      stage_tile(n0, kst, k_base, a.k_ss, k2_base, a.k2_ss);
-  };
-  auto stage_v = [&](int n0) {
-    if constexpr (kVqSrc)
-      stage_tile_q(n0, vst, v8_base, a.v_ss, vs_base, a.vcs_ss, v2_base, a.v2_ss);
-    else
-      stage_tile(n0, vst, v_base, a.v_ss, v2_base, a.v2_ss);
-  };
-  // 16 consecutive threads write one whole 256-byte row, so the swizzle costs no conflicts here.
-  // Rows ld_row + kRowsPerPass r share ld_row's swizzle (kRowsPerPass is a multiple of 16).
-  const int st_col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(ld_row)) : ld_col;
-  static_assert(kDirect || kRowsPerPass % 16 == 0, "staging passes keep the swizzle phase");
-  // Rows of a quantised source (keys below split) are dequantised on the way into LDS.
-  auto stage_write = [&](auto quant_c, __bf16* lds, int stride, const u32x4* st, int n0) {
-    constexpr bool kQ = decltype(quant_c)::value;
-    const bool all_q = kQ && n0 + kBlockN <= kv_split;
-    const bool some_q = kQ && n0 < kv_split;
-#pragma unroll
-    for (int r = 0; r < kChunksPerThread; ++r) {
-      // (a row past the tile would land in the next buffer)
-      if (kPartialPass && ld_row + kRowsPerPass * r >= kBlockN) continue;
-      u32x4 x = st[r];
-      if (kQ && all_q) {
-        x = dequant(x);
-      } else if (kQ && some_q) {
-        const u32x4 d = dequant(x);
-        x = n0 + ld_row + kRowsPerPass * r < kv_split ? d : x;
-      }
-      *reinterpret_cast<u32x4*>(&lds[(ld_row + kRowsPerPass * r) * stride + st_col]) = x;
-    }
-  };
-  auto write_k = [&](__bf16* lds, int n0) {
-    stage_write(std::integral_constant<bool, kKqSrc>{}, lds, kKStride, kst, n0);
-  };
-  auto write_v = [&](__bf16* lds, int n0) {
-    stage_write(std::integral_constant<bool, kVqSrc>{}, lds, kVStride, vst, n0);
   };
 
   // ---- filling the ring: direct loads ----------------------------------------------------------
@@ -455,7 +320,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   constexpr int kGroups = kBlockN / 4;
   constexpr int kFills = 2 * kGroups;
   constexpr int kFillsPerWave = (kFills + kW - 1) / kW;
-  static_assert(!kDirect || (kW % 4 == 0 && kGroups % 4 == 0), "one swizzle phase per wave");
+  static_assert(kW % 4 == 0 && kGroups % 4 == 0, "one swizzle phase per wave");
   const int dma_r = lane >> 4;
   const int dma_p = lane & 15;
   auto fill_n = [&](int i) { return wave + kW * i; };  // wave-uniform
@@ -472,13 +337,16 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   };
   // This wave's fills of a whole tile from descriptors kr and vr (row strides kss, vss; lane
   // offsets koff, voff).
+  // (do_k, do_v: std::bool_constant; a tensor whose rows come from codes is not filled here)
   auto fill_whole = [&](__amdgpu_buffer_rsrc_t kr, int64_t kss, uint32_t koff,
-                        __amdgpu_buffer_rsrc_t vr, int64_t vss, uint32_t voff, auto buf) {
+                        __amdgpu_buffer_rsrc_t vr, int64_t vss, uint32_t voff, auto buf,
+                        auto do_k, auto do_v) {
 #pragma unroll
     for (int i = 0; i < kFillsPerWave; ++i) {
       if (kFills % kW != 0 && fill_n(i) >= kFills) break;
       const int r0 = 4 * fill_g(i);
       const bool v = fill_is_v(i);
+      if (v ? !decltype(do_v)::value : !decltype(do_k)::value) continue;
       const uint32_t rows_off = (uint32_t)(r0 * (v ? vss : kss) * 2);
       const uint32_t vo = kDecode ? (v ? voff : koff) : (v ? voff : koff) + rows_off;
       const uint32_t so = kDecode ? rows_off : 0u;
@@ -491,13 +359,13 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)n0 * ss), (short)0,
                                              (int)(uint32_t)bytes, kBufferWord3);
   };
-  const uint32_t dma_k = kDirect ? lane_off(a.k_ss) : 0u, dma_v = kDirect ? lane_off(a.v_ss) : 0u;
-  const uint32_t dma_k2 = kDirect && kDecode ? lane_off(a.k2_ss) : 0u;
-  const uint32_t dma_v2 = kDirect && kDecode ? lane_off(a.v2_ss) : 0u;
+  const uint32_t dma_k = lane_off(a.k_ss), dma_v = lane_off(a.v_ss);
+  const uint32_t dma_k2 = kDecode ? lane_off(a.k2_ss) : 0u;
+  const uint32_t dma_v2 = kDecode ? lane_off(a.v2_ss) : 0u;
   auto dma_tile = [&](int n0, auto buf) {
     if constexpr (!kDecode) {
       fill_whole(dma_rsrc(k_base, a.k_ss, n0), a.k_ss, dma_k, dma_rsrc(v_base, a.v_ss, n0), a.v_ss,
-                 dma_v, buf);
+                 dma_v, buf, std::true_type{}, std::true_type{});
       return;
     }
     const bool in_end = n0 + kBlockN <= kv_end;
@@ -505,14 +373,16 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const bool src2 = n0 >= kv_split;
     // decode: whole tiles from one source through buffer loads, the rest row by row below
     if (in_end && src1) {
-      fill_whole(tile_rsrc(k_base + (int64_t)n0 * a.k_ss, a.k_ss * 2), a.k_ss, dma_k,
-                 tile_rsrc(v_base + (int64_t)n0 * a.v_ss, a.v_ss * 2), a.v_ss, dma_v, buf);
+      if constexpr (!kKqSrc || !kVqSrc)
+        fill_whole(tile_rsrc(k_base + (int64_t)n0 * a.k_ss, a.k_ss * 2), a.k_ss, dma_k,
+                   tile_rsrc(v_base + (int64_t)n0 * a.v_ss, a.v_ss * 2), a.v_ss, dma_v, buf,
+                   std::bool_constant<!kKqSrc>{}, std::bool_constant<!kVqSrc>{});
       return;
     }
     if (in_end && src2) {
       fill_whole(tile_rsrc(k2_base + (int64_t)(n0 - kv_split) * a.k2_ss, a.k2_ss * 2), a.k2_ss,
                  dma_k2, tile_rsrc(v2_base + (int64_t)(n0 - kv_split) * a.v2_ss, a.v2_ss * 2),
-                 a.v2_ss, dma_v2, buf);
+                 a.v2_ss, dma_v2, buf, std::true_type{}, std::true_type{});
       return;
     }
 #pragma unroll
@@ -522,6 +392,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       // keys past the end fetch row kv_end - 1 (masked, finite)
       const int key = min(n0 + fill_row(i), kv_end - 1);
       const bool first = key < kv_split;
+      // a quantised tensor's cache rows come from its codes (convert): those lanes load nothing
+      if ((v ? kVqSrc : kKqSrc) && first) continue;
       const uint16_t* p = v ? (first ? v_base + (int64_t)key * a.v_ss
                                      : v2_base + (int64_t)(key - kv_split) * a.v2_ss)
                             : (first ? k_base + (int64_t)key * a.k_ss
@@ -529,6 +401,65 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       const int dst = 4 * fill_g(i) * kHeadDim;
       __builtin_amdgcn_global_load_lds((const void*)(p + fill_col),
                                        (lds_void*)&(v ? v_lds(buf) : k_lds(buf))[dst], 16, 0, 0);
+    }
+  };
+
+  // ---- quantised cache rows (direct-fill decode over an FP8 cache) ------------------------------
+  // code_fill: the code bytes and scales of tile n0's cache rows (rows past the split repeat the
+  // last cache row; convert skips them) into code buffer cb.  Per quantised tensor five loads:
+  // four of 8 rows x 128 B (lane L: row L / 8, bytes 16 (L % 8) ..) and one of the 32 row scales
+  // (lane L: row L % 32); load i goes to wave i % kW.  Buffer loads from a descriptor at the
+  // tile's first row, with 32-bit lane offsets.
+  constexpr int kCodeLoads = (kVqSrc ? 5 : 0) + (kKqSrc ? 5 : 0);
+  auto code_fill = [&](int n0, auto cb) {
+    if constexpr (kDirectQ) {
+      if (n0 >= kv_split) return;
+      const int last = min(kBlockN, kv_split - n0) - 1;  // last cache row of the tile
+      for (int i = wave; i < kCodeLoads; i += kW) {
+        const bool v = kVqSrc && i < 5;
+        const int g = i % 5;
+        if (g < 4) {
+          const int64_t ss = v ? a.v_ss : a.k_ss;
+          const uint8_t* base = (v ? v8_base : k8_base) + (int64_t)n0 * ss;
+          const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)base, (short)0, (int)(uint32_t)(last * ss + kHeadDim), kBufferWord3);
+          const uint32_t off =
+              (uint32_t)min(8 * g + (lane >> 3), last) * (uint32_t)ss + 16u * (lane & 7);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(code_lds(v, cb) + 8 * g * kHeadDim),
+                                                   16, off, 0, 0, 0);
+        } else {
+          const int64_t ss = v ? a.vcs_ss : a.kcs_ss;
+          const float* base = (v ? vs_base : ks_base) + (int64_t)n0 * ss;
+          const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)base, (short)0, (int)(uint32_t)((last * ss + 1) * 4), kBufferWord3);
+          const uint32_t off = (uint32_t)min(lane & 31, last) * (uint32_t)ss * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)scl_lds(v, cb), 4, off, 0, 0, 0);
+        }
+      }
+    }
+  };
+  // convert: the cache rows of tile n0 from code buffer `buf` into the bf16 tile of the same
+  // index, value = E4M3(code) * scale rounded to bf16 (dequant), in the tile's swizzled layout.
+  // Work items of 8 values, 512 per quantised tensor (V first): item c is row (c % 512) / 16,
+  // columns 8 (c % 16) .. + 7, taken by thread c % kThreads.
+  auto convert = [&](int n0, auto buf) {
+    if constexpr (kDirectQ) {
+      if (n0 >= kv_split) return;
+      constexpr int kItems = 512 * ((kVqSrc ? 1 : 0) + (kKqSrc ? 1 : 0));
+#pragma unroll
+      for (int c0 = 0; c0 < kItems; c0 += kThreads) {
+        const int c = c0 + tid;
+        if (kItems % kThreads != 0 && c >= kItems) break;
+        const bool v = kVqSrc && c < 512;
+        const int row = (c & 511) >> 4, col8 = c & 15;
+        if (n0 + row >= kv_split) continue;
+        const uint2 codes =
+            *reinterpret_cast<const uint2*>(code_lds(v, buf) + row * kHeadDim + 8 * col8);
+        const float sc = scl_lds(v, buf)[row];
+        const u32x4 x = {codes.x, codes.y, __builtin_bit_cast(uint32_t, sc), 0u};
+        __bf16* dst = (v ? v_lds(buf) : k_lds(buf)) + row * kHeadDim + 8 * (col8 ^ swz(row));
+        *reinterpret_cast<u32x4*>(dst) = dequant(x);
+      }
     }
   };
 
@@ -541,11 +472,13 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       kDecode || (a.kc == nullptr && a.vc == nullptr) ? 0 : min(cache_lo + kRows, cache_len);
   // Chunk tid + kThreads r of the tile: row (tid >> 4) + kRowsPerPass r, chunk tid % 16 (a
   // partial last pass stores nothing past the tile).
+  const int ld_row = tid >> 4;
+  const int ld_col = (tid & 15) * 8;
   auto store_row = [&](int n0, auto buf, int r) {
     const int row = ld_row + kRowsPerPass * r;
     const int key = n0 + row;
     if (row >= kBlockN || key < cache_lo || key >= cache_hi) return;
-    const int col = kSwizzle ? 8 * ((ld_col >> 3) ^ swz(row)) : ld_col;
+    const int col = 8 * ((ld_col >> 3) ^ swz(row));
     const int64_t at = (int64_t)cache_row0 + key;
     if (a.kc != nullptr)
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kc) + b * a.kc_sb + at * a.kc_ss +
@@ -576,12 +509,12 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   auto k_addr = [&](int kb, int c) {
     const int row = 32 * kb + qn;
     const int chunk = 2 * c + half;
-    return row * kKStride + 8 * (kSwizzle ? (chunk ^ swz(row)) : chunk);
+    return row * kKStride + 8 * (chunk ^ swz(row));
   };
   auto v_addr = [&](int kc, int d, int hi) {
     const int row = 16 * kc + tr_row + 8 * hi;
     const int col = 32 * d + tr_col;
-    return row * kVStride + (kSwizzle ? 8 * ((col >> 3) ^ swz(row)) + (col & 7) : col);
+    return row * kVStride + 8 * ((col >> 3) ^ swz(row)) + (col & 7);
   };
   // The same offsets computed once, in bytes.  Key block kb (K) and 16-row group kc (V) only add
   // constants (swz(row) depends on row bits 0..3, and those do not change with kb or kc), and so
@@ -590,29 +523,18 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // step c (K) and each (row half hi, column block d) pair (V) keeps its own offset; the asm
   // barrier stops the compiler from re-deriving them inside the loop.
   int koff[8], voff[2][4];
-  if constexpr (kSwizzle) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      koff[c] = 2 * k_addr(0, c);
-      asm volatile("" : "+v"(koff[c]));
-    }
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        voff[hi][d] = 2 * v_addr(0, d, hi);
-        asm volatile("" : "+v"(voff[hi][d]));
-      }
-  } else {
-    int k0 = 2 * k_addr(0, 0), v0 = 2 * v_addr(0, 0, 0);
-    asm volatile("" : "+v"(k0), "+v"(v0));
-#pragma unroll
-    for (int c = 0; c < 8; ++c) koff[c] = k0 + 32 * c;
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) voff[hi][d] = v0 + 2 * (8 * hi * kVStride + 32 * d);
+  for (int c = 0; c < 8; ++c) {
+    koff[c] = 2 * k_addr(0, c);
+    asm volatile("" : "+v"(koff[c]));
   }
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      voff[hi][d] = 2 * v_addr(0, d, hi);
+      asm volatile("" : "+v"(voff[hi][d]));
+    }
   // Operand reads from buffer `cur`: an int, or a std::integral_constant where the loop is
   // unrolled by two tiles, which leaves no address arithmetic in the loop at all.
   auto k_read = [&](auto cur, int c, int kb) {
@@ -638,31 +560,25 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ---- prologue ----------------------------------------------------------------------------------
-  // Tile j lives in buffer (j - j_begin) % 2.  Direct fills: the first two tiles resident.
-  // Staging: the first tile resident, the next one in registers.
+  // Tile j lives in buffer (j - j_begin) % 2; the first two tiles resident.
   using Buf0 = std::integral_constant<int, 0>;
   using Buf1 = std::integral_constant<int, 1>;
-  if constexpr (kDirect) {
-    auto prime = [&](int t, auto buf) {
-      if (j_begin + t < j_end) {
-        if constexpr (kConstBuf) dma_tile((j_begin + t) * kBlockN, buf);
-        else dma_tile((j_begin + t) * kBlockN, (int)decltype(buf)::value);
-      }
-    };
-    prime(0, Buf0{});
-    prime(1, Buf1{});
+  if (j_begin < j_end) dma_tile(j_begin * kBlockN, Buf0{});
+  if (j_begin + 1 < j_end) dma_tile((j_begin + 1) * kBlockN, Buf1{});
+  if constexpr (kDirectQ) {
+    // the codes of the first two tiles, converted once they are all in; the third tile's codes
+    // go into code buffer 0 only after every wave has converted from it
+    if (j_begin < j_end) code_fill(j_begin * kBlockN, Buf0{});
+    if (j_begin + 1 < j_end) code_fill((j_begin + 1) * kBlockN, Buf1{});
     __builtin_amdgcn_s_waitcnt(0);
-  } else {
-    const int first = j_begin * kBlockN;
-    stage_k(first);
-    stage_v(first);
-    write_k(k_lds(0), first);
-    write_v(v_lds(0), first);
-    if (j_begin + 1 < j_end) {
-      stage_k(first + kBlockN);
-      stage_v(first + kBlockN);
-    }
+    __syncthreads();
+    if (j_begin < j_end) convert(j_begin * kBlockN, Buf0{});
+    if (j_begin + 1 < j_end) convert((j_begin + 1) * kBlockN, Buf1{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j_begin + 2 < j_end) code_fill((j_begin + 2) * kBlockN, Buf0{});
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // One key tile j from buffer cur.  kMasked: the tile crosses some row's key limit.  Full tiles
@@ -786,45 +702,36 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     }
 
-    // ---- refill.  Staging: write tile j+1 into the other buffer (its tile j-1 was consumed
-    // before the last barrier) and start fetching tile j+2.  Direct: tile j+1 was issued one
-    // iteration ago; wait for it, then after the barrier reuse this buffer for tile j+2.
-    if constexpr (kDirect) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (j + 2 < j_end) dma_tile((j + 2) * kBlockN, cur);
-    } else {
-      if (j + 1 < j_end) {
-        write_k(k_lds(cur ^ 1), n0 + kBlockN);
-        write_v(v_lds(cur ^ 1), n0 + kBlockN);
+    // ---- refill: tile j+1 was issued one iteration ago; wait for it, then after the barrier
+    // reuse this buffer for tile j+2
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 2 < j_end) {
+      // quantised cache rows of tile j+2: their codes (code buffer cur, fetched one tile ago)
+      // into this buffer; then the codes of tile j+3 into the other code buffer, which every
+      // wave finished converting from before this barrier
+      convert((j + 2) * kBlockN, cur);
+      dma_tile((j + 2) * kBlockN, cur);
+      if constexpr (kDirectQ) {
+        if (j + 3 < j_end)
+          code_fill((j + 3) * kBlockN, std::integral_constant<int, 1 - decltype(cur)::value>{});
       }
-      if (j + 2 < j_end) {
-        stage_k((j + 2) * kBlockN);
-        stage_v((j + 2) * kBlockN);
-      }
-      __syncthreads();
     }
   };
   // tiles [0, n_full) lie entirely below every row's limit; the rest need the mask
   const int n_full = min(j_end, kv_full / kBlockN);
-  if constexpr (kConstBuf) {
-    // two tiles per trip, buffer 0 then buffer 1, so that each copy names its buffer by a constant
-    auto run = [&](auto masked_c, int lo, int hi) {
-      int j = lo;
-      if (j < hi && ((j - j_begin) & 1)) tile_step(masked_c, j++, Buf1{});
-      for (; j + 1 < hi; j += 2) {
-        tile_step(masked_c, j, Buf0{});
-        tile_step(masked_c, j + 1, Buf1{});
-      }
-      if (j < hi) tile_step(masked_c, j, Buf0{});
-    };
-    run(std::false_type{}, j_begin, n_full);
-    run(std::true_type{}, max(j_begin, n_full), j_end);
-  } else {
-    for (int j = j_begin; j < n_full; ++j) tile_step(std::false_type{}, j, (j - j_begin) & 1);
-    for (int j = max(j_begin, n_full); j < j_end; ++j)
-      tile_step(std::true_type{}, j, (j - j_begin) & 1);
-  }
+  // two tiles per trip, buffer 0 then buffer 1, so that each copy names its buffer by a constant
+  auto run = [&](auto masked_c, int lo, int hi) {
+    int j = lo;
+    if (j < hi && ((j - j_begin) & 1)) tile_step(masked_c, j++, Buf1{});
+    for (; j + 1 < hi; j += 2) {
+      tile_step(masked_c, j, Buf0{});
+      tile_step(masked_c, j + 1, Buf1{});
+    }
+    if (j < hi) tile_step(masked_c, j, Buf0{});
+  };
+  run(std::false_type{}, j_begin, n_full);
+  run(std::true_type{}, max(j_begin, n_full), j_end);
 
   // ---- split epilogue: this key range's unnormalised O, running max m (scaled, base 2) and row
   // sum l, to be merged by split_combine.  Layout [split][b][row][h] (x 128 for O).
@@ -909,25 +816,17 @@ __global__ __launch_bounds__(256) void split_combine(const AttnArgs a) {
 __global__ __launch_bounds__(64 * kPrefillWaves)
 __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
 void attn_prefill(const AttnArgs a) {
-  attn_fwd<false, true, kCacheBf16, kPrefillBlockN, kPrefillWaves>(a);
+  attn_fwd<false, kCacheBf16, kPrefillBlockN, kPrefillWaves>(a);
 }
 
-// Decode over [prefix cache in format kFmt ; target], register-staged fills: the FP8 caches,
-// which are dequantised on their way into LDS.
-template <int kFmt, int kW>
-__global__ __launch_bounds__(64 * kW)
-__attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd, kDecodeWavesPerSimd)))
-void attn_decode(const AttnArgs a) {
-  attn_fwd<true, false, kFmt, kDecodeBlockN, kW>(a);
-}
-
-// Decode over a bf16 cache: direct-to-LDS fills like the prefill's, 32-key tiles at 3 waves per
+// Decode over [prefix cache in format kFmt ; target]: direct-to-LDS fills like the prefill's
+// (an FP8 cache's codes and scales too, turned into bf16 in LDS), 32-key tiles at 3 waves per
 // SIMD, kW waves per workgroup.
-template <int kW>
+template <int kFmt, int kW>
 __global__ __launch_bounds__(64 * kW)
 __attribute__((amdgpu_waves_per_eu(kDecodeDirectWavesPerSimd, kDecodeDirectWavesPerSimd)))
 void attn_decode_direct(const AttnArgs a) {
-  attn_fwd<true, true, kCacheBf16, kDecodeDirectBlockN, kW>(a);
+  attn_fwd<true, kFmt, kDecodeDirectBlockN, kW>(a);
 }
 
 // Compute units of the current device (cached per device).
@@ -1002,22 +901,17 @@ hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   };
   // the wider workgroup where its grid gives every CU at least two, else the narrower one
   auto wide = [&](int waves) { return tiles(waves) * heads >= 2 * (int64_t)device_cus(); };
-  auto staged = [&](auto fmt_c) {
+  auto direct = [&](auto fmt_c) {
     constexpr int kF = decltype(fmt_c)::value;
-    if (wide(kStagedWaves))
-      launch(attn_decode<kF, kStagedWaves>, kStagedWaves);
+    if (wide(kDecodeDirectWaves))
+      launch(attn_decode_direct<kF, kDecodeDirectWaves>, kDecodeDirectWaves);
     else
-      launch(attn_decode<kF, kStagedSmallWaves>, kStagedSmallWaves);
+      launch(attn_decode_direct<kF, kDecodeDirectSmallWaves>, kDecodeDirectSmallWaves);
   };
   switch (a.cache_fmt) {
-    case kCacheBf16:
-      if (wide(kDecodeDirectWaves))
-        launch(attn_decode_direct<kDecodeDirectWaves>, kDecodeDirectWaves);
-      else
-        launch(attn_decode_direct<kDecodeDirectSmallWaves>, kDecodeDirectSmallWaves);
-      break;
-    case kCacheFp8V: staged(std::integral_constant<int, kCacheFp8V>{}); break;
-    case kCacheFp8KV: staged(std::integral_constant<int, kCacheFp8KV>{}); break;
+    case kCacheBf16: direct(std::integral_constant<int, kCacheBf16>{}); break;
+    case kCacheFp8V: direct(std::integral_constant<int, kCacheFp8V>{}); break;
+    case kCacheFp8KV: direct(std::integral_constant<int, kCacheFp8KV>{}); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -11,36 +11,27 @@
 namespace bca {
 
 // Tile shape.  A wave owns kQueryBlocks blocks of 32 query rows, and a workgroup's query rows
-// form one tile.  Per kernel: waves per workgroup, keys per key tile (32 or 64) and waves per
-// SIMD.  The prefill and the bf16-cache decode are filled by direct loads and run 32-key tiles
-// at 3 waves per SIMD; their workgroups have 12 waves (one workgroup per CU), so each K/V tile
-// loaded into LDS serves 384 query rows.  A decode whose 12-wave grid would not give every CU
-// two workgroups runs 4-wave ones instead.  The decode over an FP8 cache dequantises through
-// registers and runs 64-key tiles at 2 waves per SIMD in 8-wave workgroups (4 on small grids)
-// (measured fastest for each).
+// form one tile.  Per kernel: waves per workgroup, keys per key tile and waves per SIMD.  The
+// prefill and the decode (any cache format) are filled by direct loads and run 32-key tiles at 3
+// waves per SIMD; their workgroups have 12 waves (one workgroup per CU), so each K/V tile loaded
+// into LDS serves 384 query rows.  A decode whose 12-wave grid would not give every CU two
+// workgroups runs 4-wave ones instead.
 constexpr int kHeadDim = 128;  // the only head width the kernels are built for
 constexpr int kQueryBlocks = 1;
 constexpr int kPrefillWaves = 12;
 constexpr int kDecodeDirectWaves = 12;      // large decode grids
 constexpr int kDecodeDirectSmallWaves = 4;  // small decode grids
-// Waves per workgroup of the register-staged decode (FP8 caches): 8 on large grids (one
-// workgroup per CU at 2 waves per SIMD), 4 on grids under two such workgroups per CU.
-constexpr int kStagedWaves = 8;
-constexpr int kStagedSmallWaves = 4;
 constexpr int kBlockM = 32 * kQueryBlocks * kPrefillWaves;  // prefill query tile (= plan tile)
 // Fewest query rows any decode workgroup takes (bounds the decode's grid).
 constexpr int kDecodeMinBlockM = 32 * kQueryBlocks * 4;
 constexpr int kPrefillBlockN = 32;
 constexpr int kPrefillWavesPerSimd = 3;
-constexpr int kDecodeBlockN = 64;  // register-staged decode (FP8 caches)
-constexpr int kDecodeWavesPerSimd = 2;
-constexpr int kDecodeDirectBlockN = 32;  // direct-fill decode (bf16 cache)
+constexpr int kDecodeDirectBlockN = 32;
 constexpr int kDecodeDirectWavesPerSimd = 3;
 // A split decode's key ranges are whole multiples of kSplitUnit keys, whatever the kernel's tile
 // width (which divides it), so the workspace a plan needs does not depend on the cache format.
 constexpr int kSplitUnit = 64;
-static_assert(kSplitUnit % kDecodeBlockN == 0 && kSplitUnit % kDecodeDirectBlockN == 0,
-              "split units hold whole key tiles");
+static_assert(kSplitUnit % kDecodeDirectBlockN == 0, "split units hold whole key tiles");
 
 // Prefix-cache storage formats (values of bca_cache_format).
 constexpr int kCacheBf16 = 0;   // K and V bf16

@@ -276,8 +276,8 @@ bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, floa
 
 /*
  * bca_decode_ex -- bca_decode reading the prefix from a cache of any format.  Quantised rows are
- * dequantised on their way into the kernel's on-chip tiles (value * scale, rounded to bf16);
- * nothing is written back.  cache may be NULL only when the plan's prefix_len is 0.
+ * brought on chip as codes and scales and dequantised there into the kernel's bf16 tiles
+ * (value * scale, rounded to bf16); nothing is written back.  cache may be NULL only when the plan's prefix_len is 0.
  */
 bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
                          const bca_tensor* q_tgt, const bca_kv_cache* cache,
@@ -288,9 +288,8 @@ bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float
  * bca_cache_dequantize -- writes a prefix cache of any format back as bf16: k_out, v_out bf16
  * [B, P, H, D] receive E4M3(code) * scale formed in fp32 and rounded to bf16 (RNE) for a quantised
  * tensor, a copy for a bf16 one.  That is the value bca_decode_ex uses for the same code, so the
- * decode over the expanded cache sees bitwise the K and V of bca_decode_ex over the FP8 one (the
- * two outputs agree to rounding: the bf16 and FP8 decodes walk the keys in tiles of different
- * width).
+ * decode over the expanded cache sees bitwise the K and V of bca_decode_ex over the FP8 one, and
+ * the two outputs are bitwise equal (both decodes walk the same bf16 tiles).
  * Meant for expanding one layer's FP8 cache into a transient buffer just before that layer's
  * cached step (the FP8 form keeps the memory of all layers; the bf16 decode is the faster one).
  * The outputs must not overlap the cache.  D must be 128.  Enqueues one kernel on stream.
