@@ -425,15 +425,25 @@ def decode_generation_timing(torch, bca, plan, kc2, vc2, od, Bd, N, H, flops_dec
             "frac_peak_median": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def plan_timing(torch, bca, ids, dev):
-    """Where the plan's build time goes: host planning alone (a host-only plan), the full build
-    (host planning + one device allocation and copy) twice, the first one in the process paying
-    the runtime's first-use costs."""
+def plan_timing(torch, bca, W, ids, dev, reps=5):
+    """Where the plan's build time goes: host planning alone (host-only plans: the first call in
+    the process, then the median of `reps` more), for this shape, the 4-ref long layout and the
+    NEO-like varlen batch; and the full build (host planning + one device allocation and copy)
+    twice, the first one in the process paying the runtime's first-use costs."""
+    def host_ms(make):
+        ts = []
+        for _ in range(reps + 1):
+            t0 = time.perf_counter()
+            h = make()
+            ts.append((time.perf_counter() - t0) * 1e3)
+            h.free()
+        return round(ts[0], 3), round(float(np.median(ts[1:])), 3)
     out = {}
-    t0 = time.perf_counter()
-    h = bca.Plan(ids, host_only=True)
-    out["host_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
-    h.free()
+    out["host_first_ms"], out["host_ms"] = host_ms(lambda: bca.Plan(ids, host_only=True))
+    ids5 = W.LONG_4REF.block_ids()
+    out["host_ms_long_4ref"] = host_ms(lambda: bca.Plan(ids5, host_only=True))[1]
+    neo, _ = W.neo_like_batch(16, 16, 8192, 246)
+    out["host_ms_varlen_neo16x8192"] = host_ms(lambda: bca.Plan.varlen(neo, host_only=True))[1]
     for key in ("full_first_ms", "full_again_ms"):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -490,7 +500,7 @@ def main():
     cfg = W.EDIT_2REF_CFG
     ids = pre.block_ids()
     S, H = pre.seq_len, pre.heads
-    plan_split = plan_timing(torch, bca, ids, dev)
+    plan_split = plan_timing(torch, bca, W, ids, dev)
     t0 = time.perf_counter()
     plan = bca.Plan(ids)
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -581,7 +591,7 @@ def main():
 
     # the dominant kernel: the call with the larger share of the step
     if dec_ms.mean() >= pre_ms.mean():
-        dom, key, achieved = ("decode: attn_decode_direct<12> (bf16 cache), B=2", "decode_cfg_b2",
+        dom, key, achieved = ("decode: attn_decode_direct<0, 12> (bf16 cache), B=2", "decode_cfg_b2",
                               dec_tf)
     else:
         dom, key, achieved = ("prefill: attn_prefill (writes the bf16 prefix cache), B=1",
