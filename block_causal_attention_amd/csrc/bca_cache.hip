@@ -5,8 +5,8 @@
 //     cost the loop registers it needs for its operand reads.
 //   cache_dequant: a cache written back as bf16, once per layer, so that the cached step can run
 //     the bf16 decode.  The value of a code is its E4M3 value times the row scale, formed in fp32
-//     and rounded to bf16 (RNE): the same rule the decode applies when it dequantises while
-//     staging, so both paths see bitwise the same K and V.
+//     and rounded to bf16 (RNE): the same rule the decode applies when it turns the codes into
+//     its bf16 tiles in LDS, so both paths see bitwise the same K and V.
 // Sixteen lanes per 128-value row, eight values per lane.  HBM-bound.
 #include "bca_internal.h"
 
