@@ -9,6 +9,9 @@ with its own cache (the guide's section "The prefix cache is a compute-for-memor
 * The full-size pair (the 2-ref 1024^2 edit as the cond branch, S = 12,400, and an uncond branch
   with an 8-position prompt, S = 12,360; H = 32): caches bitwise, prefill and cached step on
   sampled rows against the oracle, and the batched step bitwise equal to per-branch decodes.
+* Strided views (Q/K/V rows of one packed buffer, caches and outputs inside wider buffers) give
+  bitwise the contiguous results, and a one-sequence plan through bca_decode_varlen is bitwise
+  the plain decode.
 """
 import numpy as np
 import pytest
@@ -146,3 +149,44 @@ def test_cfg_full_size_pair():
         got = r["od"][int(off["t"][b]) + drows[b]][:, heads]
         check(got, dwant[b], f"cached step branch {b} (sampled rows)")
     check_per_branch_decode(r, ids_list, H)
+
+
+def test_cfg_strided_views_and_single_plan():
+    """Strided inputs (packed QKV rows), strided cache views and a strided output give bitwise the
+    contiguous results; a single-sequence plan through bca_decode_varlen is the plain decode."""
+    ids_list = [branch_layout(*b) for b in [(29, 130, 3, 200), (5, 130, 3, 200)]]
+    lens = [len(i) for i in ids_list]
+    starts = O.packed_row_starts(lens)
+    H = 2
+    say("test_cfg_strided_views_and_single_plan")
+    r = run_branches(ids_list, starts, H, 311)
+    plan = r["plan"]
+    P, N = plan.info.prefix_len, plan.info.target_len
+    R = r["q"].shape[0]
+    # Q, K, V as slices of one packed [R, 3, H, 128] buffer; caches inside wider buffers
+    qkv = torch.stack([to_dev(r["q"]), to_dev(r["k"]), to_dev(r["v"])], dim=1)
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    kc_big = torch.zeros((P, H + 1, 128), dtype=torch.bfloat16, device=DEV)
+    vc_big = torch.zeros((P, 2, H, 128), dtype=torch.bfloat16, device=DEV)
+    kc, vc = kc_big[:, :H], vc_big[:, 1]
+    o_big = torch.zeros((R, H, 2, 128), dtype=torch.float32, device=DEV)
+    o = o_big[:, :, 1]
+    bca.prefill_varlen(plan, q, k, v, k_cache=kc, v_cache=vc, out=o)
+    t = torch.stack([to_dev(r["qt"]), to_dev(r["kt"]), to_dev(r["vt"])], dim=2)
+    od_big = torch.zeros((N, 2, H, 128), dtype=torch.float32, device=DEV)
+    od = bca.decode_varlen(plan, t[:, :, 0], kc, vc, t[:, :, 1], t[:, :, 2], out=od_big[:, 0])
+    torch.cuda.synchronize()
+    for a, bq in ((o, r["o"]), (od, r["od"])):
+        assert np.array_equal(a.cpu().numpy()[:bq.shape[0]], bq)
+    assert torch.equal(kc.cpu(), r["kc"].cpu()) and torch.equal(vc.cpu(), r["vc"].cpu())
+    # one sequence, planned with bca_plan: bca_decode_varlen is the plain decode
+    ids = ids_list[0]
+    plan1 = bca.Plan(ids)
+    P1, N1 = plan1.info.prefix_len, plan1.info.target_len
+    qb, kb, vb = (to_dev(x[:len(ids)]) for x in (r["q"], r["k"], r["v"]))
+    kc1 = kb[:P1].contiguous()
+    vc1 = vb[:P1].contiguous()
+    od1 = bca.decode_varlen(plan1, qb[P1:], kc1, vc1, kb[P1:], vb[P1:])
+    od2 = bca.decode(plan1, qb[None, P1:], kc1[None], vc1[None], kb[None, P1:], vb[None, P1:])
+    torch.cuda.synchronize()
+    assert np.array_equal(od1.cpu().numpy(), od2.cpu().numpy()[0])
