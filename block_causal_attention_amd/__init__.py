@@ -45,19 +45,27 @@ def _check(status: int) -> None:
         raise BcaError(status, _lib.load().bca_last_error().decode())
 
 
+def _ids32(block_ids) -> np.ndarray:
+    """A block-id vector as contiguous int32, rejecting values outside the int32 range."""
+    if hasattr(block_ids, "detach"):
+        block_ids = block_ids.detach().cpu().numpy()
+    a = np.asarray(block_ids)
+    if a.dtype.kind == "i" and a.dtype.itemsize <= 4 or a.dtype.kind == "u" and a.dtype.itemsize < 4:
+        return np.ascontiguousarray(a, dtype=np.int32)
+    a = np.asarray(a, dtype=np.int64)
+    if a.size and (a.min() < -(2**31) or a.max() >= 2**31):
+        raise BcaError(_lib.BCA_ERR_BLOCK_IDS, "block id out of int32 range")
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
 class Plan:
     """Launch plan built from a per-position block-id vector (see include/bca.h, bca_plan)."""
 
     def __init__(self, block_ids, host_only: bool = False):
         lib = _lib.load()
-        if hasattr(block_ids, "detach"):
-            block_ids = block_ids.detach().cpu().numpy()
-        ids = np.ascontiguousarray(np.asarray(block_ids, dtype=np.int64))
-        if ids.ndim != 1:
+        ids32 = _ids32(block_ids)
+        if ids32.ndim != 1:
             raise ValueError("block ids must be 1-D")
-        if ids.size and (ids.min() < -(2**31) or ids.max() >= 2**31):
-            raise BcaError(_lib.BCA_ERR_BLOCK_IDS, "block id out of int32 range")
-        ids32 = ids.astype(np.int32)
         self._h = ctypes.c_void_p()
         flags = _lib.BCA_PLAN_HOST_ONLY if host_only else 0
         ptr = ids32.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if ids32.size else None
@@ -69,11 +77,10 @@ class Plan:
         """Plan for a batch of sequences with their own layouts (bca_plan_varlen): sequence b
         at rows [row_start[b], row_start[b] + len_b) (default: packed)."""
         lib = _lib.load()
-        seqs = [np.asarray(i.detach().cpu().numpy() if hasattr(i, "detach") else i, np.int64)
-                for i in ids_list]
+        seqs = [_ids32(i) for i in ids_list]
         if not seqs or any(x.ndim != 1 for x in seqs):
             raise ValueError("ids_list must be a non-empty list of 1-D id vectors")
-        flat = np.ascontiguousarray(np.concatenate(seqs).astype(np.int32))
+        flat = np.ascontiguousarray(np.concatenate(seqs))
         lens = np.ascontiguousarray(np.array([x.size for x in seqs], dtype=np.int64))
         starts = None
         if row_start is not None:

@@ -313,6 +313,11 @@ def test_varlen_plan_errors():
     assert status(lambda: bca.Plan.varlen([a, np.array([0, -1, 0])], host_only=True)) == \
         _lib.BCA_ERR_BLOCK_IDS
     assert b"sequence 1" in _lib.load().bca_last_error()
+    # ids past int32 are rejected before they reach the library (not wrapped)
+    assert status(lambda: bca.Plan.varlen([a, np.array([-1, 2**31], np.int64)],
+                                          host_only=True)) == _lib.BCA_ERR_BLOCK_IDS
+    assert status(lambda: bca.Plan(np.array([0, 2**31, 2**31], np.uint32), host_only=True)) == \
+        _lib.BCA_ERR_BLOCK_IDS
     ok = bca.Plan.varlen([a, b], row_start=[3, 0], host_only=True)   # gaps, any order
     assert ok.info.rows == 6
     lib = _lib.load()
