@@ -36,6 +36,9 @@
 // come in the same way, two tiles ahead, and are turned into the bf16 tile in LDS.
 #include <atomic>
 #include <mutex>
+#include <queue>
+#include <vector>
+#include <algorithm>
 #include <type_traits>
 
 #include "bca_internal.h"
@@ -202,8 +205,37 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   const int full8 = total & ~7;
   int work = blockIdx.x;
   if (work < full8) work = (work & 7) * (full8 >> 3) + (work >> 3);
-  const int bhs = work / a.n_qtiles;
-  const int slot = work - bhs * a.n_qtiles;
+  int bhs = work / a.n_qtiles;
+  int slot = work - bhs * a.n_qtiles;
+  // The 12-wave decode may instead take query tiles of three heights (AttnArgs::mix): a round of
+  // 256-row tiles (two waves per SIMD with rows) after the 384-row ones fills a grid whose
+  // 384-row tiles would leave the last round part empty.
+  constexpr bool kMix = kDecode && kW == kDecodeDirectWaves;
+  static_assert(!kMix || kRows == 384, "tile heights 384, 256, 128");
+  int mix_row0 = 0, tile_rows = kRows;
+  if constexpr (kMix) {
+    mix_row0 = slot * kRows;
+    if (a.mix[0] > 0) {
+      // this XCD's bh_count / 8 (batch, head) entries (bh_count % 8 == 0 here)
+      const int nb = bh_count >> 3;
+      int l = blockIdx.x >> 3, hl;
+      if (l < nb * a.mix[0]) {
+        hl = l / a.mix[0];
+        mix_row0 = 384 * (l - hl * a.mix[0]);
+      } else if ((l -= nb * a.mix[0]) < nb * a.mix[1]) {
+        hl = l / a.mix[1];
+        mix_row0 = 384 * a.mix[0] + 256 * (l - hl * a.mix[1]);
+        tile_rows = 256;
+      } else {
+        l -= nb * a.mix[1];
+        hl = l / a.mix[2];
+        mix_row0 = 384 * a.mix[0] + 256 * a.mix[1] + 128 * (l - hl * a.mix[2]);
+        tile_rows = 128;
+      }
+      bhs = (blockIdx.x & 7) * nb + hl;
+      slot = 0;
+    }
+  }
   const int bh = kDecode ? bhs / n_split : bhs;
   const int split = kDecode ? bhs - bh * n_split : 0;
   const int b = bh / a.heads;
@@ -216,6 +248,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // cache_row0: first cache row of the sequence's prefix (stored by the prefill, read by a
   // decode over a batch of sequences, whose targets start at tensor row seq_row0).
   int seq_row0 = 0, row0 = tile * kRows, n_rows = a.n_q, rl_off = 0;
+  if constexpr (kMix) row0 = mix_row0;
   int kv_len = a.kv_len, kv_split = a.split, kv_end = a.kv_len, kv_full = a.kv_len;
   int cache_len = 0, cache_row0 = 0;
   if constexpr (!kDecode) {
@@ -239,6 +272,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     // workgroup leaves before any barrier)
     if (row0 >= n_rows) return;
   }
+  // this tile's real rows end here
+  const int row_end = kMix ? min(n_rows, row0 + tile_rows) : n_rows;
   const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
   // key tiles this workgroup visits: all of them, or its split's range
   const int split_tiles = a.split_units * (kSplitUnit / kBlockN);
@@ -247,7 +282,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
 
   // does any of this wave's query rows exist (wave-uniform)
   const int wave_row0 = row0 + wave * 32 * kQueryBlocks;
-  const bool live = wave_row0 + 32 * kQueryBlocks > 0 && wave_row0 < n_rows;
+  const bool live = wave_row0 + 32 * kQueryBlocks > 0 && wave_row0 < row_end;
   // Prefill: the largest key limit among this wave's real rows (wave-uniform: limits never
   // decrease along a sequence, so it is the last real row's).  A key tile starting at or past it
   // is invisible to the whole wave, whose part of that tile then adds exact zeros.
@@ -256,9 +291,8 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     const int last = min(wave_row0 + 32 * kQueryBlocks - 1, n_rows - 1);
     wave_lim = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : a.row_limit[rl_off + last]);
   }
-  // Waves whose rows all lie past the end skip their compute in the 4-wave bf16 decode only
-  // (measured +5% there, from its code generation rather than from the rare dead waves; the
-  // 12-wave kernels run 4% slower with it).
+  // In the 4-wave decode, a wave whose rows all lie past the end skips its compute inside the
+  // tile loop (measured 5% faster there than a loop of its own, from the code generation).
   constexpr bool kSkipDead = kDecode && kW == kDecodeDirectSmallWaves;
 
   // This lane's query rows, their key limits, and their Q slices as MFMA B operands.
@@ -268,7 +302,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
 #pragma unroll
   for (int qb = 0; qb < kQueryBlocks; ++qb) {
     const int row = row0 + (wave * kQueryBlocks + qb) * 32 + qn;
-    row_ok[qb] = row >= 0 && row < n_rows;  // a prefill tile's first rows may be padding
+    row_ok[qb] = row >= 0 && row < row_end;  // a prefill tile's first rows may be padding
     lim[qb] = kDecode ? kv_len : a.row_limit[rl_off + (row_ok[qb] ? row : n_rows - 1)];
     const uint16_t* qp = a.q + b * a.q_sb + (int64_t)(seq_row0 + (row_ok[qb] ? row : 0)) * a.q_ss +
                          h * a.q_sh + 8 * half;
@@ -718,6 +752,19 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
       }
     }
   };
+  // The share of tile j of a wave without query rows: the same fills and barrier.
+  auto idle_step = [&](int j, auto cur) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 2 < j_end) {
+      convert((j + 2) * kBlockN, cur);
+      dma_tile((j + 2) * kBlockN, cur);
+      if constexpr (kDirectQ) {
+        if (j + 3 < j_end)
+          code_fill((j + 3) * kBlockN, std::integral_constant<int, 1 - decltype(cur)::value>{});
+      }
+    }
+  };
   // tiles [0, n_full) lie entirely below every row's limit; the rest need the mask
   const int n_full = min(j_end, kv_full / kBlockN);
   // two tiles per trip, buffer 0 then buffer 1, so that each copy names its buffer by a constant
@@ -730,6 +777,21 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     }
     if (j < hi) tile_step(masked_c, j, Buf0{});
   };
+  // 12-wave decode: a wave without query rows (a 256- or 128-row tile, or past the end) runs the
+  // tile loop's barriers in a loop of its own, which leaves the compute loop free of any test for
+  // it.  (The prefill's padding waves, in a sequence's first tile only, compute zeros.)
+  if constexpr (kMix) {
+    if (!live) {
+      int j = j_begin;
+      if (j < j_end && ((j - j_begin) & 1)) idle_step(j++, Buf1{});
+      for (; j + 1 < j_end; j += 2) {
+        idle_step(j, Buf0{});
+        idle_step(j + 1, Buf1{});
+      }
+      if (j < j_end) idle_step(j, Buf0{});
+      return;
+    }
+  }
   run(std::false_type{}, j_begin, n_full);
   run(std::true_type{}, max(j_begin, n_full), j_end);
 
@@ -886,6 +948,65 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Query-tile mix of the 12-wave decode for n rows per (batch, head), nb (batch, head) entries
+// per XCD and cx CUs per XCD.  Candidates: n2 tiles of 256 rows (0..4) and n1 of 128 rows (0..1)
+// after as many 384-row tiles as the rest needs, no tile without rows.  Each is priced by a list
+// schedule of the XCD's tiles in launch order on cx CUs (a free CU takes the next tile), a tile
+// costing the step time of its busiest SIMD: 1, 0.755 and 0.60 for 3, 2 and 1 waves with rows
+// (measured over 12,400 keys), plus 0.01 for its prologue and epilogue.  The shortest schedule
+// wins, ties to the fewer tiles.  The last query is cached per thread.
+void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
+  thread_local int key[3] = {-1, -1, -1};
+  thread_local int32_t last[3] = {0, 0, 0};
+  if (key[0] == n && key[1] == nb && key[2] == cx) {
+    mix[0] = last[0], mix[1] = last[1], mix[2] = last[2];
+    return;
+  }
+  const int quarters = (n + 127) / 128;
+  auto tile_cost = [&](int row0, int rows) {
+    const int live = std::min(rows, n - row0);
+    const int waves = (live + 31) / 32;
+    const int busiest = (waves + 3) / 4;
+    return (busiest >= 3 ? 1.0 : busiest == 2 ? 0.755 : 0.60) + 0.01;
+  };
+  std::vector<double> loads((size_t)cx);
+  double best = 0.0;
+  int32_t pick[3] = {(n + 383) / 384, 0, 0};
+  bool have = false;
+  for (int n2 = 0; n2 <= 4; ++n2)
+    for (int n1 = 0; n1 <= 1; ++n1) {
+      const int n3 = std::max(0, (quarters - 2 * n2 - n1 + 2) / 3);
+      const int covered = 384 * n3 + 256 * n2 + 128 * n1;
+      const int last_rows = n1 ? 128 : n2 ? 256 : 384;
+      if (n3 + n2 + n1 == 0 || covered < n || covered - last_rows >= n) continue;
+      std::fill(loads.begin(), loads.end(), 0.0);
+      std::priority_queue<double, std::vector<double>, std::greater<double>> free_at(
+          loads.begin(), loads.end());
+      double span = 0.0;
+      auto take = [&](double c) {
+        const double t = free_at.top() + c;
+        free_at.pop();
+        free_at.push(t);
+        span = std::max(span, t);
+      };
+      const int counts[3] = {n3, n2, n1}, heights[3] = {384, 256, 128};
+      int base = 0;
+      for (int k = 0; k < 3; ++k) {
+        for (int e = 0; e < nb; ++e)
+          for (int t = 0; t < counts[k]; ++t) take(tile_cost(base + heights[k] * t, heights[k]));
+        base += heights[k] * counts[k];
+      }
+      if (!have || span < best - 1e-9) {
+        best = span;
+        pick[0] = n3, pick[1] = n2, pick[2] = n1;
+        have = true;
+      }
+    }
+  mix[0] = pick[0], mix[1] = pick[1], mix[2] = pick[2];
+  key[0] = n, key[1] = nb, key[2] = cx;
+  last[0] = pick[0], last[1] = pick[1], last[2] = pick[2];
+}
+
 hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   AttnArgs a = args;
   const int n_split = a.n_split > 1 ? a.n_split : 1;
@@ -896,6 +1017,12 @@ hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   };
   auto launch = [&](auto kernel, int waves) {
     a.n_qtiles = tiles(waves);
+    a.mix[0] = a.mix[1] = a.mix[2] = 0;
+    const int cus = device_cus();
+    if (waves == kDecodeDirectWaves && heads % 8 == 0 && cus % 8 == 0) {
+      decode_mix(a.n_q, (int)(heads / 8), cus / 8, a.mix);
+      a.n_qtiles = a.mix[0] + a.mix[1] + a.mix[2];
+    }
     const dim3 grid((unsigned)(a.n_qtiles * heads));
     hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream, a);
   };

@@ -98,6 +98,11 @@ struct AttnArgs {
   int32_t split_units;
   float* part_o;
   float* part_ml;
+  // Decode, 12-wave kernel: query tiles per (batch, head) of 384, 256 and 128 rows (mix[0..2]),
+  // laid out along the rows in that order.  Each XCD takes the tiles of its own (batch, head)
+  // entries, all 384-row tiles first, then the 256-row ones, then the 128-row ones.  mix[0] == 0:
+  // every tile 384 rows, (batch, head)-major (launch_decode fills it in).
+  int32_t mix[3];
 };
 
 // Q/K prologue: RMS-normalise each 128-value head row of q and k (weights wq, wk), rotate its

@@ -320,6 +320,48 @@ def test_decode_workgroup_widths_agree_bitwise():
     assert torch.equal(both[:1], one)
 
 
+# Query-tile mixes of the 12-wave decode, as the launch picks them on 256 CUs: per (batch, head),
+# tiles of 384, then 256, then 128 rows; each XCD runs its 384-row tiles first.
+MIX_CASES = [
+    (4000, 2, 32),  # 8 x 384 + 4 x 256 (the last one 160 rows)
+    (3356, 2, 32),  # 6 x 384 + 4 x 256 + 1 x 128
+    (3615, 2, 32),  # 8 x 384 + 2 x 256 + 1 x 128
+    (777, 4, 64),   # 1 x 384 + 2 x 256
+    (8192, 2, 32),  # 20 x 384 + 2 x 256
+]
+
+
+@pytest.mark.parametrize("N,B,H", MIX_CASES)
+def test_decode_tile_mix(N, B, H):
+    """Decode grids large enough for 12-wave workgroups, whose query tiles then come in several
+    heights: every output is bitwise the 4-wave decode's (run on 8-head slices, whose grids are
+    small), and two heads are checked against the oracle on sampled rows, including every tile's
+    first and last row."""
+    P = 300
+    ids = np.r_[np.full(40, -1), np.zeros(P - 40), np.ones(N)].astype(np.int32)
+    plan = bca.Plan(ids)
+    assert (plan.info.prefix_len, plan.info.target_len) == (P, N)
+    rng = np.random.default_rng(9000 + N)
+    kcb, vcb = (W.draw_bf16(rng, (B, P, H, 128), scaled=False) for _ in range(2))
+    qt, kt, vt = (W.draw_bf16(rng, (B, N, H, 128), scaled=False) for _ in range(3))
+    say(f"case: decode tile mix N={N} B={B} H={H}")
+    kc, vc, q, k, v = (to_dev(x) for x in (kcb, vcb, qt, kt, vt))
+    o = bca.decode(plan, q, kc, vc, k, v)
+    torch.cuda.synchronize()
+    for h0 in range(0, H, 8):
+        sl = slice(h0, h0 + 8)
+        o8 = bca.decode(plan, q[:, :, sl], kc[:, :, sl], vc[:, :, sl], k[:, :, sl], v[:, :, sl])
+        torch.cuda.synchronize()
+        assert torch.equal(o8, o[:, :, sl]), f"heads {h0}..{h0 + 7}"
+    edges = [r for t in range(0, N, 128) for r in (t, t + 127)]
+    rows = np.unique(np.clip(np.r_[np.arange(0, N, 7), edges, N - 1], 0, N - 1))
+    heads = [0, H - 1]
+    got = o[:, torch.from_numpy(rows).to(DEV)][:, :, heads].cpu().numpy()
+    ref = O.decode(f32(qt[:, :, heads]), f32(kcb[:, :, heads]), f32(vcb[:, :, heads]),
+                   f32(kt[:, :, heads]), f32(vt[:, :, heads]), rows=rows)
+    check(got, ref, "decode tile mix vs oracle")
+
+
 def test_max_extent_strided():
     """K/V at the ABI's extent limit: rows * stride_s just below 2^31 elements (4 GiB of bf16 per
     tensor), through views with stride_s = 16,384 into padded buffers (one head of 128 values per
