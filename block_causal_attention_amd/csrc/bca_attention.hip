@@ -117,22 +117,21 @@ __device__ inline float halves_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
 }
 
-// FP8 prefix cache (E4M3, one fp32 scale per (token, head) row; the exact rule is in bca.h).
-// dequant turns {8 code bytes of a row, its scale bits, 0} into the 8 bf16 values
-// E4M3(code) * scale that the LDS tile holds.
+// FP8 prefix cache (E4M3, one fp32 scale per (token, head) row, a power of two; the exact rule is
+// in bca.h).  dequant turns {8 code bytes of a row, its scale bits, 0} into the 8 bf16 values
+// E4M3(code) * scale that the LDS tile holds: v_cvt_scalef32_pk_bf16_fp8 forms each pair exactly
+// (a power-of-two scale only moves the exponent).
 __device__ inline u32x4 dequant(u32x4 x) {
   // (the element goes through a scalar first: hipcc lowers a bit_cast of an ext_vector element
   // operand to a cast of element 0)
   const uint32_t sc_bits = x[2];
   const float sc = __builtin_bit_cast(float, sc_bits);
-  const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], false);  // bytes 0, 1
-  const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], true);   // bytes 2, 3
-  const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], false);
-  const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], true);
-  const bf16x8 r = {(__bf16)(p0[0] * sc), (__bf16)(p0[1] * sc), (__bf16)(p1[0] * sc),
-                    (__bf16)(p1[1] * sc), (__bf16)(p2[0] * sc), (__bf16)(p2[1] * sc),
-                    (__bf16)(p3[0] * sc), (__bf16)(p3[1] * sc)};
-  return __builtin_bit_cast(u32x4, r);
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[0], sc, false);  // bytes 0, 1
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[0], sc, true);   // bytes 2, 3
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[1], sc, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[1], sc, true);
+  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+               __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
 }
 
 // The body of all the kernels.  kBlockN keys per key tile and kW waves per workgroup are chosen

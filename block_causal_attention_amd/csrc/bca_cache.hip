@@ -4,9 +4,10 @@
 //     kernel itself stores only the cache's bf16 tensors: quantising inside its key-tile loop
 //     cost the loop registers it needs for its operand reads.
 //   cache_dequant: a cache written back as bf16, once per layer, so that the cached step can run
-//     the bf16 decode.  The value of a code is its E4M3 value times the row scale, formed in fp32
-//     and rounded to bf16 (RNE): the same rule the decode applies when it turns the codes into
-//     its bf16 tiles in LDS, so both paths see bitwise the same K and V.
+//     the bf16 decode.  The value of a code is its E4M3 value times the row scale, a power of two,
+//     which v_cvt_scalef32_pk_bf16_fp8 forms exactly (rounded to nearest even only below bf16's
+//     normal range): the instruction the decode uses when it turns the codes into its bf16 tiles
+//     in LDS, so both paths see bitwise the same K and V.
 // Sixteen lanes per 128-value row, eight values per lane.  HBM-bound.
 #include "bca_internal.h"
 
@@ -18,14 +19,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline u32x4 expand8(u32x2 c, float sc) {
-  const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[0], false);  // bytes 0, 1
-  const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[0], true);   // bytes 2, 3
-  const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[1], false);
-  const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[1], true);
-  const bf16x8 r = {(__bf16)(p0[0] * sc), (__bf16)(p0[1] * sc), (__bf16)(p1[0] * sc),
-                    (__bf16)(p1[1] * sc), (__bf16)(p2[0] * sc), (__bf16)(p2[1] * sc),
-                    (__bf16)(p3[0] * sc), (__bf16)(p3[1] * sc)};
-  return __builtin_bit_cast(u32x4, r);
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], sc, false);  // bytes 0, 1
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], sc, true);   // bytes 2, 3
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], sc, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], sc, true);
+  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+               __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
 }
 
 // One tensor's chunk of row (b, p, h): 8 values at dims d0 .. d0 + 7.
@@ -42,9 +41,10 @@ __device__ inline u32x4 load8(const void* base, int64_t sb, int64_t ss, int64_t 
 }
 
 // Quantises this lane's 8 bf16 values of a 128-wide row held by 16 consecutive lanes (8 values
-// each): the row's amax comes from a 16-lane max, scale = max(amax / 448, 2^-126) (1 if amax is
-// 0) and codes = E4M3(x * (1 / scale)), all divisions correctly rounded and the conversion
-// round-to-nearest-even.  Returns the 8 codes; *scale_out gets the row scale.
+// each): the row's amax comes from a 16-lane max; the scale is 2^k, the smallest power of two
+// with amax <= 448 * 2^k and k >= -126 (1 if amax is 0), and codes = E4M3(x * 2^-k), the product
+// exact and the conversion round-to-nearest-even.  Returns the 8 codes; *scale_out gets the row
+// scale.
 __device__ inline u32x2 quantize_row8(u32x4 x, float* scale_out) {
   const bf16x8 xb = __builtin_bit_cast(bf16x8, x);
   float f[8];
@@ -56,8 +56,14 @@ __device__ inline u32x2 quantize_row8(u32x4 x, float* scale_out) {
   }
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  const float scale = amax > 0.0f ? fmaxf(amax / 448.0f, 0x1p-126f) : 1.0f;
-  const float inv = 1.0f / scale;
+  // amax = 1.m * 2^e: 448 = 1.75 * 2^8, so k = e - 8, or e - 7 when 1.m > 1.75 (a subnormal
+  // amax, exponent field 0, takes the floor)
+  const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
+  const int e = (int)(bits >> 23) - 127;
+  int k = e - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  k = (bits >> 23) == 0 ? -126 : max(k, -126);
+  const float scale = amax > 0.0f ? __builtin_bit_cast(float, (uint32_t)(k + 127) << 23) : 1.0f;
+  const float inv = amax > 0.0f ? __builtin_bit_cast(float, (uint32_t)(127 - k) << 23) : 1.0f;
   int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv, f[1] * inv, 0, false);
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv, f[3] * inv, w0, true);
   int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * inv, f[5] * inv, 0, false);

@@ -149,8 +149,8 @@ struct DequantArgs {
 
 // Cache quantisation: prefix rows [0, P) of bf16 K and V [B, S, H, D] written as E4M3 codes
 // [B, P, H, D] plus one fp32 scale per (b, p, h) for each tensor with a code pointer (ko, vo;
-// NULL: that tensor is not quantised).  The rule is the cache format's (scale = max(amax / 448,
-// 2^-126), 1 for an all-zero row; codes = E4M3(x * (1 / scale)), RNE).
+// NULL: that tensor is not quantised).  The rule is the cache format's (scale = the smallest power
+// of two 2^k >= amax / 448 with k >= -126, 1 for an all-zero row; codes = E4M3(x * 2^-k), RNE).
 struct QuantArgs {
   const uint16_t* k;
   int64_t k_sb, k_ss, k_sh;

@@ -236,11 +236,13 @@ bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
  * (OCP E4M3FN: bias 7, largest finite 448, subnormals, no infinities, 0x7F/0xFF = NaN) plus an
  * fp32 scale tensor [B, P, H].  For each (b, j, h) row x of D values:
  *     amax  = max_d |x[d]|
- *     scale = amax > 0 ? max(amax / 448, 2^-126) : 1          (fp32, correctly rounded)
- *     inv   = 1 / scale                                        (fp32, correctly rounded)
- *     code[d] = E4M3(x[d] * inv)   (fp32 product, then nearest E4M3 value, ties to even)
- * and the value the decode uses is E4M3 value(code[d]) * scale, rounded to bf16.  Inputs must be
- * finite.
+ *     scale = 2^k, the smallest power of two with amax <= 448 * 2^k and k >= -126; 1 if amax = 0
+ *     code[d] = E4M3(x[d] * 2^-k)  (an exact fp32 product, then the nearest E4M3 value, ties to
+ *                                   even; it never exceeds 448)
+ * and the value the decode uses is E4M3 value(code[d]) * scale, which bf16 holds exactly (down to
+ * bf16's smallest normal number; below it, rounded to nearest even).  The row's largest value
+ * lands in E4M3's top binade, so the power-of-two scale costs no relative precision.  Inputs must
+ * be finite.
  *
  * Layout rules on top of the general ones: code tensors follow the bf16 rules with 1-byte
  * elements (data 16-byte aligned, strides non-negative multiples of 16); scale tensors are fp32

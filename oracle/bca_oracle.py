@@ -296,11 +296,11 @@ def prefix_cache_bytes(layers: int, batch: int, prefix_len: int, heads: int, hea
 # token and per attention head; quantising only V saves about 25% of the cache and is the safer
 # trade (K carries RoPE and drives the attention weights).  Readings: E4M3 is the OCP "E4M3FN"
 # encoding (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
-# S.1111.111 = NaN, largest finite 448); the scale of a (token, head) row is amax(|x|) / 448
-# computed in fp32, floored at the smallest normal fp32 number (1 for an all-zero row); a row is
-# quantised as x * (1 / scale) in fp32 and rounded to the nearest E4M3 value, ties to the even
-# code, saturating at +-448 (never reached: |x * (1 / scale)| exceeds 448 by a few fp32 ulps at
-# most).
+# S.1111.111 = NaN, largest finite 448); the scale of a (token, head) row is the smallest power of
+# two 2^k with amax(|x|) <= 448 * 2^k, k >= -126 (the smallest normal fp32 number; 1 for an
+# all-zero row), so the row's largest value lands in E4M3's top binade; a row is quantised as
+# x * 2^-k (exact in fp32) rounded to the nearest E4M3 value, ties to the even code (|x| * 2^-k
+# never exceeds 448); a stored value is E4M3(code) * 2^k, exact.
 
 E4M3_MAX = 448.0
 SCALE_FLOOR = 2.0 ** -126  # smallest normal fp32 number
@@ -346,24 +346,38 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
+def fp8_row_scale(amax: np.ndarray) -> np.ndarray:
+    """The scale of rows with these amax values: the smallest power of two 2^k with
+    amax <= 448 * 2^k, at least 2^-126; 1 for amax = 0.  float32."""
+    a = np.asarray(amax, dtype=np.float64)
+    k = np.zeros(a.shape, dtype=np.int64)
+    pos = a > 0
+    k[pos] = np.ceil(np.log2(a[pos] / E4M3_MAX)).astype(np.int64)
+    # log2 may land one off next to a power of two: settle k by exact comparisons
+    for _ in range(2):
+        k = np.where(pos & (a > E4M3_MAX * np.exp2(k.astype(np.float64))), k + 1, k)
+        k = np.where(pos & (a <= E4M3_MAX * np.exp2((k - 1).astype(np.float64))), k - 1, k)
+    k = np.where(pos, np.maximum(k, int(np.log2(SCALE_FLOOR))), 0)
+    return np.exp2(k.astype(np.float64)).astype(np.float32)
+
+
 def quantize_fp8_rows(x: np.ndarray):
-    """Per-row (last axis) FP8 quantisation in the precision the method fixes (fp32 scales).
+    """Per-row (last axis) FP8 quantisation with fp32 scales, as the method fixes them.
 
     Returns (codes uint8 like x, scales float32 of x.shape[:-1])."""
     xf = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(xf), axis=-1)
-    # Reading: the scale is amax / 448 kept at or above the smallest normal fp32 number, so that
-    # its reciprocal stays finite for rows of tiny values (it only bites below amax ~ 2^-117);
-    # an all-zero row takes scale 1.
-    scale = np.maximum(amax / np.float32(E4M3_MAX), np.float32(SCALE_FLOOR))
-    scale = np.where(amax > 0, scale, np.float32(1.0)).astype(np.float32)
+    # Reading: one power-of-two scale per row, the smallest that keeps the row within E4M3's
+    # range (its largest value then uses E4M3's top binade, so no relative precision is lost),
+    # floored at the smallest normal fp32 number; x * 2^-k is exact.
+    scale = fp8_row_scale(amax)
     inv = (np.float32(1.0) / scale).astype(np.float32)
     q = (xf * inv[..., None]).astype(np.float32)
     return e4m3_encode(q), scale
 
 
 def dequantize_fp8_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """code value * scale, exact in float64."""
+    """code value * scale, exact in float64 (and in bf16 down to bf16's smallest normal)."""
     return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
 
 

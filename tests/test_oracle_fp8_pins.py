@@ -73,15 +73,30 @@ def test_e4m3_encoder():
     check_encoder(O.e4m3_encode, O.e4m3_value_table())
 
 
+def brute_scale(amax):
+    """The smallest power of two 2^k, k >= -126, with amax <= 448 * 2^k, by a search in exact
+    rational arithmetic (1 for amax = 0)."""
+    from fractions import Fraction
+    a = Fraction(float(amax))
+    if a == 0:
+        return 1.0
+    k = -126
+    while a > 448 * Fraction(2) ** k:
+        k += 1
+    return float(Fraction(2) ** k)
+
+
 def test_quantize_rows_error_bound_and_scale():
     rng = np.random.default_rng(4)
     x = W.bf16_bits_to_f32(W.draw_bf16(rng, (3, 50, 2, 128), scaled=False))
     codes, scales = O.quantize_fp8_rows(x)
     assert scales.dtype == np.float32 and scales.shape == (3, 50, 2)
     amax = np.abs(x).max(axis=-1)
-    np.testing.assert_array_equal(scales, (amax / np.float32(448)).astype(np.float32))
-    # the element that attains amax lands on the largest code
-    assert (O.e4m3_decode(codes).__abs__().max(axis=-1) == 448.0).all()
+    want = np.array([brute_scale(a) for a in amax.ravel()], np.float32).reshape(amax.shape)
+    np.testing.assert_array_equal(scales, want)
+    # the element that attains amax lands in E4M3's top binade: no range is wasted
+    top = O.e4m3_decode(codes).__abs__().max(axis=-1)
+    assert ((top >= 224.0) & (top <= 448.0)).all()
     back = O.dequantize_fp8_rows(codes, scales)
     # 3 mantissa bits: half an ulp is 1/16 relative for normal values; subnormal steps are
     # 2^-9 * scale absolute
@@ -175,16 +190,40 @@ def test_quantize_tiny_rows_keep_a_normal_scale():
     code is NaN, and every value comes back within half a step of the coarsest grid."""
     x = np.zeros((4, 128), np.float32)
     x[0, :3] = [2.0 ** -130, -2.0 ** -128, 2.0 ** -133]      # bf16 subnormals
-    x[1, 5] = 2.0 ** -118                                    # amax / 448 just below 2^-126
+    x[1, 5] = 2.0 ** -118                                    # amax / 448 = 2^-126.8
     x[2, 7] = 448 * 2.0 ** -126                              # exactly at the floor
     x[3, :] = 2.0 ** -100                                    # well above it
     codes, scales = O.quantize_fp8_rows(x)
     assert (scales >= np.float32(2.0 ** -126)).all()
     assert np.isfinite(np.float32(1) / scales).all()
     assert not np.isnan(O.e4m3_decode(codes)).any()
-    assert scales[2] == np.float32(2.0 ** -126) and scales[3] == np.float32(2.0 ** -100 / 448)
+    assert scales[1] == np.float32(2.0 ** -126) and scales[2] == np.float32(2.0 ** -126)
+    assert scales[3] == np.float32(2.0 ** -108)              # 2^-100 / 448 = 2^-108.8
     back = O.dequantize_fp8_rows(codes, scales)
     step = 2.0 ** -9 * scales[:, None].astype(np.float64)    # finest E4M3 step times the scale
     assert (np.abs(back - x) <= np.maximum(np.abs(x) / 16, step / 2)).all()
     nz = back != 0
     assert (np.sign(back[nz]) == np.sign(x[nz])).all()
+
+
+@pytest.mark.parametrize("amax", [448.0, 448.0 * 2.0 ** 5, 448.0 * 2.0 ** -7, np.nextafter(448.0, 1e9),
+                                  np.nextafter(448.0, 0), 224.0, 224.5, 1.0, 7.0, 3.0e38,
+                                  2.0 ** -118, 2.0 ** -133, 448 * 2.0 ** -126, 0.0])
+def test_scale_is_the_smallest_power_of_two_in_range(amax):
+    """Edge amax values: exactly 448 times a power of two, one fp32 ulp either side of one, the
+    top of the fp32 range, values at and below the floor, zero."""
+    a = np.float32(amax)
+    got = O.fp8_row_scale(np.array([a]))[0]
+    assert got == np.float32(brute_scale(a))
+    if a > 448 * 2.0 ** -126:
+        assert 224 < float(a) / float(got) <= 448            # the top binade of E4M3
+
+
+def test_planted_scale_mistake_is_caught():
+    """A scale one power of two too large (amax / 448 rounded up twice) fails the scale pin."""
+    rng = np.random.default_rng(8)
+    amax = np.abs(rng.normal(0, 3, 200)).astype(np.float32)
+    wrong = (O.fp8_row_scale(amax) * 2).astype(np.float32)
+    want = np.array([brute_scale(a) for a in amax], np.float32)
+    assert not np.array_equal(wrong, want)
+    np.testing.assert_array_equal(O.fp8_row_scale(amax), want)
