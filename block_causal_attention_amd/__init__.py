@@ -27,7 +27,7 @@ from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
            "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen",
            "decode_split", "split_workspace", "dequantize_cache", "decode_split_noalloc",
-           "decode_varlen"]
+           "decode_varlen", "decode_layout"]
 
 
 class BcaError(RuntimeError):
@@ -493,6 +493,15 @@ def decode_varlen(plan: Plan, q, k_cache, v_cache, k, v, *, scale: Optional[floa
             ctypes.byref(_desc3(v, "v", torch.bfloat16)),
             ctypes.byref(_desc3(out, "out", torch.float32)), ctypes.c_void_p(stream)))
     return out
+
+
+def decode_layout(n_q: int, groups: int, cus: int = 0):
+    """(waves, tiles of 384, 256 and 128 rows per group) of a cached step with n_q query rows per
+    group and `groups` (batch, head, key range) groups on `cus` compute units (0: the current
+    device's) (bca_decode_layout)."""
+    out = (ctypes.c_int32 * 4)()
+    _check(_lib.load().bca_decode_layout(n_q, groups, cus, out))
+    return tuple(out)
 
 
 def split_workspace(plan: Plan, batch: int, heads: int, n_split: int = 0):

@@ -890,6 +890,14 @@ void attn_decode_direct(const AttnArgs a) {
   attn_fwd<true, kFmt, kDecodeDirectBlockN, kW>(a);
 }
 
+// Library-owned device scratch for the allocation-free split decode (bca_decode_split_noalloc):
+// the partial O, m and l of its key ranges.  One copy per GPU the library runs on, held until the
+// process ends; every call on a GPU shares it.  In host code the array's name is only a
+// stand-in: its device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) static unsigned char scratch[kScratchBytes];
+
+}  // namespace
+
 // Compute units of the current device (cached per device).
 int device_cus() {
   static std::atomic<int> cache[64];
@@ -906,15 +914,6 @@ int device_cus() {
   if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
-
-
-// Library-owned device scratch for the allocation-free split decode (bca_decode_split_noalloc):
-// the partial O, m and l of its key ranges.  One copy per GPU the library runs on, held until the
-// process ends; every call on a GPU shares it.  In host code the array's name is only a
-// stand-in: its device address comes from hipGetSymbolAddress, once per device.
-__device__ __align__(256) static unsigned char scratch[kScratchBytes];
-
-}  // namespace
 
 hipError_t scratch_memory(void** out) {
   constexpr int kMaxDevices = 64;
@@ -951,9 +950,10 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
 // per XCD and cx CUs per XCD.  Candidates: n2 tiles of 256 rows (0..4) and n1 of 128 rows (0..1)
 // after as many 384-row tiles as the rest needs, no tile without rows.  Each is priced by a list
 // schedule of the XCD's tiles in launch order on cx CUs (a free CU takes the next tile), a tile
-// costing the step time of its busiest SIMD: 1, 0.755 and 0.60 for 3, 2 and 1 waves with rows
-// (measured over 12,400 keys), plus 0.01 for its prologue and epilogue.  The shortest schedule
-// wins, ties to the fewer tiles.  The last query is cached per thread.
+// costing the step time of its busiest SIMD: 1, 0.88 and 0.66 for 3, 2 and 1 waves with rows
+// (measured on the CFG cached step, 12,400 keys, whose query tiles share each K/V tile in L2),
+// plus 0.01 for its prologue and epilogue.  The shortest schedule wins; a tie keeps the earlier
+// candidate (fewer 256-row, then fewer 128-row tiles).  The last query is cached per thread.
 void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
   thread_local int key[3] = {-1, -1, -1};
   thread_local int32_t last[3] = {0, 0, 0};
@@ -966,7 +966,7 @@ void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
     const int live = std::min(rows, n - row0);
     const int waves = (live + 31) / 32;
     const int busiest = (waves + 3) / 4;
-    return (busiest >= 3 ? 1.0 : busiest == 2 ? 0.755 : 0.60) + 0.01;
+    return (busiest >= 3 ? 1.0 : busiest == 2 ? 0.88 : 0.66) + 0.01;
   };
   std::vector<double> loads((size_t)cx);
   double best = 0.0;
@@ -1006,30 +1006,42 @@ void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
   last[0] = pick[0], last[1] = pick[1], last[2] = pick[2];
 }
 
+DecodeLayout decode_layout(int64_t n_q, int64_t groups, int cus) {
+  DecodeLayout l{};
+  auto tiles = [&](int waves) {
+    const int64_t rows = 32 * kQueryBlocks * waves;
+    return (n_q + rows - 1) / rows;
+  };
+  // the wider workgroup where its grid gives every CU at least two, else the narrower one
+  if (tiles(kDecodeDirectWaves) * groups >= 2 * (int64_t)cus) {
+    l.waves = kDecodeDirectWaves;
+    if (groups % 8 == 0 && cus % 8 == 0) {
+      decode_mix((int)n_q, (int)(groups / 8), cus / 8, l.tiles);
+      l.mixed = true;
+    } else {
+      l.tiles[0] = (int32_t)tiles(kDecodeDirectWaves);
+    }
+  } else {
+    l.waves = kDecodeDirectSmallWaves;
+    l.tiles[2] = (int32_t)tiles(kDecodeDirectSmallWaves);
+  }
+  return l;
+}
+
 hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   AttnArgs a = args;
   const int n_split = a.n_split > 1 ? a.n_split : 1;
   const int64_t heads = (int64_t)a.batch * a.heads * n_split;
-  auto tiles = [&](int waves) {
-    const int rows = 32 * kQueryBlocks * waves;
-    return (a.n_q + rows - 1) / rows;
-  };
+  const DecodeLayout l = decode_layout(a.n_q, heads, device_cus());
+  a.n_qtiles = l.tiles[0] + l.tiles[1] + l.tiles[2];
+  for (int i = 0; i < 3; ++i) a.mix[i] = l.mixed ? l.tiles[i] : 0;
   auto launch = [&](auto kernel, int waves) {
-    a.n_qtiles = tiles(waves);
-    a.mix[0] = a.mix[1] = a.mix[2] = 0;
-    const int cus = device_cus();
-    if (waves == kDecodeDirectWaves && heads % 8 == 0 && cus % 8 == 0) {
-      decode_mix(a.n_q, (int)(heads / 8), cus / 8, a.mix);
-      a.n_qtiles = a.mix[0] + a.mix[1] + a.mix[2];
-    }
     const dim3 grid((unsigned)(a.n_qtiles * heads));
     hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream, a);
   };
-  // the wider workgroup where its grid gives every CU at least two, else the narrower one
-  auto wide = [&](int waves) { return tiles(waves) * heads >= 2 * (int64_t)device_cus(); };
   auto direct = [&](auto fmt_c) {
     constexpr int kF = decltype(fmt_c)::value;
-    if (wide(kDecodeDirectWaves))
+    if (l.waves == kDecodeDirectWaves)
       launch(attn_decode_direct<kF, kDecodeDirectWaves>, kDecodeDirectWaves);
     else
       launch(attn_decode_direct<kF, kDecodeDirectSmallWaves>, kDecodeDirectSmallWaves);

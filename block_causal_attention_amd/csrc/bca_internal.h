@@ -181,4 +181,18 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 
+// Launch shape of the decode: n_q query rows per group, `groups` (batch, head, key range) groups,
+// on a device of `cus` compute units.  waves: 12 where the 384-row grid gives every CU at least
+// two workgroups, else 4.  tiles: query tiles per group of 384, 256 and 128 rows, laid along the
+// rows in that order.  12 waves: the mix decode_mix picks when groups and cus are multiples of the
+// 8 XCDs (mixed = true), else {ceil(n_q / 384), 0, 0}; 4 waves: {0, 0, ceil(n_q / 128)}.
+struct DecodeLayout {
+  int waves;
+  int32_t tiles[3];
+  bool mixed;
+};
+DecodeLayout decode_layout(int64_t n_q, int64_t groups, int cus);
+// Compute units of the current device (256 where the runtime cannot tell).
+int device_cus();
+
 }  // namespace bca

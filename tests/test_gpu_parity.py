@@ -320,13 +320,13 @@ def test_decode_workgroup_widths_agree_bitwise():
     assert torch.equal(both[:1], one)
 
 
-# Query-tile mixes of the 12-wave decode, as the launch picks them on 256 CUs: per (batch, head),
-# tiles of 384, then 256, then 128 rows; each XCD runs its 384-row tiles first.
+# Query-tile mixes of the 12-wave decode, as the launch picks them on 256 CUs (bca_decode_layout):
+# per (batch, head), tiles of 384, then 256, then 128 rows; each XCD runs its 384-row tiles first.
 MIX_CASES = [
     (4000, 2, 32),  # 8 x 384 + 4 x 256 (the last one 160 rows)
     (3356, 2, 32),  # 6 x 384 + 4 x 256 + 1 x 128
     (3615, 2, 32),  # 8 x 384 + 2 x 256 + 1 x 128
-    (777, 4, 64),   # 1 x 384 + 2 x 256
+    (777, 4, 64),   # 2 x 384 + 1 x 128
     (8192, 2, 32),  # 20 x 384 + 2 x 256
 ]
 
@@ -344,7 +344,7 @@ def test_decode_tile_mix(N, B, H):
     rng = np.random.default_rng(9000 + N)
     kcb, vcb = (W.draw_bf16(rng, (B, P, H, 128), scaled=False) for _ in range(2))
     qt, kt, vt = (W.draw_bf16(rng, (B, N, H, 128), scaled=False) for _ in range(3))
-    say(f"case: decode tile mix N={N} B={B} H={H}")
+    say(f"case: decode tile mix N={N} B={B} H={H} layout={bca.decode_layout(N, B * H)}")
     kc, vc, q, k, v = (to_dev(x) for x in (kcb, vcb, qt, kt, vt))
     o = bca.decode(plan, q, kc, vc, k, v)
     torch.cuda.synchronize()
