@@ -356,6 +356,30 @@ def split_decode_timing(torch, bca, W, dev, iters=20):
     return out
 
 
+def decode_b1_timing(torch, bca, plan, kc2, vc2, sets, N, H, S, dev, iters=20):
+    """The cached step without CFG (one branch, B = 1; the pages' production default of guidance
+    scale 1): batch item 0 of the CFG pair's cache and of the first target set."""
+    kc1, vc1 = kc2[:1].contiguous(), vc2[:1].contiguous()
+    qt, kt, vt = (x[:1].contiguous() for x in sets[0])
+    o = torch.empty((1, N, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    fn = lambda: bca.decode(plan, qt, kc1, vc1, kt, vt, out=o)
+    settle(torch, fn, SETTLE["extra_ms"])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    flops = 4.0 * HEAD_DIM * H * N * S
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"cached step without CFG (B=1): {ms:.4f} ms = {tf:.1f} TFLOP/s")
+    return {"workload": f"one cached step without CFG: B=1, N={N} over {S} keys, H={H}, "
+                        f"launch {list(bca.decode_layout(N, H))}",
+            "ms": round(ms, 4), "useful_tflops": round(tf, 2),
+            "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "useful_gflop": round(flops / 1e9, 1)}
+
+
 def prefill_timing(torch, bca, W, name, dev, iters=10):
     """One prefill shape on its own (B = 1, H = 32, writing its prefix cache): ms per call (mean
     and median of event-timed calls) and useful TFLOP/s from the median."""
@@ -600,9 +624,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(key), "kernel": dom}
 
-    prologue = varlen = split = gen = pre_c2 = pre_c5 = cfg = None
+    prologue = varlen = split = gen = pre_c2 = pre_c5 = cfg = dec_b1 = None
     if not args.no_extras:
         gen = decode_generation_timing(torch, bca, plan, kc2, vc2, od, Bd, N, H, flops_dec, dev)
+        dec_b1 = decode_b1_timing(torch, bca, plan, kc2, vc2, sets, N, H, S, dev)
         pre_c2 = prefill_timing(torch, bca, W, "t2i_1024", dev)
         pre_c5 = prefill_timing(torch, bca, W, "long_4ref", dev)
         prologue = prologue_timings(torch, bca, W, ids, Bd, S, N, H, dev)
@@ -640,6 +665,7 @@ def main():
         "plan_ms": round(plan_ms, 3),
         "plan_build": plan_split,
         "decode_49_steps": gen,
+        "decode_b1": dec_b1,
         "prefill_t2i_1024": pre_c2,
         "prefill_long_4ref": pre_c5,
         "mfma_utilisation": mfma_utilisation(),

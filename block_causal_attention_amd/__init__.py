@@ -495,12 +495,12 @@ def decode_varlen(plan: Plan, q, k_cache, v_cache, k, v, *, scale: Optional[floa
     return out
 
 
-def decode_layout(n_q: int, groups: int, cus: int = 0):
-    """(waves, tiles of 384, 256 and 128 rows per group) of a cached step with n_q query rows per
-    group and `groups` (batch, head, key range) groups on `cus` compute units (0: the current
-    device's) (bca_decode_layout)."""
+def decode_layout(n_q: int, batch_heads: int, n_split: int = 1, cus: int = 0):
+    """(waves, tiles of 384, 256 and 128 rows per (batch, head, key range)) of a cached step with
+    n_q query rows per (batch, head), batch_heads = B * H and n_split key ranges, on `cus` compute
+    units (0: the current device's) (bca_decode_layout)."""
     out = (ctypes.c_int32 * 4)()
-    _check(_lib.load().bca_decode_layout(n_q, groups, cus, out))
+    _check(_lib.load().bca_decode_layout(n_q, batch_heads, n_split, cus, out))
     return tuple(out)
 
 

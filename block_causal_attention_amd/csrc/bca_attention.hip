@@ -214,7 +214,7 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   int mix_row0 = 0, tile_rows = kRows;
   if constexpr (kMix) {
     mix_row0 = slot * kRows;
-    if (a.mix[0] > 0) {
+    if ((a.mix[0] | a.mix[1] | a.mix[2]) != 0) {
       // this XCD's bh_count / 8 (batch, head) entries (bh_count % 8 == 0 here)
       const int nb = bh_count >> 3;
       int l = blockIdx.x >> 3, hl;
@@ -947,20 +947,27 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
 }
 
 // Query-tile mix of the 12-wave decode for n rows per (batch, head), nb (batch, head) entries
-// per XCD and cx CUs per XCD.  Candidates: n2 tiles of 256 rows (0..4) and n1 of 128 rows (0..1)
+// per XCD and cx CUs per XCD.  Candidates: n2 tiles of 256 rows (0..16) and n1 of 128 rows (0..2)
 // after as many 384-row tiles as the rest needs, no tile without rows.  Each is priced by a list
 // schedule of the XCD's tiles in launch order on cx CUs (a free CU takes the next tile), a tile
 // costing the step time of its busiest SIMD: 1, 0.88 and 0.66 for 3, 2 and 1 waves with rows
 // (measured on the CFG cached step, 12,400 keys, whose query tiles share each K/V tile in L2),
-// plus 0.01 for its prologue and epilogue.  The shortest schedule wins; a tie keeps the earlier
-// candidate (fewer 256-row, then fewer 128-row tiles).  The last query is cached per thread.
+// plus 0.01 for its prologue and epilogue.  When 256- or 128-row tiles follow, every 384-row tile
+// is full and that phase is dealt in whole rounds (the first k3 % cx CUs take one tile more).
+// The shortest schedule wins; a tie keeps the earlier candidate (fewer 256-row, then fewer
+// 128-row tiles).  The last 8 queries are cached per thread.
 void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
-  thread_local int key[3] = {-1, -1, -1};
-  thread_local int32_t last[3] = {0, 0, 0};
-  if (key[0] == n && key[1] == nb && key[2] == cx) {
-    mix[0] = last[0], mix[1] = last[1], mix[2] = last[2];
-    return;
-  }
+  struct Entry {
+    int n, nb, cx;
+    int32_t m[3];
+  };
+  thread_local Entry cache[8];
+  thread_local int cached = 0, next = 0;
+  for (int i = 0; i < cached; ++i)
+    if (cache[i].n == n && cache[i].nb == nb && cache[i].cx == cx) {
+      mix[0] = cache[i].m[0], mix[1] = cache[i].m[1], mix[2] = cache[i].m[2];
+      return;
+    }
   const int quarters = (n + 127) / 128;
   auto tile_cost = [&](int row0, int rows) {
     const int live = std::min(rows, n - row0);
@@ -972,27 +979,33 @@ void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
   double best = 0.0;
   int32_t pick[3] = {(n + 383) / 384, 0, 0};
   bool have = false;
-  for (int n2 = 0; n2 <= 4; ++n2)
-    for (int n1 = 0; n1 <= 1; ++n1) {
+  for (int n2 = 0; n2 <= 16; ++n2)
+    for (int n1 = 0; n1 <= 2; ++n1) {
       const int n3 = std::max(0, (quarters - 2 * n2 - n1 + 2) / 3);
       const int covered = 384 * n3 + 256 * n2 + 128 * n1;
       const int last_rows = n1 ? 128 : n2 ? 256 : 384;
       if (n3 + n2 + n1 == 0 || covered < n || covered - last_rows >= n) continue;
+      const int counts[3] = {n3, n2, n1}, heights[3] = {384, 256, 128};
+      int k0 = 0;
       std::fill(loads.begin(), loads.end(), 0.0);
+      if (n2 + n1 > 0) {
+        const int64_t k3 = (int64_t)nb * n3;
+        const double c3 = tile_cost(0, 384);
+        for (int c = 0; c < cx; ++c) loads[(size_t)c] = (double)(k3 / cx + (c < k3 % cx)) * c3;
+        k0 = 1;
+      }
       std::priority_queue<double, std::vector<double>, std::greater<double>> free_at(
           loads.begin(), loads.end());
-      double span = 0.0;
-      auto take = [&](double c) {
-        const double t = free_at.top() + c;
-        free_at.pop();
-        free_at.push(t);
-        span = std::max(span, t);
-      };
-      const int counts[3] = {n3, n2, n1}, heights[3] = {384, 256, 128};
-      int base = 0;
-      for (int k = 0; k < 3; ++k) {
+      double span = *std::max_element(loads.begin(), loads.end());
+      int base = k0 ? 384 * n3 : 0;
+      for (int k = k0; k < 3; ++k) {
         for (int e = 0; e < nb; ++e)
-          for (int t = 0; t < counts[k]; ++t) take(tile_cost(base + heights[k] * t, heights[k]));
+          for (int t = 0; t < counts[k]; ++t) {
+            const double done = free_at.top() + tile_cost(base + heights[k] * t, heights[k]);
+            free_at.pop();
+            free_at.push(done);
+            span = std::max(span, done);
+          }
         base += heights[k] * counts[k];
       }
       if (!have || span < best - 1e-9) {
@@ -1002,29 +1015,34 @@ void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
       }
     }
   mix[0] = pick[0], mix[1] = pick[1], mix[2] = pick[2];
-  key[0] = n, key[1] = nb, key[2] = cx;
-  last[0] = pick[0], last[1] = pick[1], last[2] = pick[2];
+  cache[next] = Entry{n, nb, cx, {pick[0], pick[1], pick[2]}};
+  next = (next + 1) % 8;
+  cached = std::min(cached + 1, 8);
 }
 
-DecodeLayout decode_layout(int64_t n_q, int64_t groups, int cus) {
+DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus) {
   DecodeLayout l{};
   auto tiles = [&](int waves) {
     const int64_t rows = 32 * kQueryBlocks * waves;
     return (n_q + rows - 1) / rows;
   };
-  // the wider workgroup where its grid gives every CU at least two, else the narrower one
-  if (tiles(kDecodeDirectWaves) * groups >= 2 * (int64_t)cus) {
-    l.waves = kDecodeDirectWaves;
-    if (groups % 8 == 0 && cus % 8 == 0) {
+  const int64_t t12 = tiles(kDecodeDirectWaves);
+  if (n_split <= 1 && groups % 8 == 0 && cus % 8 == 0) {
+    // mixed tile heights: 12-wave workgroups once 384-row tiles would fill one round
+    if (t12 * groups >= (int64_t)cus) {
+      l.waves = kDecodeDirectWaves;
       decode_mix((int)n_q, (int)(groups / 8), cus / 8, l.tiles);
       l.mixed = true;
-    } else {
-      l.tiles[0] = (int32_t)tiles(kDecodeDirectWaves);
+      return l;
     }
-  } else {
-    l.waves = kDecodeDirectSmallWaves;
-    l.tiles[2] = (int32_t)tiles(kDecodeDirectSmallWaves);
+  } else if (t12 * groups * std::max(n_split, 1) >= 2 * (int64_t)cus) {
+    // 384-row tiles only: 12-wave workgroups where they give every CU at least two
+    l.waves = kDecodeDirectWaves;
+    l.tiles[0] = (int32_t)t12;
+    return l;
   }
+  l.waves = kDecodeDirectSmallWaves;
+  l.tiles[2] = (int32_t)tiles(kDecodeDirectSmallWaves);
   return l;
 }
 
@@ -1032,7 +1050,7 @@ hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   AttnArgs a = args;
   const int n_split = a.n_split > 1 ? a.n_split : 1;
   const int64_t heads = (int64_t)a.batch * a.heads * n_split;
-  const DecodeLayout l = decode_layout(a.n_q, heads, device_cus());
+  const DecodeLayout l = decode_layout(a.n_q, (int64_t)a.batch * a.heads, n_split, device_cus());
   a.n_qtiles = l.tiles[0] + l.tiles[1] + l.tiles[2];
   for (int i = 0; i < 3; ++i) a.mix[i] = l.mixed ? l.tiles[i] : 0;
   auto launch = [&](auto kernel, int waves) {

@@ -181,17 +181,19 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 
-// Launch shape of the decode: n_q query rows per group, `groups` (batch, head, key range) groups,
-// on a device of `cus` compute units.  waves: 12 where the 384-row grid gives every CU at least
-// two workgroups, else 4.  tiles: query tiles per group of 384, 256 and 128 rows, laid along the
-// rows in that order.  12 waves: the mix decode_mix picks when groups and cus are multiples of the
-// 8 XCDs (mixed = true), else {ceil(n_q / 384), 0, 0}; 4 waves: {0, 0, ceil(n_q / 128)}.
+// Launch shape of the decode: n_q query rows per (batch, head), `groups` = B * H, n_split key
+// ranges, on a device of `cus` compute units.  tiles: query tiles per (batch, head, key range) of
+// 384, 256 and 128 rows, laid along the rows in that order.
+//   Unsplit, groups and cus multiples of the 8 XCDs: 12-wave workgroups with the mix decode_mix
+//   picks (mixed = true) once 384-row tiles would fill one round of the CUs, else 4-wave ones.
+//   Otherwise: 12-wave workgroups in 384-row tiles {ceil(n_q / 384), 0, 0} where those give every
+//   CU at least two, else 4-wave ones.  4 waves: {0, 0, ceil(n_q / 128)}.
 struct DecodeLayout {
   int waves;
   int32_t tiles[3];
   bool mixed;
 };
-DecodeLayout decode_layout(int64_t n_q, int64_t groups, int cus);
+DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus);
 // Compute units of the current device (256 where the runtime cannot tell).
 int device_cus();
 

@@ -228,25 +228,28 @@ bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
 
 /*
  * bca_decode_layout -- HOST.  The launch shape the cached step (bca_decode, bca_decode_varlen,
- * bca_decode_ex, and each key range of a split decode) takes for n_q query rows per group and
- * `groups` groups (B * H, times the key ranges of a split decode; for bca_decode_varlen n_q is the
- * largest N_b) on a GPU of `cus` compute units (0 = the current device's, 256 where the runtime
- * cannot tell).  out[0] = waves per workgroup; out[1..3] = query tiles per group of 384, 256 and
- * 128 rows, laid along the rows in that order (out[1] * 384 + out[2] * 256 + out[3] * 128 >= n_q,
- * and every tile holds a row).
- *   12-wave workgroups where 384-row tiles would give every CU at least two workgroups.  When
- *   groups and cus are multiples of 8 (one share per XCD), each XCD runs its groups' 384-row
- *   tiles, then their 256-row ones, then their 128-row ones, and the mix is the candidate (0..4
- *   tiles of 256 rows, 0..1 of 128, as many of 384 as the rest needs) whose replayed list
- *   schedule on the XCD's CUs ends first.  The replay prices a tile at its busiest SIMD's step time,
- *   1, 0.88 and 0.66 for 3, 2 and 1 waves with rows (the 384-, 256- and 128-row tiles' ratios
- *   measured on an MI355X), plus 0.01; a tie keeps the candidate with fewer 256-row, then fewer
- *   128-row tiles.  Otherwise all tiles are 384 rows.
- *   4-wave workgroups otherwise, in 128-row tiles.
- * A row's result does not depend on the tile that holds it.  BCA_ERR_ARG for n_q or groups
- * outside [1, 2^31 - 1], cus < 0 or out NULL.
+ * bca_decode_ex, bca_decode_split) takes for n_q query rows per (batch, head) (for
+ * bca_decode_varlen, the largest N_b), batch_heads = B * H, n_split key ranges (1 = unsplit) on a
+ * GPU of `cus` compute units (0 = the current device's, 256 where the runtime cannot tell).
+ * out[0] = waves per workgroup; out[1..3] = query tiles per (batch, head, key range) of 384, 256
+ * and 128 rows, laid along the rows in that order (out[1] * 384 + out[2] * 256 + out[3] * 128 >=
+ * n_q, and every tile holds a row).
+ *   Unsplit, with batch_heads and cus multiples of 8 (one share per XCD): 12-wave workgroups once
+ *   384-row tiles would fill one round of the CUs (ceil(n_q / 384) * batch_heads >= cus).  Each
+ *   XCD runs its (batch, head) entries' 384-row tiles, then their 256-row ones, then their 128-row
+ *   ones, and the mix is the candidate (0..16 tiles of 256 rows, 0..2 of 128, as many of 384 as
+ *   the rest needs) whose replayed list schedule on the XCD's CUs ends first.  The replay prices
+ *   a tile at its busiest SIMD's step time, 1, 0.88 and 0.66 for 3, 2 and 1 waves with rows (the
+ *   384-, 256- and 128-row tiles' ratios measured on an MI355X), plus 0.01; a tie keeps the
+ *   candidate with fewer 256-row, then fewer 128-row tiles.
+ *   Otherwise: 12-wave workgroups in 384-row tiles where those give every CU at least two
+ *   (ceil(n_q / 384) * batch_heads * n_split >= 2 * cus).
+ *   4-wave workgroups in 128-row tiles in the remaining cases.
+ * A row's result does not depend on the tile that holds it.  BCA_ERR_ARG for n_q or batch_heads
+ * outside [1, 2^31 - 1], n_split < 1, batch_heads * n_split >= 2^31, cus < 0 or out NULL.
  */
-bca_status bca_decode_layout(int64_t n_q, int64_t groups, int32_t cus, int32_t* out);
+bca_status bca_decode_layout(int64_t n_q, int64_t batch_heads, int32_t n_split, int32_t cus,
+                             int32_t* out);
 
 /*
  * FP8 prefix cache (10100.com article, FP8 part: the prefix K/V cache may be stored as FP8 E4M3

@@ -1,14 +1,14 @@
 """The cached step's launch shape (bca_decode_layout, host only): waves per workgroup and the
-query tiles of 384, 256 and 128 rows per (batch, head, key range) group, as include/bca.h
-states them.
+query tiles of 384, 256 and 128 rows per (batch, head, key range), as include/bca.h states them.
 
 * The tiles cover every query row, and every tile holds at least one row.
-* 12-wave workgroups exactly where 384-row tiles give every CU two workgroups; 4-wave ones,
-  in 128-row tiles, otherwise.
+* The width rules: unsplit shares that are whole per XCD take 12-wave workgroups once 384-row
+  tiles fill one round of the CUs; other shapes once they give every CU two workgroups; 4-wave
+  ones, in 128-row tiles, otherwise.
 * The mix equals a replay written here from the header's description: for each candidate, a list
   schedule of one XCD's tiles (384-row tiles first, then 256, then 128) on its CUs, each tile
   priced at its busiest SIMD's step time (1, 0.88, 0.66 for 3, 2, 1 waves with rows) + 0.01.
-* Shares that are not whole per XCD keep 384-row tiles only; bad arguments are BCA_ERR_ARG.
+* Bad arguments are BCA_ERR_ARG.
 """
 import heapq
 
@@ -18,32 +18,34 @@ bca = pytest.importorskip("block_causal_attention_amd")
 from block_causal_attention_amd import _lib  # noqa: E402
 
 
+def cdiv(a, b):
+    return -(-a // b)
+
+
 def replay(n, nb, cx):
-    quarters = -(-n // 128)
+    quarters = cdiv(n, 128)
 
     def cost(row0, rows):
-        live = min(rows, n - row0)
-        busiest = -(-(-(-live // 32)) // 4)
+        busiest = cdiv(cdiv(min(rows, n - row0), 32), 4)
         return {3: 1.0, 2: 0.88, 1: 0.66}[min(busiest, 3)] + 0.01
 
     best = None
-    for n2 in range(5):
-        for n1 in range(2):
-            n3 = max(0, -(-(quarters - 2 * n2 - n1) // 3))
+    for n2 in range(17):
+        for n1 in range(3):
+            n3 = max(0, cdiv(quarters - 2 * n2 - n1, 3))
             covered = 384 * n3 + 256 * n2 + 128 * n1
             last = 128 if n1 else 256 if n2 else 384
             if n3 + n2 + n1 == 0 or covered < n or covered - last >= n:
                 continue
+            tiles = [(384 * t, 384) for _ in range(nb) for t in range(n3)]
+            tiles += [(384 * n3 + 256 * t, 256) for _ in range(nb) for t in range(n2)]
+            tiles += [(384 * n3 + 256 * n2 + 128 * t, 128) for _ in range(nb) for t in range(n1)]
             free = [0.0] * cx
             span = 0.0
-            base = 0
-            for count, height in ((n3, 384), (n2, 256), (n1, 128)):
-                for _ in range(nb):
-                    for t in range(count):
-                        done = heapq.heappop(free) + cost(base + height * t, height)
-                        heapq.heappush(free, done)
-                        span = max(span, done)
-                base += height * count
+            for row0, rows in tiles:          # a free CU takes the next tile
+                done = heapq.heappop(free) + cost(row0, rows)
+                heapq.heappush(free, done)
+                span = max(span, done)
             if best is None or span < best[0] - 1e-9:
                 best = (span, (n3, n2, n1))
     return best[1]
@@ -55,37 +57,42 @@ def covers(n, tiles):
     return sum(heights) >= n and all(s < n for s in starts)
 
 
-SHAPES = [(n, g, c) for n in (1, 100, 384, 385, 777, 1024, 3356, 3615, 4000, 4096, 8192, 12288,
-                              16384, 40000)
-          for g in (1, 8, 24, 32, 64, 256, 1000) for c in (256, 304, 80)]
+SHAPES = [(n, g, s, c) for n in (1, 100, 384, 385, 777, 1024, 2048, 3072, 3356, 3615, 4000, 4096,
+                                 5120, 8192, 16384, 40000)
+          for g in (1, 8, 24, 32, 64, 256) for s in (1, 3) for c in (256, 304, 80)]
 
 
-@pytest.mark.parametrize("n,groups,cus", SHAPES)
-def test_layout_covers_rows_and_follows_the_rules(n, groups, cus):
-    waves, t3, t2, t1 = bca.decode_layout(n, groups, cus)
-    wide = -(-n // 384) * groups >= 2 * cus
+@pytest.mark.parametrize("n,bh,n_split,cus", SHAPES)
+def test_layout_covers_rows_and_follows_the_rules(n, bh, n_split, cus):
+    waves, t3, t2, t1 = bca.decode_layout(n, bh, n_split, cus)
+    t12 = cdiv(n, 384)
+    mixable = n_split == 1 and bh % 8 == 0 and cus % 8 == 0
+    wide = t12 * bh >= cus if mixable else t12 * bh * n_split >= 2 * cus
     assert waves == (12 if wide else 4)
     if waves == 4:
-        assert (t3, t2, t1) == (0, 0, -(-n // 128))
+        assert (t3, t2, t1) == (0, 0, cdiv(n, 128))
         return
     assert covers(n, (t3, t2, t1))
-    if groups % 8 == 0 and cus % 8 == 0:
-        assert (t3, t2, t1) == replay(n, groups // 8, cus // 8)
+    if mixable:
+        assert (t3, t2, t1) == replay(n, bh // 8, cus // 8)
     else:
-        assert (t3, t2, t1) == (-(-n // 384), 0, 0)
+        assert (t3, t2, t1) == (t12, 0, 0)
 
 
 def test_headline_shapes():
     # the CFG cached step (B = 2, H = 32, N = 4,096) on 256 CUs: two rounds of 384-row tiles and
-    # one of 256-row tiles; at B = 1 the grid is small and takes 4-wave workgroups
-    assert bca.decode_layout(4096, 64, 256) == (12, 8, 4, 0)
-    assert bca.decode_layout(4096, 32, 256) == (4, 0, 0, 32)
-    assert bca.decode_layout(16384, 64, 256) == (12, 40, 4, 0)
-    assert bca.decode_layout(3356, 64, 256) == (12, 6, 4, 1)
+    # one of 256-row tiles; without CFG (B = 1) mostly 256-row tiles in two rounds
+    assert bca.decode_layout(4096, 64, 1, 256) == (12, 8, 4, 0)
+    assert bca.decode_layout(4096, 32, 1, 256) == (12, 2, 12, 2)
+    assert bca.decode_layout(16384, 64, 1, 256) == (12, 40, 4, 0)
+    # under one round of 384-row tiles the 4-wave kernel stays (512^2 target, unsplit and split)
+    assert bca.decode_layout(2048, 32, 1, 256) == (4, 0, 0, 16)
+    assert bca.decode_layout(1024, 32, 3, 256) == (4, 0, 0, 8)
 
 
-@pytest.mark.parametrize("args", [(0, 64, 256), (4096, 0, 256), (4096, 64, -1), (2**31, 64, 256),
-                                  (4096, 2**31, 256)])
+@pytest.mark.parametrize("args", [(0, 64, 1, 256), (4096, 0, 1, 256), (4096, 64, 0, 256),
+                                  (4096, 64, 1, -1), (2**31, 64, 1, 256), (4096, 2**31, 1, 256),
+                                  (4096, 2**30, 2, 256)])
 def test_bad_arguments(args):
     with pytest.raises(bca.BcaError) as e:
         bca.decode_layout(*args)

@@ -186,7 +186,8 @@ def test_cfg_fp8_full_size(fname, fmt):
                           rows=rows)
     check(got, ref, "fresh-step decode over FP8 cache vs oracle")
     # Heads are independent: two of them as strided views make a grid small enough for the
-    # 4-wave decode (the full one runs 8-wave workgroups); a row's arithmetic is the same.
+    # 4-wave decode (the full one runs 12-wave workgroups in 384- and 256-row tiles); a row's
+    # arithmetic is the same.
     two = slice(0, 2)
     sub = bca.KVCache(fmt, cache.k[:, :, two], cache.v[:, :, two],
                       None if cache.k_scale is None else cache.k_scale[:, :, two],

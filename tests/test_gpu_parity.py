@@ -300,10 +300,12 @@ def test_strided_inputs_and_side_stream():
 
 
 def test_decode_workgroup_widths_agree_bitwise():
-    """The bf16 decode runs 12-wave workgroups on large grids and 4-wave ones on small grids
-    (B = 2 and B = 1 at N = 4,096, H = 32).  A row's arithmetic and key order do not depend on
-    the width, so batch item 0 of the B = 2 decode equals the B = 1 decode of the same inputs
-    bit for bit (sampled against the oracle too, through the CFG test)."""
+    """A row's arithmetic and key order depend neither on the workgroup width nor on the height
+    of the query tile that holds it.  At N = 4,096, H = 32 the B = 2 decode runs 12-wave
+    workgroups in 8 x 384 + 4 x 256-row tiles, the B = 1 decode 12-wave ones in 2 x 384 +
+    12 x 256 + 2 x 128-row tiles, and an 8-head view of B = 1 4-wave ones in 128-row tiles: batch
+    item 0 of the first equals the other two bit for bit (sampled against the oracle too, through
+    the CFG test)."""
     lay = W.EDIT_2REF
     ids = lay.block_ids()
     S, H = lay.seq_len, lay.heads
@@ -316,18 +318,25 @@ def test_decode_workgroup_widths_agree_bitwise():
     both = bca.decode(plan, q, kc, vc, k, v)
     one = bca.decode(plan, q[:1].contiguous(), kc[:1].contiguous(), vc[:1].contiguous(),
                      k[:1].contiguous(), v[:1].contiguous())
+    eight = bca.decode(plan, q[:1, :, :8], kc[:1, :, :8], vc[:1, :, :8], k[:1, :, :8],
+                       v[:1, :, :8])
     torch.cuda.synchronize()
+    assert bca.decode_layout(N, 2 * H) == (12, 8, 4, 0)
+    assert bca.decode_layout(N, H) == (12, 2, 12, 2) and bca.decode_layout(N, 8)[0] == 4
     assert torch.equal(both[:1], one)
+    assert torch.equal(one[:, :, :8], eight)
 
 
 # Query-tile mixes of the 12-wave decode, as the launch picks them on 256 CUs (bca_decode_layout):
 # per (batch, head), tiles of 384, then 256, then 128 rows; each XCD runs its 384-row tiles first.
 MIX_CASES = [
     (4000, 2, 32),  # 8 x 384 + 4 x 256 (the last one 160 rows)
-    (3356, 2, 32),  # 6 x 384 + 4 x 256 + 1 x 128
+    (3356, 2, 32),  # 7 x 384 + 2 x 256 + 2 x 128
     (3615, 2, 32),  # 8 x 384 + 2 x 256 + 1 x 128
     (777, 4, 64),   # 2 x 384 + 1 x 128
-    (8192, 2, 32),  # 20 x 384 + 2 x 256
+    (8192, 2, 32),  # 18 x 384 + 4 x 256 + 2 x 128
+    (4096, 1, 32),  # 2 x 384 + 12 x 256 + 2 x 128 (no CFG)
+    (3072, 1, 32),  # 8 x 384: one round, 12-wave workgroups
 ]
 
 
