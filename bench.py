@@ -615,7 +615,8 @@ def main():
 
     # the dominant kernel: the call with the larger share of the step
     if dec_ms.mean() >= pre_ms.mean():
-        dom, key, achieved = ("decode: attn_decode_direct<0, 12> (bf16 cache), B=2", "decode_cfg_b2",
+        dom, key, achieved = ("decode (bf16 cache, B=2): attn_decode_direct<0, 12> for 384-row "
+                              "query tiles, then attn_decode_tail for the rest", "decode_cfg_b2",
                               dec_tf)
     else:
         dom, key, achieved = ("prefill: attn_prefill (writes the bf16 prefix cache), B=1",

@@ -495,12 +495,14 @@ def decode_varlen(plan: Plan, q, k_cache, v_cache, k, v, *, scale: Optional[floa
     return out
 
 
-def decode_layout(n_q: int, batch_heads: int, n_split: int = 1, cus: int = 0):
-    """(waves, tiles of 384, 256 and 128 rows per (batch, head, key range)) of a cached step with
-    n_q query rows per (batch, head), batch_heads = B * H and n_split key ranges, on `cus` compute
-    units (0: the current device's) (bca_decode_layout)."""
-    out = (ctypes.c_int32 * 4)()
-    _check(_lib.load().bca_decode_layout(n_q, batch_heads, n_split, cus, out))
+def decode_layout(n_q: int, batch_heads: int, n_split: int = 1, cache_fmt: int = 0,
+                  cus: int = 0):
+    """(waves, tiles of 384, 256 and 128 rows, tail tiles of 256 rows in a second 8-wave launch)
+    per (batch, head, key range) of a cached step with n_q query rows per (batch, head),
+    batch_heads = B * H, n_split key ranges and a cache of format cache_fmt (KVCache.BF16 / FP8_V /
+    FP8_KV), on `cus` compute units (0: the current device's) (bca_decode_layout)."""
+    out = (ctypes.c_int32 * 5)()
+    _check(_lib.load().bca_decode_layout(n_q, batch_heads, n_split, cache_fmt, cus, out))
     return tuple(out)
 
 

@@ -100,7 +100,7 @@ def load() -> ctypes.CDLL:
     lib.bca_decode_split_noalloc.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_float, T, C, T, T, T, ctypes.c_int32, P]
     lib.bca_decode_layout.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                      i32p]
+                                      ctypes.c_int32, i32p]
     lib.bca_status_str.argtypes = [ctypes.c_int]
     lib.bca_status_str.restype = ctypes.c_char_p
     lib.bca_last_error.argtypes = []

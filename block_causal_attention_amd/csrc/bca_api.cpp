@@ -641,8 +641,8 @@ bca_status bca_decode_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float
                      stream);
 }
 
-bca_status bca_decode_layout(int64_t n_q, int64_t batch_heads, int32_t n_split, int32_t cus,
-                             int32_t* out) {
+bca_status bca_decode_layout(int64_t n_q, int64_t batch_heads, int32_t n_split, int32_t cache_fmt,
+                             int32_t cus, int32_t* out) {
   if (out == nullptr) return fail(BCA_ERR_ARG, "out is NULL");
   if (n_q < 1 || n_q > INT32_MAX) return fail(BCA_ERR_ARG, "n_q must be in [1, 2^31 - 1]");
   if (batch_heads < 1 || batch_heads > INT32_MAX)
@@ -650,12 +650,15 @@ bca_status bca_decode_layout(int64_t n_q, int64_t batch_heads, int32_t n_split, 
   if (n_split < 1 || batch_heads * n_split > INT32_MAX)
     return fail(BCA_ERR_ARG, "n_split must be >= 1, with batch_heads * n_split below 2^31");
   if (cus < 0) return fail(BCA_ERR_ARG, "cus must be >= 0 (0 = the current device's)");
-  const bca::DecodeLayout l =
-      bca::decode_layout(n_q, batch_heads, n_split, cus > 0 ? cus : bca::device_cus());
+  if (cache_fmt != BCA_CACHE_BF16 && cache_fmt != BCA_CACHE_FP8_V && cache_fmt != BCA_CACHE_FP8_KV)
+    return fail(BCA_ERR_ARG, "cache_fmt must be BCA_CACHE_BF16, BCA_CACHE_FP8_V or BCA_CACHE_FP8_KV");
+  const bca::DecodeLayout l = bca::decode_layout(n_q, batch_heads, n_split,
+                                                 cus > 0 ? cus : bca::device_cus(), cache_fmt);
   out[0] = l.waves;
   out[1] = l.tiles[0];
   out[2] = l.tiles[1];
   out[3] = l.tiles[2];
+  out[4] = l.tail;
   return BCA_OK;
 }
 

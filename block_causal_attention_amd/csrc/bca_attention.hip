@@ -246,7 +246,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // Keys below kv_split come from the first source, the rest from the second; kv_len in all.
   // cache_row0: first cache row of the sequence's prefix (stored by the prefill, read by a
   // decode over a batch of sequences, whose targets start at tensor row seq_row0).
-  int seq_row0 = 0, row0 = tile * kRows, n_rows = a.n_q, rl_off = 0;
+  // (the decode's tail launch starts its tiles at row_base)
+  constexpr bool kTail = kDecode && kW == kDecodeTailWaves;
+  int seq_row0 = 0, row0 = tile * kRows + (kTail ? a.row_base : 0), n_rows = a.n_q, rl_off = 0;
   if constexpr (kMix) row0 = mix_row0;
   int kv_len = a.kv_len, kv_split = a.split, kv_end = a.kv_len, kv_full = a.kv_len;
   int cache_len = 0, cache_row0 = 0;
@@ -623,116 +625,123 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
     store_cache(n0, cur);
     // A wave that sees no key of a masked tile, or (4-wave bf16 decode) whose query rows all lie
     // past the end, only fills and synchronises: its share of the tile is exactly zero.
-    if ((!kSkipDead || live) && !(kMasked && !kDecode && n0 >= wave_lim)) {
+    // A 64-key tile is computed as two 32-key halves in key order, exactly as two 32-key tiles.
+#pragma unroll
+    for (int kh = 0; kh < kKeyBlocks; ++kh) {
+      const int nh = n0 + 32 * kh;
+      if ((!kSkipDead || live) && !(kMasked && !kDecode && nh >= wave_lim)) {
+        constexpr int kKB = 1;
 
-      // ---- S^T = K Q^T
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPrioLevel);
-      f32x16 s[kQueryBlocks][kKeyBlocks];
+        // ---- S^T = K Q^T
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPrioLevel);
+        f32x16 s[kQueryBlocks][kKB];
 #pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb) {
+        for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < kQueryBlocks; ++qb) s[qb][kb] = f32x16{};
+          for (int qb = 0; qb < kQueryBlocks; ++qb) s[qb][kb] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const bf16x8 ka = k_read(cur, c, kb);
+          for (int c = 0; c < 8; ++c) {
+            const bf16x8 ka = k_read(cur, c, kh + kb);
+#pragma unroll
+            for (int qb = 0; qb < kQueryBlocks; ++qb)
+              s[qb][kb] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[qb][kb], 0, 0, 0);
+          }
+        }
+        pipeline_reads<8 * kKB, 1, kQueryBlocks, kSchedKDepth>();
+
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+        // ---- mask: only tiles that cross some row's limit.  Accumulator element i of key block kb
+        // holds key n0 + 32 kb + 8 (i / 4) + 4 half + i % 4.
+        if (kMasked) {
 #pragma unroll
           for (int qb = 0; qb < kQueryBlocks; ++qb)
-            s[qb][kb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[qb][kb], 0, 0, 0);
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int key = nh + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+                if (key >= lim[qb]) s[qb][kb][i] = -__builtin_inff();
+              }
         }
-      }
-      pipeline_reads<8 * kKeyBlocks, 1, kQueryBlocks, kSchedKDepth>();
 
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
-      // ---- mask: only tiles that cross some row's limit.  Accumulator element i of key block kb
-      // holds key n0 + 32 kb + 8 (i / 4) + 4 half + i % 4.
-      if (kMasked) {
+        // ---- p = 2^(s c2 - m) against the running max m of earlier tiles, as bf16 P^T
+        // operands (chunks of 16 keys), plus this tile's row-sum share.  A row whose scores grew
+        // past m + kRescaleThreshold (or any row on its first tile, where m = -inf) shows a lane
+        // sum above 2^threshold (or inf); only then does the wave take the exact path: per-row
+        // max, raise and rescale for rows that grew by more than the threshold, and p recomputed.
+        // Rows that do not raise recompute the same values, so each row still depends on its own
+        // scores alone.
+        bf16x8 pb[kQueryBlocks][2 * kKB];
+        float tsum[kQueryBlocks];
+        auto exp_tile = [&](int qb) {
+          const float mneg = -m_run[qb];
+          float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-        for (int qb = 0; qb < kQueryBlocks; ++qb)
+          for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-              if (key >= lim[qb]) s[qb][kb][i] = -__builtin_inff();
+            for (int i = 0; i < 16; i += 2) {
+              const float x0 = __builtin_fmaf(s[qb][kb][i], c2, mneg);
+              const float x1 = __builtin_fmaf(s[qb][kb][i + 1], c2, mneg);
+              const float p0 = __builtin_amdgcn_exp2f(x0);
+              const float p1 = __builtin_amdgcn_exp2f(x1);
+              const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+              pb[qb][2 * kb + (i >> 3)][i & 7] = pp[0];
+              pb[qb][2 * kb + (i >> 3)][(i & 7) + 1] = pp[1];
+              if (i & 2)
+                acc1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc1, false);
+              else
+                acc0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc0, false);
             }
-      }
-
-      // ---- p = 2^(s c2 - m) against the running max m of earlier tiles, as bf16 P^T operands
-      // (chunks of 16 keys), plus this tile's row-sum share.  A row whose scores grew past
-      // m + kRescaleThreshold (or any row on its first tile, where m = -inf) shows a lane sum
-      // above 2^threshold (or inf); only then does the wave take the exact path: per-row max, raise
-      // and rescale for rows that grew by more than the threshold, and p recomputed.  Rows that do
-      // not raise recompute the same values, so each row still depends on its own scores alone.
-      bf16x8 pb[kQueryBlocks][2 * kKeyBlocks];
-      float tsum[kQueryBlocks];
-      auto exp_tile = [&](int qb) {
-        const float mneg = -m_run[qb];
-        float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            const float x0 = __builtin_fmaf(s[qb][kb][i], c2, mneg);
-            const float x1 = __builtin_fmaf(s[qb][kb][i + 1], c2, mneg);
-            const float p0 = __builtin_amdgcn_exp2f(x0);
-            const float p1 = __builtin_amdgcn_exp2f(x1);
-            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-            pb[qb][2 * kb + (i >> 3)][i & 7] = pp[0];
-            pb[qb][2 * kb + (i >> 3)][(i & 7) + 1] = pp[1];
-            if (i & 2)
-              acc1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc1, false);
-            else
-              acc0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc0, false);
-          }
-        tsum[qb] = acc0 + acc1;
-      };
-      bool redo = false;
-#pragma unroll
-      for (int qb = 0; qb < kQueryBlocks; ++qb) {
-        exp_tile(qb);
-        redo = redo || !(tsum[qb] <= kRescaleBound);
-      }
-      if (__builtin_amdgcn_ballot_w64(redo)) {
+          tsum[qb] = acc0 + acc1;
+        };
+        bool redo = false;
 #pragma unroll
         for (int qb = 0; qb < kQueryBlocks; ++qb) {
-          float mx = s[qb][0][0];
-#pragma unroll
-          for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-          mx = halves_max(mx);
-          const float m_cand = fmaxf(m_run[qb], mx * c2);
-          const bool raise = m_cand > m_run[qb] + kRescaleThreshold;
-          // (0 on the first tile)
-          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[qb] - m_cand) : 1.0f;
-          m_run[qb] = raise ? m_cand : m_run[qb];
-          l_part[qb] *= alpha;
-#pragma unroll
-          for (int d = 0; d < 4; ++d) o[qb][d] *= alpha;
           exp_tile(qb);
+          redo = redo || !(tsum[qb] <= kRescaleBound);
         }
-      }
+        if (__builtin_amdgcn_ballot_w64(redo)) {
 #pragma unroll
-      for (int qb = 0; qb < kQueryBlocks; ++qb) l_part[qb] += tsum[qb];
-
-      // ---- O^T += V^T P^T
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPrioLevel);
+          for (int qb = 0; qb < kQueryBlocks; ++qb) {
+            float mx = s[qb][0][0];
 #pragma unroll
-      for (int kc = 0; kc < 2 * kKeyBlocks; ++kc) {
+            for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const bf16x4 lo = v_read(cur, 0, d, kc);
-          const bf16x4 hi = v_read(cur, 1, d, kc);
-          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+            mx = halves_max(mx);
+            const float m_cand = fmaxf(m_run[qb], mx * c2);
+            const bool raise = m_cand > m_run[qb] + kRescaleThreshold;
+            // (0 on the first tile)
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[qb] - m_cand) : 1.0f;
+            m_run[qb] = raise ? m_cand : m_run[qb];
+            l_part[qb] *= alpha;
 #pragma unroll
-          for (int qb = 0; qb < kQueryBlocks; ++qb)
-            o[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kc], o[qb][d], 0, 0, 0);
+            for (int d = 0; d < 4; ++d) o[qb][d] *= alpha;
+            exp_tile(qb);
+          }
         }
-      }
-      pipeline_reads<8 * kKeyBlocks, 2, kQueryBlocks, kSchedVDepth>();
+#pragma unroll
+        for (int qb = 0; qb < kQueryBlocks; ++qb) l_part[qb] += tsum[qb];
 
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+        // ---- O^T += V^T P^T
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPrioLevel);
+#pragma unroll
+        for (int kc = 0; kc < 2 * kKB; ++kc) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const bf16x4 lo = v_read(cur, 0, d, 2 * kh + kc);
+            const bf16x4 hi = v_read(cur, 1, d, 2 * kh + kc);
+            const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int qb = 0; qb < kQueryBlocks; ++qb)
+              o[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kc], o[qb][d], 0, 0, 0);
+          }
+        }
+        pipeline_reads<8 * kKB, 2, kQueryBlocks, kSchedVDepth>();
+
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+      }
     }
 
     // ---- refill: tile j+1 was issued one iteration ago; wait for it, then after the barrier
@@ -898,6 +907,16 @@ __device__ __align__(256) static unsigned char scratch[kScratchBytes];
 
 }  // namespace
 
+// Decode tail: the query tiles past the 12-wave launch's 384-row ones, as 256-row workgroups of 8
+// waves at 2 waves per SIMD (the register budget of two waves allows 64-key fills, half the
+// barriers) over a bf16 cache.  Each 64-key tile is computed as two 32-key halves, so every row
+// gets bitwise the arithmetic of the 12-wave kernel.
+__global__ __launch_bounds__(64 * kDecodeTailWaves)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_decode_tail(const AttnArgs a) {
+  attn_fwd<true, kCacheBf16, kDecodeTailBlockN, kDecodeTailWaves>(a);
+}
+
 // Compute units of the current device (cached per device).
 int device_cus() {
   static std::atomic<int> cache[64];
@@ -956,16 +975,18 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
 // is full and that phase is dealt in whole rounds (the first k3 % cx CUs take one tile more).
 // The shortest schedule wins; a tie keeps the earlier candidate (fewer 256-row, then fewer
 // 128-row tiles).  The last 8 queries are cached per thread.
-void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
+void decode_mix(int n, int nb, int cx, int32_t mix[3], double* span_out) {
   struct Entry {
     int n, nb, cx;
     int32_t m[3];
+    double span;
   };
   thread_local Entry cache[8];
   thread_local int cached = 0, next = 0;
   for (int i = 0; i < cached; ++i)
     if (cache[i].n == n && cache[i].nb == nb && cache[i].cx == cx) {
       mix[0] = cache[i].m[0], mix[1] = cache[i].m[1], mix[2] = cache[i].m[2];
+      *span_out = cache[i].span;
       return;
     }
   const int quarters = (n + 127) / 128;
@@ -1015,12 +1036,34 @@ void decode_mix(int n, int nb, int cx, int32_t mix[3]) {
       }
     }
   mix[0] = pick[0], mix[1] = pick[1], mix[2] = pick[2];
-  cache[next] = Entry{n, nb, cx, {pick[0], pick[1], pick[2]}};
+  *span_out = best;
+  cache[next] = Entry{n, nb, cx, {pick[0], pick[1], pick[2]}, best};
   next = (next + 1) % 8;
   cached = std::min(cached + 1, 8);
 }
 
-DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus) {
+// Two launches instead of one mixed launch: n3 tiles of 384 rows per (batch, head) in the 12-wave
+// kernel, then the remaining rows in 256-row tiles of the 8-wave tail kernel, which start once
+// the first launch has ended.  Both phases deal equal tiles, in whole rounds of the XCD's cx CUs:
+// ceil(nb n3 / cx) * 1.01 + 0.02 (the launch boundary) + ceil(nb n_tail / cx) * 0.737, a 256-row
+// tail tile costing 0.727 of a 384-row 12-wave tile (measured on the CFG cached step) + 0.01.
+// Returns the best n3 and its span, or n3 = -1 when no rows are left for a tail.
+static void decode_two_launch(int n, int nb, int cx, int* best_n3, double* best_span) {
+  *best_n3 = -1;
+  *best_span = 0.0;
+  auto rounds = [&](int64_t k) { return (double)((k + cx - 1) / cx); };
+  for (int n3 = 0; 384 * n3 < n; ++n3) {
+    const int n_tail = (n - 384 * n3 + 255) / 256;
+    const double span = rounds((int64_t)nb * n3) * 1.01 + (n3 > 0 ? 0.02 : 0.0) +
+                        rounds((int64_t)nb * n_tail) * 0.737;
+    if (*best_n3 < 0 || span < *best_span - 1e-9) {
+      *best_n3 = n3;
+      *best_span = span;
+    }
+  }
+}
+
+DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus, int cache_fmt) {
   DecodeLayout l{};
   auto tiles = [&](int waves) {
     const int64_t rows = 32 * kQueryBlocks * waves;
@@ -1031,8 +1074,22 @@ DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus) {
     // mixed tile heights: 12-wave workgroups once 384-row tiles would fill one round
     if (t12 * groups >= (int64_t)cus) {
       l.waves = kDecodeDirectWaves;
-      decode_mix((int)n_q, (int)(groups / 8), cus / 8, l.tiles);
+      double span = 0.0;
+      decode_mix((int)n_q, (int)(groups / 8), cus / 8, l.tiles, &span);
       l.mixed = true;
+      // a bf16 cache may instead finish with the 8-wave tail launch, taken when the replay
+      // predicts it at least 3% shorter and each XCD holds at least 8 (batch, head) entries
+      // (with 4, at B = 1 and 32 heads, two launches measured no faster for N = 4,096 to 8,192)
+      if (cache_fmt == kCacheBf16 && groups / 8 >= 8) {
+        int n3 = -1;
+        double two = 0.0;
+        decode_two_launch((int)n_q, (int)(groups / 8), cus / 8, &n3, &two);
+        if (n3 >= 0 && two < 0.97 * span) {
+          l.tiles[0] = n3;
+          l.tiles[1] = l.tiles[2] = 0;
+          l.tail = (int32_t)((n_q - 384 * (int64_t)n3 + 255) / 256);
+        }
+      }
       return l;
     }
   } else if (t12 * groups * std::max(n_split, 1) >= 2 * (int64_t)cus) {
@@ -1050,9 +1107,25 @@ hipError_t launch_decode(const AttnArgs& args, hipStream_t stream) {
   AttnArgs a = args;
   const int n_split = a.n_split > 1 ? a.n_split : 1;
   const int64_t heads = (int64_t)a.batch * a.heads * n_split;
-  const DecodeLayout l = decode_layout(a.n_q, (int64_t)a.batch * a.heads, n_split, device_cus());
+  const DecodeLayout l =
+      decode_layout(a.n_q, (int64_t)a.batch * a.heads, n_split, device_cus(), a.cache_fmt);
   a.n_qtiles = l.tiles[0] + l.tiles[1] + l.tiles[2];
   for (int i = 0; i < 3; ++i) a.mix[i] = l.mixed ? l.tiles[i] : 0;
+  a.row_base = 0;
+  if (l.tail > 0) {
+    // 384-row tiles in the 12-wave kernel, then the 8-wave tail kernel from row 384 n3 on
+    if (a.n_qtiles > 0)
+      hipLaunchKernelGGL((attn_decode_direct<kCacheBf16, kDecodeDirectWaves>),
+                         dim3((unsigned)(a.n_qtiles * heads)), dim3(64 * kDecodeDirectWaves), 0,
+                         stream, a);
+    AttnArgs t = a;
+    t.row_base = 384 * l.tiles[0];
+    t.n_qtiles = l.tail;
+    t.mix[0] = t.mix[1] = t.mix[2] = 0;
+    hipLaunchKernelGGL(attn_decode_tail, dim3((unsigned)(t.n_qtiles * heads)),
+                       dim3(64 * kDecodeTailWaves), 0, stream, t);
+    return hipGetLastError();
+  }
   auto launch = [&](auto kernel, int waves) {
     const dim3 grid((unsigned)(a.n_qtiles * heads));
     hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream, a);

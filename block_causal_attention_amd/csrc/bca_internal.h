@@ -28,6 +28,8 @@ constexpr int kPrefillBlockN = 32;
 constexpr int kPrefillWavesPerSimd = 3;
 constexpr int kDecodeDirectBlockN = 32;
 constexpr int kDecodeDirectWavesPerSimd = 3;
+constexpr int kDecodeTailWaves = 8;    // decode tail launch: 256-row tiles
+constexpr int kDecodeTailBlockN = 64;  // ... filled 64 keys at a time
 // A split decode's key ranges are whole multiples of kSplitUnit keys, whatever the kernel's tile
 // width (which divides it), so the workspace a plan needs does not depend on the cache format.
 constexpr int kSplitUnit = 64;
@@ -103,6 +105,8 @@ struct AttnArgs {
   // entries, all 384-row tiles first, then the 256-row ones, then the 128-row ones.  mix[0] == 0:
   // every tile 384 rows, (batch, head)-major (launch_decode fills it in).
   int32_t mix[3];
+  // Decode tail launch (attn_decode_tail): first query row of its tile 0 in every (batch, head).
+  int32_t row_base;
 };
 
 // Q/K prologue: RMS-normalise each 128-value head row of q and k (weights wq, wk), rotate its
@@ -188,12 +192,16 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 //   picks (mixed = true) once 384-row tiles would fill one round of the CUs, else 4-wave ones.
 //   Otherwise: 12-wave workgroups in 384-row tiles {ceil(n_q / 384), 0, 0} where those give every
 //   CU at least two, else 4-wave ones.  4 waves: {0, 0, ceil(n_q / 128)}.
+//   With a bf16 cache, an unsplit mixed launch may instead be two launches (tail > 0): tiles[0]
+//   384-row tiles in the 12-wave kernel (mixed = true, tiles[1] = tiles[2] = 0), then `tail`
+//   256-row tiles of the 8-wave tail kernel from row 384 * tiles[0] on.
 struct DecodeLayout {
   int waves;
   int32_t tiles[3];
   bool mixed;
+  int32_t tail;
 };
-DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus);
+DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus, int cache_fmt);
 // Compute units of the current device (256 where the runtime cannot tell).
 int device_cus();
 

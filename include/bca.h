@@ -229,11 +229,12 @@ bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
 /*
  * bca_decode_layout -- HOST.  The launch shape the cached step (bca_decode, bca_decode_varlen,
  * bca_decode_ex, bca_decode_split) takes for n_q query rows per (batch, head) (for
- * bca_decode_varlen, the largest N_b), batch_heads = B * H, n_split key ranges (1 = unsplit) on a
- * GPU of `cus` compute units (0 = the current device's, 256 where the runtime cannot tell).
- * out[0] = waves per workgroup; out[1..3] = query tiles per (batch, head, key range) of 384, 256
- * and 128 rows, laid along the rows in that order (out[1] * 384 + out[2] * 256 + out[3] * 128 >=
- * n_q, and every tile holds a row).
+ * bca_decode_varlen, the largest N_b), batch_heads = B * H, n_split key ranges (1 = unsplit) and
+ * a cache of format cache_fmt, on a GPU of `cus` compute units (0 = the current device's, 256
+ * where the runtime cannot tell).  out[0] = waves per workgroup of the first launch; out[1..3] =
+ * its query tiles per (batch, head, key range) of 384, 256 and 128 rows, laid along the rows in
+ * that order; out[4] = query tiles of 256 rows that a second launch of 8-wave workgroups takes
+ * from row 384 * out[1] on (0 = one launch).  The tiles cover every row, and every tile holds one.
  *   Unsplit, with batch_heads and cus multiples of 8 (one share per XCD): 12-wave workgroups once
  *   384-row tiles would fill one round of the CUs (ceil(n_q / 384) * batch_heads >= cus).  Each
  *   XCD runs its (batch, head) entries' 384-row tiles, then their 256-row ones, then their 128-row
@@ -242,14 +243,20 @@ bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
  *   a tile at its busiest SIMD's step time, 1, 0.88 and 0.66 for 3, 2 and 1 waves with rows (the
  *   384-, 256- and 128-row tiles' ratios measured on an MI355X), plus 0.01; a tie keeps the
  *   candidate with fewer 256-row, then fewer 128-row tiles.
+ *   With a bf16 cache and batch_heads >= 64 (8 entries per XCD) the step may instead take two
+ *   launches: n3 tiles of 384 rows in the 12-wave kernel, then the rest in 256-row tiles of
+ *   8-wave workgroups (2 waves per SIMD, 64-key fills), priced in whole rounds of the XCD's CUs
+ *   at 1.01 and 0.737 per tile plus 0.02 for the second launch; the best n3 is taken when it
+ *   replays at least 3% shorter than the mix.
  *   Otherwise: 12-wave workgroups in 384-row tiles where those give every CU at least two
  *   (ceil(n_q / 384) * batch_heads * n_split >= 2 * cus).
  *   4-wave workgroups in 128-row tiles in the remaining cases.
- * A row's result does not depend on the tile that holds it.  BCA_ERR_ARG for n_q or batch_heads
- * outside [1, 2^31 - 1], n_split < 1, batch_heads * n_split >= 2^31, cus < 0 or out NULL.
+ * A row's result does not depend on the tile or launch that holds it.  BCA_ERR_ARG for n_q or
+ * batch_heads outside [1, 2^31 - 1], n_split < 1, batch_heads * n_split >= 2^31, an unknown
+ * cache_fmt, cus < 0 or out NULL.
  */
-bca_status bca_decode_layout(int64_t n_q, int64_t batch_heads, int32_t n_split, int32_t cus,
-                             int32_t* out);
+bca_status bca_decode_layout(int64_t n_q, int64_t batch_heads, int32_t n_split, int32_t cache_fmt,
+                             int32_t cus, int32_t* out);
 
 /*
  * FP8 prefix cache (10100.com article, FP8 part: the prefix K/V cache may be stored as FP8 E4M3

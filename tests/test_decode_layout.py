@@ -8,6 +8,8 @@ query tiles of 384, 256 and 128 rows per (batch, head, key range), as include/bc
 * The mix equals a replay written here from the header's description: for each candidate, a list
   schedule of one XCD's tiles (384-row tiles first, then 256, then 128) on its CUs, each tile
   priced at its busiest SIMD's step time (1, 0.88, 0.66 for 3, 2, 1 waves with rows) + 0.01.
+  With a bf16 cache, the two-launch plan (384-row tiles, then 256-row tail tiles, each phase in
+  whole rounds at 1.01 and 0.737 per tile + 0.02) replaces it when at least 3% shorter.
 * Bad arguments are BCA_ERR_ARG.
 """
 import heapq
@@ -29,7 +31,7 @@ def replay(n, nb, cx):
         busiest = cdiv(cdiv(min(rows, n - row0), 32), 4)
         return {3: 1.0, 2: 0.88, 1: 0.66}[min(busiest, 3)] + 0.01
 
-    best = None
+    best = None  # (span, (n3, n2, n1))
     for n2 in range(17):
         for n1 in range(3):
             n3 = max(0, cdiv(quarters - 2 * n2 - n1, 3))
@@ -48,7 +50,21 @@ def replay(n, nb, cx):
                 span = max(span, done)
             if best is None or span < best[0] - 1e-9:
                 best = (span, (n3, n2, n1))
-    return best[1]
+    return best
+
+
+def two_launch(n, nb, cx):
+    """384-row tiles in the 12-wave kernel, then 256-row tail tiles, each phase in whole rounds:
+    (span, n3, n_tail) of the best n3 (fewest on ties)."""
+    best = None
+    n3 = 0
+    while 384 * n3 < n:
+        n_tail = cdiv(n - 384 * n3, 256)
+        span = cdiv(nb * n3, cx) * 1.01 + (0.02 if n3 else 0.0) + cdiv(nb * n_tail, cx) * 0.737
+        if best is None or span < best[0] - 1e-9:
+            best = (span, n3, n_tail)
+        n3 += 1
+    return best
 
 
 def covers(n, tiles):
@@ -62,37 +78,46 @@ SHAPES = [(n, g, s, c) for n in (1, 100, 384, 385, 777, 1024, 2048, 3072, 3356, 
           for g in (1, 8, 24, 32, 64, 256) for s in (1, 3) for c in (256, 304, 80)]
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("n,bh,n_split,cus", SHAPES)
-def test_layout_covers_rows_and_follows_the_rules(n, bh, n_split, cus):
-    waves, t3, t2, t1 = bca.decode_layout(n, bh, n_split, cus)
+def test_layout_covers_rows_and_follows_the_rules(n, bh, n_split, cus, fmt):
+    waves, t3, t2, t1, tail = bca.decode_layout(n, bh, n_split, fmt, cus)
     t12 = cdiv(n, 384)
     mixable = n_split == 1 and bh % 8 == 0 and cus % 8 == 0
     wide = t12 * bh >= cus if mixable else t12 * bh * n_split >= 2 * cus
     assert waves == (12 if wide else 4)
     if waves == 4:
-        assert (t3, t2, t1) == (0, 0, cdiv(n, 128))
+        assert (t3, t2, t1, tail) == (0, 0, cdiv(n, 128), 0)
         return
-    assert covers(n, (t3, t2, t1))
-    if mixable:
-        assert (t3, t2, t1) == replay(n, bh // 8, cus // 8)
+    if not mixable:
+        assert (t3, t2, t1, tail) == (t12, 0, 0, 0)
+        return
+    span, mix = replay(n, bh // 8, cus // 8)
+    two = two_launch(n, bh // 8, cus // 8)
+    if fmt == 0 and bh // 8 >= 8 and two is not None and two[0] < 0.97 * span:
+        assert (t3, t2, t1, tail) == (two[1], 0, 0, two[2])
+        assert 384 * t3 < n <= 384 * t3 + 256 * tail and 384 * t3 + 256 * (tail - 1) < n
     else:
-        assert (t3, t2, t1) == (t12, 0, 0)
+        assert (t3, t2, t1, tail) == mix + (0,)
+        assert covers(n, mix)
 
 
 def test_headline_shapes():
-    # the CFG cached step (B = 2, H = 32, N = 4,096) on 256 CUs: two rounds of 384-row tiles and
-    # one of 256-row tiles; without CFG (B = 1) mostly 256-row tiles in two rounds
-    assert bca.decode_layout(4096, 64, 1, 256) == (12, 8, 4, 0)
-    assert bca.decode_layout(4096, 32, 1, 256) == (12, 2, 12, 2)
-    assert bca.decode_layout(16384, 64, 1, 256) == (12, 40, 4, 0)
+    # the CFG cached step (B = 2, H = 32, N = 4,096) on 256 CUs, bf16 cache: two rounds of
+    # 384-row tiles, then one round of 256-row tiles in the 8-wave tail launch; over an FP8
+    # cache the same rows in one launch (384- and 256-row tiles)
+    assert bca.decode_layout(4096, 64, 1, 0, 256) == (12, 8, 0, 0, 4)
+    assert bca.decode_layout(4096, 64, 1, 1, 256) == (12, 8, 4, 0, 0)
+    assert bca.decode_layout(16384, 64, 1, 0, 256) == (12, 40, 4, 0, 0)
     # under one round of 384-row tiles the 4-wave kernel stays (512^2 target, unsplit and split)
-    assert bca.decode_layout(2048, 32, 1, 256) == (4, 0, 0, 16)
-    assert bca.decode_layout(1024, 32, 3, 256) == (4, 0, 0, 8)
+    assert bca.decode_layout(2048, 32, 1, 0, 256) == (4, 0, 0, 16, 0)
+    assert bca.decode_layout(1024, 32, 3, 0, 256) == (4, 0, 0, 8, 0)
 
 
-@pytest.mark.parametrize("args", [(0, 64, 1, 256), (4096, 0, 1, 256), (4096, 64, 0, 256),
-                                  (4096, 64, 1, -1), (2**31, 64, 1, 256), (4096, 2**31, 1, 256),
-                                  (4096, 2**30, 2, 256)])
+@pytest.mark.parametrize("args", [(0, 64, 1, 0, 256), (4096, 0, 1, 0, 256), (4096, 64, 0, 0, 256),
+                                  (4096, 64, 1, 0, -1), (2**31, 64, 1, 0, 256),
+                                  (4096, 2**31, 1, 0, 256), (4096, 2**30, 2, 0, 256),
+                                  (4096, 64, 1, 3, 256)])
 def test_bad_arguments(args):
     with pytest.raises(bca.BcaError) as e:
         bca.decode_layout(*args)

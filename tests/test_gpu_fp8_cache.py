@@ -244,3 +244,40 @@ def test_fp8_decode_without_prefix():
     ref = O.attention(f32(qb), f32(kb), f32(vb), ids)
     check(o.cpu().numpy(), ref, "prefill")
     check(od.cpu().numpy(), ref, "decode")
+
+
+@pytest.mark.parametrize("fname,fmt", FORMATS)
+def test_fp8_decode_tile_mix(fname, fmt):
+    """A target height (N = 3,356, B = 2, H = 32) whose FP8 cached step runs 12-wave workgroups
+    in 384-, 256- and 128-row tiles in one launch: sampled rows of three heads against the
+    oracle, and two heads as strided views (a grid for the 4-wave decode) bitwise equal."""
+    ids = W.block_ids_from_segments([("text", 45), ("image", 260), ("image", 3356)])
+    B, H = 2, 32
+    plan = bca.Plan(ids)
+    P, N = plan.info.prefix_len, plan.info.target_len
+    assert N == 3356
+    assert bca.decode_layout(N, B * H, 1, fmt)[:4] == (12, 7, 2, 2)
+    say(f"case: FP8 tile mix {fname} P={P} N={N}")
+    qb, kb, vb = W.qkv(21, B, len(ids), H, scaled=False)
+    cache = poison_cache(plan, B, H, fmt)
+    bca.prefill_ex(plan, to_dev(qb), to_dev(kb), to_dev(vb), cache)
+    qt, kt, vt = W.qkv(22, B, N, H, scaled=False)
+    od = bca.decode_ex(plan, to_dev(qt), cache, to_dev(kt), to_dev(vt))
+    torch.cuda.synchronize()
+    heads = [0, 13, 31]
+    rows = np.unique(np.concatenate([np.arange(0, N, 37), [383, 384, 2687, 2688, 3199, 3200,
+                                                           3327, 3328, N - 1]]))
+    got = od[:, torch.from_numpy(rows).to(DEV)][:, :, heads].cpu().numpy()
+    oc = oracle_cache(kb, vb, ids, fmt, heads=heads)
+    ref = O.decode_cached(f32(qt[:, :, heads]), oc, f32(kt[:, :, heads]), f32(vt[:, :, heads]),
+                          rows=rows)
+    check(got, ref, "tile-mix decode over FP8 cache vs oracle")
+    two = slice(5, 7)
+    assert bca.decode_layout(N, B * 2, 1, fmt)[0] == 4
+    sub = bca.KVCache(fmt, cache.k[:, :, two], cache.v[:, :, two],
+                      None if cache.k_scale is None else cache.k_scale[:, :, two],
+                      None if cache.v_scale is None else cache.v_scale[:, :, two])
+    od2 = bca.decode_ex(plan, to_dev(qt)[:, :, two], sub, to_dev(kt)[:, :, two],
+                        to_dev(vt)[:, :, two])
+    torch.cuda.synchronize()
+    assert torch.equal(od[:, :, two], od2)

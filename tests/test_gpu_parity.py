@@ -301,11 +301,12 @@ def test_strided_inputs_and_side_stream():
 
 def test_decode_workgroup_widths_agree_bitwise():
     """A row's arithmetic and key order depend neither on the workgroup width nor on the height
-    of the query tile that holds it.  At N = 4,096, H = 32 the B = 2 decode runs 12-wave
-    workgroups in 8 x 384 + 4 x 256-row tiles, the B = 1 decode 12-wave ones in 2 x 384 +
-    12 x 256 + 2 x 128-row tiles, and an 8-head view of B = 1 4-wave ones in 128-row tiles: batch
-    item 0 of the first equals the other two bit for bit (sampled against the oracle too, through
-    the CFG test)."""
+    of the query tile or the launch that holds it.  At N = 4,096, H = 32 the B = 2 decode runs
+    8 x 384-row tiles in 12-wave workgroups and the last 1,024 rows in the 8-wave tail launch,
+    the B = 1 decode runs one launch of 384-, 256- and 128-row tiles in 12-wave workgroups, and
+    an 8-head view of B = 1 runs 4-wave workgroups in 128-row tiles: batch item 0 of the first
+    equals the other two bit for bit
+    (sampled against the oracle too, through the CFG test)."""
     lay = W.EDIT_2REF
     ids = lay.block_ids()
     S, H = lay.seq_len, lay.heads
@@ -321,31 +322,32 @@ def test_decode_workgroup_widths_agree_bitwise():
     eight = bca.decode(plan, q[:1, :, :8], kc[:1, :, :8], vc[:1, :, :8], k[:1, :, :8],
                        v[:1, :, :8])
     torch.cuda.synchronize()
-    assert bca.decode_layout(N, 2 * H) == (12, 8, 4, 0)
-    assert bca.decode_layout(N, H) == (12, 2, 12, 2) and bca.decode_layout(N, 8)[0] == 4
+    assert bca.decode_layout(N, 2 * H) == (12, 8, 0, 0, 4)
+    assert bca.decode_layout(N, H) == (12, 2, 12, 2, 0) and bca.decode_layout(N, 8)[0] == 4
     assert torch.equal(both[:1], one)
     assert torch.equal(one[:, :, :8], eight)
 
 
-# Query-tile mixes of the 12-wave decode, as the launch picks them on 256 CUs (bca_decode_layout):
-# per (batch, head), tiles of 384, then 256, then 128 rows; each XCD runs its 384-row tiles first.
+# Launch shapes of the bf16 cached step on 256 CUs (bca_decode_layout): per (batch, head), query
+# tiles of 384 (then 256, 128) rows in the 12-wave kernel, and 256-row tiles of a second,
+# 8-wave launch (tail).
 MIX_CASES = [
-    (4000, 2, 32),  # 8 x 384 + 4 x 256 (the last one 160 rows)
-    (3356, 2, 32),  # 7 x 384 + 2 x 256 + 2 x 128
-    (3615, 2, 32),  # 8 x 384 + 2 x 256 + 1 x 128
-    (777, 4, 64),   # 2 x 384 + 1 x 128
-    (8192, 2, 32),  # 18 x 384 + 4 x 256 + 2 x 128
-    (4096, 1, 32),  # 2 x 384 + 12 x 256 + 2 x 128 (no CFG)
-    (3072, 1, 32),  # 8 x 384: one round, 12-wave workgroups
+    (4000, 2, 32),   # 8 x 384, tail 4 x 256 (the last one 160 rows)
+    (3356, 2, 32),   # 4 x 384, tail 8 x 256
+    (777, 4, 64),    # 1 x 384, tail 2 x 256
+    (2048, 2, 32),   # tail only, 8 x 256
+    (4096, 1, 32),   # 2 x 384 + 12 x 256 + 2 x 128 in one launch (no CFG: 4 entries per XCD)
+    (3072, 1, 32),   # 8 x 384 in one launch: one round
+    (16384, 2, 32),  # 40 x 384 + 4 x 256 in one launch
 ]
 
 
 @pytest.mark.parametrize("N,B,H", MIX_CASES)
 def test_decode_tile_mix(N, B, H):
     """Decode grids large enough for 12-wave workgroups, whose query tiles then come in several
-    heights: every output is bitwise the 4-wave decode's (run on 8-head slices, whose grids are
-    small), and two heads are checked against the oracle on sampled rows, including every tile's
-    first and last row."""
+    heights and, past the 384-row ones, from the 8-wave tail launch: every output is bitwise the
+    4-wave decode's (run on 8-head slices, whose grids are small), and two heads are checked
+    against the oracle on sampled rows, including every tile's first and last row."""
     P = 300
     ids = np.r_[np.full(40, -1), np.zeros(P - 40), np.ones(N)].astype(np.int32)
     plan = bca.Plan(ids)
