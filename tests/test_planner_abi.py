@@ -6,6 +6,8 @@ host-side check before anything touches a GPU.
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -32,6 +34,17 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_library_exports_only_the_c_abi():
+    """Internal C++ functions and kernel stubs stay local to libbca.so."""
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = [line.split()[-1] for line in out.splitlines() if line.strip()]
+    assert sorted(names) == sorted(declared_functions())
 
 
 def plan_host(ids):
