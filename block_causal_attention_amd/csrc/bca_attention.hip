@@ -58,8 +58,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // While a wave issues its score or PV MFMAs it runs at raised priority, so the SIMD's arbiter
 // prefers waves that can feed the matrix core and the others fill the gaps with softmax work.
-// Measured per kernel (interleaved A/B): +2% for the prefill; the decode with 12-wave workgroups
-// runs 4% faster without it.
+// Measured per kernel (interleaved A/B): +2% for the prefill; the decode's 12-wave kernel runs 4%
+// faster without it, and its 8-wave tail kernel 2%.
 constexpr int kMfmaPrio = 1;
 constexpr int kDecodeDirectMfmaPrio = 0;
 // Reads kept in flight ahead of the MFMAs (in steps of one MFMA) in the score and PV phases.
@@ -150,7 +150,9 @@ __device__ __forceinline__ void attn_fwd(const AttnArgs& a) {
   // The decode may read a quantised cache (its first key source); the prefill stores bf16 only.
   static_assert(kDecode || kFmt == kCacheBf16, "the prefill stores the cache's bf16 tensors");
   // wave priority while issuing MFMAs (0: never raised)
-  constexpr int kPrioLevel = kDecode && kW == kDecodeDirectWaves ? kDecodeDirectMfmaPrio : kMfmaPrio;
+  constexpr int kPrioLevel =
+      kDecode && (kW == kDecodeDirectWaves || kW == kDecodeTailWaves) ? kDecodeDirectMfmaPrio
+                                                                      : kMfmaPrio;
   constexpr bool kPrio = kPrioLevel > 0;
   constexpr bool kKqSrc = kDecode && kFmt == kCacheFp8KV;
   constexpr bool kVqSrc = kDecode && kFmt != kCacheBf16;
@@ -899,14 +901,6 @@ void attn_decode_direct(const AttnArgs a) {
   attn_fwd<true, kFmt, kDecodeDirectBlockN, kW>(a);
 }
 
-// Library-owned device scratch for the allocation-free split decode (bca_decode_split_noalloc):
-// the partial O, m and l of its key ranges.  One copy per GPU the library runs on, held until the
-// process ends; every call on a GPU shares it.  In host code the array's name is only a
-// stand-in: its device address comes from hipGetSymbolAddress, once per device.
-__device__ __align__(256) static unsigned char scratch[kScratchBytes];
-
-}  // namespace
-
 // Decode tail: the query tiles past the 12-wave launch's 384-row ones, as 256-row workgroups of 8
 // waves at 2 waves per SIMD (the register budget of two waves allows 64-key fills, half the
 // barriers) over a bf16 cache.  Each 64-key tile is computed as two 32-key halves, so every row
@@ -916,6 +910,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_decode_tail(const AttnArgs a) {
   attn_fwd<true, kCacheBf16, kDecodeTailBlockN, kDecodeTailWaves>(a);
 }
+
+// Library-owned device scratch for the allocation-free split decode (bca_decode_split_noalloc):
+// the partial O, m and l of its key ranges.  One copy per GPU the library runs on, held until the
+// process ends; every call on a GPU shares it.  In host code the array's name is only a
+// stand-in: its device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) static unsigned char scratch[kScratchBytes];
+
+}  // namespace
 
 // Compute units of the current device (cached per device).
 int device_cus() {
