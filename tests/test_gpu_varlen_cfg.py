@@ -190,3 +190,41 @@ def test_cfg_strided_views_and_single_plan():
     od2 = bca.decode(plan1, qb[None, P1:], kc1[None], vc1[None], kb[None, P1:], vb[None, P1:])
     torch.cuda.synchronize()
     assert np.array_equal(od1.cpu().numpy(), od2.cpu().numpy()[0])
+
+
+@pytest.mark.parametrize("seed,branches", [
+    # two sequences x 32 heads: 8 x 384 rows in the 12-wave launch, then 4 x 256 in the tail
+    # launch; the second sequence ends inside the first tail tile
+    (321, [(20, 100, 3, 4000), (7, 100, 3, 3300)]),
+    # three sequences: every row in the tail launch; the third ends inside its fourth tile
+    (322, [(20, 100, 3, 4000), (7, 100, 3, 3300), (5, 60, 0, 1000)]),
+])
+def test_batched_step_through_the_tail_launch(seed, branches):
+    """bca_decode_varlen whose longest target takes the two-launch layout: sequences with fewer
+    target rows leave tiles of either launch empty or part empty.  Caches bitwise, the batched
+    step bitwise equal to each sequence's own decode, sampled rows against the oracle."""
+    H = 32
+    ids_list = [branch_layout(*b) for b in branches]
+    lens = [len(i) for i in ids_list]
+    starts = O.packed_row_starts(lens)
+    off = O.varlen_offsets(ids_list)
+    n_max = int(off["N"].max())
+    layout = bca.decode_layout(n_max, len(ids_list) * H)
+    assert layout[4] > 0, layout
+    say(f"test_batched_step_through_the_tail_launch seed={seed} N_b={off['N'].tolist()} "
+        f"layout={layout}")
+    r = run_branches(ids_list, starts, H, seed)
+    check_caches(r, ids_list)
+    check_per_branch_decode(r, ids_list, H)
+    heads = [0, 31]
+    kc_w, vc_w = O.prefix_cache_varlen(f32(r["k"]), f32(r["v"]), ids_list, starts)
+    drows = {}
+    for b in range(len(ids_list)):
+        n = int(off["N"][b])
+        edges = [x for x in (3071, 3072, 3327, 3328, n - 1) if x < n]
+        drows[b] = np.unique(np.r_[np.arange(0, n, 89), edges])
+    dwant = O.decode_varlen(f32(r["qt"]), kc_w, vc_w, f32(r["kt"]), f32(r["vt"]), ids_list,
+                            rows_of=drows, heads=heads)
+    for b in range(len(ids_list)):
+        got = r["od"][int(off["t"][b]) + drows[b]][:, heads]
+        check(got, dwant[b], f"cached step branch {b} (sampled rows)")
