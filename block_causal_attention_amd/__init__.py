@@ -27,7 +27,7 @@ from ._lib import BcaKvCache, BcaPlanInfo, BcaTensor
 __all__ = ["Plan", "prefill", "decode", "prefill_ex", "decode_ex", "KVCache", "BcaError",
            "plan_info", "rope_positions", "rope_table", "qk_prologue", "prefill_varlen",
            "decode_split", "split_workspace", "dequantize_cache", "decode_split_noalloc",
-           "decode_varlen", "decode_layout"]
+           "decode_varlen", "decode_layout", "prefill_layout"]
 
 
 class BcaError(RuntimeError):
@@ -503,6 +503,15 @@ def decode_layout(n_q: int, batch_heads: int, n_split: int = 1, cache_fmt: int =
     FP8_KV), on `cus` compute units (0: the current device's) (bca_decode_layout)."""
     out = (ctypes.c_int32 * 5)()
     _check(_lib.load().bca_decode_layout(n_q, batch_heads, n_split, cache_fmt, cus, out))
+    return tuple(out)
+
+
+def prefill_layout(plan: Plan, batch: int, heads: int, cus: int = 0):
+    """(attention launches, query tiles per (batch, head) of the prefill launch, target rows
+    handed to the second launch) of a single-sequence prefill on `cus` compute units (0: the
+    current device's) (bca_prefill_layout)."""
+    out = (ctypes.c_int32 * 3)()
+    _check(_lib.load().bca_prefill_layout(plan.handle, batch, heads, cus, out))
     return tuple(out)
 
 

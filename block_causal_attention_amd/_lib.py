@@ -25,7 +25,7 @@ EXPORTED = ("bca_plan", "bca_plan_free", "bca_plan_get_info", "bca_plan_export",
             "bca_qk_prologue", "bca_plan_varlen", "bca_prefill_varlen",
             "bca_decode_split_workspace", "bca_decode_split", "bca_cache_dequantize",
             "bca_decode_split_noalloc", "bca_plan_sequences", "bca_decode_varlen",
-            "bca_decode_layout", "bca_status_str", "bca_last_error")
+            "bca_decode_layout", "bca_prefill_layout", "bca_status_str", "bca_last_error")
 BCA_SCRATCH_BYTES = 64 << 20
 
 
@@ -101,6 +101,7 @@ def load() -> ctypes.CDLL:
                                              ctypes.c_float, T, C, T, T, T, ctypes.c_int32, P]
     lib.bca_decode_layout.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, i32p]
+    lib.bca_prefill_layout.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p]
     lib.bca_status_str.argtypes = [ctypes.c_int]
     lib.bca_status_str.restype = ctypes.c_char_p
     lib.bca_last_error.argtypes = []
@@ -110,7 +111,7 @@ def load() -> ctypes.CDLL:
                  "bca_rope_positions", "bca_rope_table", "bca_qk_prologue", "bca_plan_varlen",
                  "bca_prefill_varlen", "bca_decode_split_workspace", "bca_decode_split",
                  "bca_cache_dequantize", "bca_decode_split_noalloc", "bca_plan_sequences",
-                 "bca_decode_varlen", "bca_decode_layout"):
+                 "bca_decode_varlen", "bca_decode_layout", "bca_prefill_layout"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

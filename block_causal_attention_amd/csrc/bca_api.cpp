@@ -24,6 +24,8 @@ struct bca_plan_s {
   int32_t* d_order = nullptr;
   int32_t* d_tiles = nullptr;
   int32_t* d_seqs = nullptr;
+  int32_t* d_prefix_tiles = nullptr;
+  int32_t* d_prefix_order = nullptr;
 };
 
 namespace {
@@ -45,17 +47,20 @@ void free_device(bca_plan_s* p) {
   if (p->d_arena) (void)hipFree(p->d_arena);
   p->d_arena = nullptr;
   p->d_row_limit = p->d_kv_full = p->d_kv_end = p->d_order = p->d_tiles = p->d_seqs = nullptr;
+  p->d_prefix_tiles = p->d_prefix_order = nullptr;
 }
 
 // The plan's device arrays: packed into one host staging buffer (each array starting on a
 // 256-byte boundary), then one hipMalloc and one synchronous hipMemcpy.
 bca_status upload(bca_plan_s* p) {
   const bca::HostPlan& h = p->host;
-  constexpr int kArrays = 6;
+  constexpr int kArrays = 8;
   const std::vector<int32_t>* src[kArrays] = {&h.row_limit, &h.kv_full, &h.kv_end,
-                                              &h.order,     &h.tiles,   &h.seqs};
+                                              &h.order,     &h.tiles,   &h.seqs,
+                                              &h.prefix_tiles, &h.prefix_order};
   int32_t** dst[kArrays] = {&p->d_row_limit, &p->d_kv_full, &p->d_kv_end,
-                            &p->d_order,     &p->d_tiles,   &p->d_seqs};
+                            &p->d_order,     &p->d_tiles,   &p->d_seqs,
+                            &p->d_prefix_tiles, &p->d_prefix_order};
   constexpr size_t kAlignInts = 64;
   size_t off[kArrays], total = 0;
   for (int i = 0; i < kArrays; ++i) {
@@ -197,6 +202,20 @@ bool grid_fits(int64_t groups, int64_t threads) {
 bool grid_fits(int64_t tiles, int32_t B, int32_t H) {
   return tiles <= (int64_t)INT32_MAX / ((int64_t)B * H) &&
          grid_fits(tiles * B * H, 64 * bca::kPrefillWaves);
+}
+
+// Whether a single-sequence prefill hands its target rows (the last block, an image block:
+// rows [P, S)) to the decode kernels.  That happens when its own grid of B * H * query tiles
+// would fill less than two rounds of the CUs while the target rows alone take the decode's
+// 12-wave launch, whose query tiles of mixed heights fill whole rounds; the prefix rows then run
+// first in a prefill launch of their own.  A row's arithmetic is the same either way (the same
+// 32-key tiles in the same order).
+bool prefill_hands_off(const bca::HostPlan& hp, int32_t B, int32_t H, int cus) {
+  if (hp.n_sequences != 1 || hp.prefix_tiles.empty()) return false;
+  const int64_t groups = (int64_t)B * H;
+  if ((int64_t)hp.kv_end.size() * groups >= 2 * (int64_t)cus) return false;
+  return bca::decode_layout(hp.target_len, groups, 1, cus, bca::kCacheBf16).waves ==
+         bca::kDecodeDirectWaves;
 }
 
 }  // namespace
@@ -394,8 +413,42 @@ bca_status bca_prefill_ex(bca_plan_t plan, int32_t B, int32_t H, int32_t D, floa
       a.vc_sb = cache->v.stride_b; a.vc_ss = cache->v.stride_s; a.vc_sh = cache->v.stride_h;
     }
   }
+  const bool hand_off = prefill_hands_off(hp, B, H, bca::device_cus());
+  if (hand_off) {  // the prefix rows in tiles of their own (they store the cache)
+    a.n_q = a.kv_len = a.split = (int32_t)hp.prefix_len;
+    a.n_qtiles = (int32_t)hp.prefix_order.size();
+    a.order = plan->d_prefix_order;
+    a.tiles = plan->d_prefix_tiles;
+  }
   hipError_t e = bca::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  if (hand_off) {
+    // then the target rows as a cached step whose prefix keys are rows [0, P) of k and v
+    const int64_t P = hp.prefix_len;
+    bca::AttnArgs d{};
+    d.q = static_cast<const uint16_t*>(q->data) + P * q->stride_s;
+    d.q_sb = q->stride_b; d.q_ss = q->stride_s; d.q_sh = q->stride_h;
+    d.k = k->data;
+    d.k_sb = k->stride_b; d.k_ss = k->stride_s; d.k_sh = k->stride_h;
+    d.v = v->data;
+    d.v_sb = v->stride_b; d.v_ss = v->stride_s; d.v_sh = v->stride_h;
+    d.k2 = static_cast<const uint16_t*>(k->data) + P * k->stride_s;
+    d.k2_sb = k->stride_b; d.k2_ss = k->stride_s; d.k2_sh = k->stride_h;
+    d.v2 = static_cast<const uint16_t*>(v->data) + P * v->stride_s;
+    d.v2_sb = v->stride_b; d.v2_ss = v->stride_s; d.v2_sh = v->stride_h;
+    d.o = static_cast<float*>(o->data) + P * o->stride_s;
+    d.o_sb = o->stride_b; d.o_ss = o->stride_s; d.o_sh = o->stride_h;
+    d.n_q = (int32_t)hp.target_len;
+    d.kv_len = (int32_t)hp.seq_len;
+    d.split = (int32_t)P;
+    d.heads = H;
+    d.batch = B;
+    d.scale_log2 = scale_log2;
+    d.cache_fmt = BCA_CACHE_BF16;
+    d.n_split = 1;
+    e = bca::launch_decode(d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill launch (target rows)");
+  }
   if (kq || vq) {
     bca::QuantArgs qa{};
     qa.k = static_cast<const uint16_t*>(k->data);
@@ -432,6 +485,18 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
   if (k_cache == nullptr) return bca_prefill_ex(plan, B, H, D, scale, q, k, v, o, nullptr, stream);
   const bca_kv_cache c = bf16_cache(k_cache, v_cache);
   return bca_prefill_ex(plan, B, H, D, scale, q, k, v, o, &c, stream);
+}
+
+bca_status bca_prefill_layout(bca_plan_t plan, int32_t B, int32_t H, int32_t cus, int32_t* out) {
+  if (plan == nullptr || out == nullptr) return fail(BCA_ERR_ARG, "plan or out is NULL");
+  if (B < 1 || H < 1) return fail(BCA_ERR_ARG, "B and H must be >= 1");
+  if (cus < 0) return fail(BCA_ERR_ARG, "cus must be >= 0 (0 = the current device's)");
+  const bca::HostPlan& hp = plan->host;
+  const bool hand_off = prefill_hands_off(hp, B, H, cus > 0 ? cus : bca::device_cus());
+  out[0] = hand_off ? 2 : 1;
+  out[1] = (int32_t)(hand_off ? hp.prefix_order.size() : hp.kv_end.size());
+  out[2] = hand_off ? (int32_t)hp.target_len : 0;
+  return BCA_OK;
 }
 
 bca_status bca_prefill_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,

@@ -94,6 +94,28 @@ int build_host_plan(const int32_t* ids, int64_t S, int block_m, HostPlan* out, s
   p.rows = S;
   for (int64_t t = 0; t < nt; ++t) p.tiles[(size_t)t * kTileInts + 6] = (int32_t)p.prefix_len;
   p.seqs = {0, (int32_t)S, (int32_t)p.prefix_len, (int32_t)p.target_len, 0, 0, p.decode_ok, 0};
+  // The prefix rows [0, P) tiled on their own: rows of the prefix see only prefix keys (P is a
+  // block boundary), so their limits are the sequence's.
+  const int64_t P = p.prefix_len;
+  if (p.decode_ok && P > 0) {
+    const int64_t ntp = (P + block_m - 1) / block_m;
+    p.prefix_tiles.assign((size_t)ntp * kTileInts, 0);
+    std::vector<int32_t> end((size_t)ntp);
+    for (int64_t t = 0; t < ntp; ++t) {
+      const int64_t first = P - (ntp - t) * block_m;
+      const int64_t last = first + block_m - 1;
+      int32_t* d = &p.prefix_tiles[(size_t)t * kTileInts];
+      d[1] = (int32_t)first;
+      d[2] = (int32_t)P;
+      d[4] = p.row_limit[(size_t)std::max<int64_t>(first, 0)];
+      d[5] = end[(size_t)t] = p.row_limit[(size_t)last];
+      d[6] = (int32_t)P;
+    }
+    p.prefix_order.resize((size_t)ntp);
+    std::iota(p.prefix_order.begin(), p.prefix_order.end(), 0);
+    std::stable_sort(p.prefix_order.begin(), p.prefix_order.end(),
+                     [&](int32_t x, int32_t y) { return end[(size_t)x] > end[(size_t)y]; });
+  }
   *out = std::move(p);
   return kPlanOk;
 }

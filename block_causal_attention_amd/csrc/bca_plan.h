@@ -30,6 +30,11 @@ struct HostPlan {
   // (start of its last block), target length N_b, first cache row (sum of the earlier P),
   // first target row (sum of the earlier N), 1 when its last block is an image block, 0.
   std::vector<int32_t> seqs;
+  // Single sequence whose last block is an image block after a non-empty prefix: query tiles of
+  // the prefix rows alone (ending at row P, tile layout and order as above, n_rows = P and the
+  // whole prefix stored to the cache), for a prefill that hands the target rows to the decode.
+  std::vector<int32_t> prefix_tiles;
+  std::vector<int32_t> prefix_order;
   int32_t n_sequences = 1;
   int64_t rows = 0;                // tensor rows spanned: max(row_start + length)
 };

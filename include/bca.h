@@ -166,11 +166,29 @@ bca_status bca_plan_export(bca_plan_t plan, int32_t* segments, int32_t* row_limi
  * they receive copies of k[:, :P] and v[:, :P] (the guide clones the prefix slices rather than
  * keeping views).  The cache holds K as handed in (post-RoPE when the caller applied RoPE).
  * Output buffers must not overlap the inputs.  D must be 128 (else BCA_ERR_UNSUPPORTED).
+ * The call is one attention launch, or two (bca_prefill_layout): the prefix rows, then the
+ * target rows by the cached step's kernels over rows [0, P) of k and v as their prefix keys.
+ * Every output row is bitwise the same either way.
  */
 bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float scale,
                        const bca_tensor* q, const bca_tensor* k, const bca_tensor* v,
                        const bca_tensor* o, const bca_tensor* k_cache, const bca_tensor* v_cache,
                        void* stream);
+
+/*
+ * bca_prefill_layout -- HOST.  How bca_prefill and bca_prefill_ex launch a single-sequence plan
+ * for B batch items and H heads on a GPU of `cus` compute units (0 = the current device's, 256
+ * where the runtime cannot tell).  out[0] = attention launches (1 or 2); out[1] = query tiles per
+ * (batch, head) of the prefill launch; out[2] = target rows handed to the second launch (0 with
+ * one launch).  Two launches when the plan's last block is an image block after a non-empty
+ * prefix, B * H * (the plan's query tiles) < 2 * cus (one launch would fill under two rounds of
+ * the CUs), and the target rows alone take the cached step's 12-wave launch (bca_decode_layout
+ * out[0] = 12 for n_q = N, batch_heads = B * H, a bf16 cache): the first launch then covers the
+ * prefix rows [0, P) in query tiles of their own (out[1] of them, ending at row P) and stores
+ * the cache, the second the target rows over all S keys.  Plans with several sequences take one
+ * launch.  BCA_ERR_ARG for a NULL plan or out, B or H < 1, or cus < 0.
+ */
+bca_status bca_prefill_layout(bca_plan_t plan, int32_t B, int32_t H, int32_t cus, int32_t* out);
 
 /*
  * bca_prefill_varlen -- block-causal attention of every sequence of a bca_plan_varlen plan (or of
