@@ -1094,6 +1094,25 @@ DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus, in
       }
       return l;
     }
+    // Under one round of 384-row tiles, over a bf16 cache: every row in 256-row tiles of the
+    // 8-wave kernel when those fill more than half of the CUs in one round, one round of 12-wave
+    // workgroups when the 256-row tiles would need a second; else the 4-wave launch below (it
+    // measured ahead once half the CUs or fewer would be busy).
+    if (cache_fmt == kCacheBf16) {
+      const int64_t n_tail = (n_q + 255) / 256;
+      if (n_tail * groups > (int64_t)cus) {
+        l.waves = kDecodeDirectWaves;
+        l.tiles[0] = (int32_t)t12;
+        l.mixed = true;
+        return l;
+      }
+      if (2 * n_tail * groups > (int64_t)cus) {
+        l.waves = kDecodeDirectWaves;
+        l.mixed = true;
+        l.tail = (int32_t)n_tail;
+        return l;
+      }
+    }
   } else if (t12 * groups * std::max(n_split, 1) >= 2 * (int64_t)cus) {
     // 384-row tiles only: 12-wave workgroups where they give every CU at least two
     l.waves = kDecodeDirectWaves;

@@ -249,10 +249,11 @@ bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
  * bca_decode_ex, bca_decode_split) takes for n_q query rows per (batch, head) (for
  * bca_decode_varlen, the largest N_b), batch_heads = B * H, n_split key ranges (1 = unsplit) and
  * a cache of format cache_fmt, on a GPU of `cus` compute units (0 = the current device's, 256
- * where the runtime cannot tell).  out[0] = waves per workgroup of the first launch; out[1..3] =
- * its query tiles per (batch, head, key range) of 384, 256 and 128 rows, laid along the rows in
- * that order; out[4] = query tiles of 256 rows that a second launch of 8-wave workgroups takes
- * from row 384 * out[1] on (0 = one launch).  The tiles cover every row, and every tile holds one.
+ * where the runtime cannot tell).  out[0] = waves per workgroup (12 or 4) of the launch over the
+ * query tiles out[1..3] per (batch, head, key range) of 384, 256 and 128 rows, laid along the rows
+ * in that order (no such launch when all three are 0); out[4] = query tiles of 256 rows that a
+ * launch of 8-wave workgroups takes from row 384 * out[1] on, after the first (0 = none).  The
+ * tiles cover every row, and every tile holds one.
  *   Unsplit, with batch_heads and cus multiples of 8 (one share per XCD): 12-wave workgroups once
  *   384-row tiles would fill one round of the CUs (ceil(n_q / 384) * batch_heads >= cus).  Each
  *   XCD runs its (batch, head) entries' 384-row tiles, then their 256-row ones, then their 128-row
@@ -266,8 +267,13 @@ bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
  *   8-wave workgroups (2 waves per SIMD, 64-key fills), priced in whole rounds of the XCD's CUs
  *   at 1.01 and 0.737 per tile plus 0.02 for the second launch; the best n3 is taken when it
  *   replays at least 3% shorter than the mix.
+ *   Unsplit and mixable under that round, with a bf16 cache: one round of 12-wave workgroups in
+ *   384-row tiles (out[1] = ceil(n_q / 384)) when 256-row tiles would need a second round
+ *   (ceil(n_q / 256) * batch_heads > cus); else every row in the 8-wave launch (out[1..3] = 0,
+ *   out[4] = ceil(n_q / 256)) when its tiles fill more than half of the CUs
+ *   (2 * ceil(n_q / 256) * batch_heads > cus).
  *   Otherwise: 12-wave workgroups in 384-row tiles where those give every CU at least two
- *   (ceil(n_q / 384) * batch_heads * n_split >= 2 * cus).
+ *   (not mixable, ceil(n_q / 384) * batch_heads * n_split >= 2 * cus).
  *   4-wave workgroups in 128-row tiles in the remaining cases.
  * A row's result does not depend on the tile or launch that holds it.  BCA_ERR_ARG for n_q or
  * batch_heads outside [1, 2^31 - 1], n_split < 1, batch_heads * n_split >= 2^31, an unknown

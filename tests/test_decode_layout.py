@@ -82,9 +82,19 @@ SHAPES = [(n, g, s, c) for n in (1, 100, 384, 385, 777, 1024, 2048, 3072, 3356, 
 @pytest.mark.parametrize("n,bh,n_split,cus", SHAPES)
 def test_layout_covers_rows_and_follows_the_rules(n, bh, n_split, cus, fmt):
     waves, t3, t2, t1, tail = bca.decode_layout(n, bh, n_split, fmt, cus)
-    t12 = cdiv(n, 384)
+    t12, n256 = cdiv(n, 384), cdiv(n, 256)
     mixable = n_split == 1 and bh % 8 == 0 and cus % 8 == 0
     wide = t12 * bh >= cus if mixable else t12 * bh * n_split >= 2 * cus
+    if mixable and not wide and fmt == 0:
+        # under one round of 384-row tiles over a bf16 cache: one round of 12-wave workgroups
+        # when 256-row tiles would need a second, all rows in the 8-wave launch when its tiles
+        # fill more than half of the CUs, else 4-wave workgroups
+        if n256 * bh > cus:
+            assert (waves, t3, t2, t1, tail) == (12, t12, 0, 0, 0)
+            return
+        if 2 * n256 * bh > cus:
+            assert (waves, t3, t2, t1, tail) == (12, 0, 0, 0, n256)
+            return
     assert waves == (12 if wide else 4)
     if waves == 4:
         assert (t3, t2, t1, tail) == (0, 0, cdiv(n, 128), 0)
@@ -109,9 +119,14 @@ def test_headline_shapes():
     assert bca.decode_layout(4096, 64, 1, 0, 256) == (12, 8, 0, 0, 4)
     assert bca.decode_layout(4096, 64, 1, 1, 256) == (12, 8, 4, 0, 0)
     assert bca.decode_layout(16384, 64, 1, 0, 256) == (12, 40, 4, 0, 0)
-    # under one round of 384-row tiles the 4-wave kernel stays (512^2 target, unsplit and split)
-    assert bca.decode_layout(2048, 32, 1, 0, 256) == (4, 0, 0, 16, 0)
+    # under one round of 384-row tiles: the 512^2 target (unsplit and split) keeps 4-wave
+    # workgroups; over a bf16 cache N = 2,048 at B = 1 runs all its rows in the 8-wave launch,
+    # N = 2,304 one round of 12-wave workgroups; an FP8 cache keeps the 4-wave launch
+    assert bca.decode_layout(1024, 32, 1, 0, 256) == (4, 0, 0, 8, 0)
     assert bca.decode_layout(1024, 32, 3, 0, 256) == (4, 0, 0, 8, 0)
+    assert bca.decode_layout(2048, 32, 1, 0, 256) == (12, 0, 0, 0, 8)
+    assert bca.decode_layout(2304, 32, 1, 0, 256) == (12, 6, 0, 0, 0)
+    assert bca.decode_layout(2048, 32, 1, 1, 256) == (4, 0, 0, 16, 0)
 
 
 @pytest.mark.parametrize("args", [(0, 64, 1, 0, 256), (4096, 0, 1, 0, 256), (4096, 64, 0, 0, 256),

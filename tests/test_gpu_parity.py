@@ -339,6 +339,9 @@ MIX_CASES = [
     (4096, 1, 32),   # 2 x 384 + 12 x 256 + 2 x 128 in one launch (no CFG: 4 entries per XCD)
     (3072, 1, 32),   # 8 x 384 in one launch: one round
     (16384, 2, 32),  # 40 x 384 + 4 x 256 in one launch
+    (2048, 1, 32),   # under one round: every row in the tail launch, 8 x 256
+    (2304, 1, 32),   # under one round: 6 x 384 in the 12-wave kernel
+    (1000, 2, 32),   # tail only, 4 x 256 (the last one 232 rows)
 ]
 
 
