@@ -206,14 +206,15 @@ bool grid_fits(int64_t tiles, int32_t B, int32_t H) {
 
 // Whether a single-sequence prefill hands its target rows (the last block, an image block:
 // rows [P, S)) to the decode kernels.  That happens when its own grid of B * H * query tiles
-// would fill less than two rounds of the CUs while the target rows alone take the decode's
-// 12-wave launch, whose query tiles of mixed heights fill whole rounds; the prefix rows then run
-// first in a prefill launch of their own.  A row's arithmetic is the same either way (the same
-// 32-key tiles in the same order).
+// would fill less than two rounds of the CUs while the target rows alone fill at least one round
+// of 384-row tiles and so take the decode's 12-wave launch, whose query tiles of mixed heights
+// fill whole rounds; the prefix rows then run first in a prefill launch of their own.  A row's
+// arithmetic is the same either way (the same 32-key tiles in the same order).
 bool prefill_hands_off(const bca::HostPlan& hp, int32_t B, int32_t H, int cus) {
   if (hp.n_sequences != 1 || hp.prefix_tiles.empty()) return false;
   const int64_t groups = (int64_t)B * H;
   if ((int64_t)hp.kv_end.size() * groups >= 2 * (int64_t)cus) return false;
+  if ((hp.target_len + 383) / 384 * groups < (int64_t)cus) return false;
   return bca::decode_layout(hp.target_len, groups, 1, cus, bca::kCacheBf16).waves ==
          bca::kDecodeDirectWaves;
 }

@@ -182,7 +182,8 @@ bca_status bca_prefill(bca_plan_t plan, int32_t B, int32_t H, int32_t D, float s
  * (batch, head) of the prefill launch; out[2] = target rows handed to the second launch (0 with
  * one launch).  Two launches when the plan's last block is an image block after a non-empty
  * prefix, B * H * (the plan's query tiles) < 2 * cus (one launch would fill under two rounds of
- * the CUs), and the target rows alone take the cached step's 12-wave launch (bca_decode_layout
+ * the CUs), and the target rows alone fill at least one round of 384-row tiles
+ * (ceil(N / 384) * B * H >= cus) in the cached step's 12-wave launch (bca_decode_layout
  * out[0] = 12 for n_q = N, batch_heads = B * H, a bf16 cache): the first launch then covers the
  * prefix rows [0, P) in query tiles of their own (out[1] of them, ending at row P) and stores
  * the cache, the second the target rows over all S keys.  Plans with several sequences take one

@@ -18,7 +18,7 @@ def expected(plan, B, H, cus):
     info = plan.info
     P, N, nt = info.prefix_len, info.target_len, info.n_qtiles
     two = (info.n_sequences == 1 and info.decode_ok and P > 0 and nt * B * H < 2 * cus
-           and bca.decode_layout(N, B * H, 1, 0, cus)[0] == 12)
+           and cdiv(N, 384) * B * H >= cus and bca.decode_layout(N, B * H, 1, 0, cus)[0] == 12)
     return (2, cdiv(P, info.block_m), N) if two else (1, nt, 0)
 
 
@@ -27,6 +27,14 @@ def test_text_to_image_hands_off_at_one_batch_item():
     assert bca.prefill_layout(plan, 1, 32, 256) == (2, 1, 4096)
     # twice the grid fills two rounds: one launch
     assert bca.prefill_layout(plan, 2, 32, 256) == (1, 12, 0)
+
+
+def test_target_under_one_round_keeps_one_launch():
+    # 2,304 target rows: one 12-wave round of its own, no better than the one-launch prefill
+    ids = W.block_ids_from_segments([("text", 256), ("image", 2304)])
+    plan = bca.Plan(ids, host_only=True)
+    assert bca.decode_layout(2304, 32, 1, 0, 256)[0] == 12
+    assert bca.prefill_layout(plan, 1, 32, 256) == (1, plan.info.n_qtiles, 0)
 
 
 def test_headline_layouts_take_one_launch():
