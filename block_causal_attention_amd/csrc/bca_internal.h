@@ -189,12 +189,16 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
 // ranges, on a device of `cus` compute units.  tiles: query tiles per (batch, head, key range) of
 // 384, 256 and 128 rows, laid along the rows in that order.
 //   Unsplit, groups and cus multiples of the 8 XCDs: 12-wave workgroups with the mix decode_mix
-//   picks (mixed = true) once 384-row tiles would fill one round of the CUs, else 4-wave ones.
+//   picks (mixed = true) once 384-row tiles would fill one round of the CUs; under that round,
+//   with a bf16 cache, one round of 384-row tiles {ceil(n_q / 384), 0, 0} (mixed = true) when
+//   256-row tiles would need a second round, else every row in the tail kernel (tiles all 0,
+//   tail = ceil(n_q / 256)) when its tiles fill more than half of the CUs; else 4-wave ones.
 //   Otherwise: 12-wave workgroups in 384-row tiles {ceil(n_q / 384), 0, 0} where those give every
 //   CU at least two, else 4-wave ones.  4 waves: {0, 0, ceil(n_q / 128)}.
 //   With a bf16 cache, an unsplit mixed launch may instead be two launches (tail > 0): tiles[0]
 //   384-row tiles in the 12-wave kernel (mixed = true, tiles[1] = tiles[2] = 0), then `tail`
-//   256-row tiles of the 8-wave tail kernel from row 384 * tiles[0] on.
+//   256-row tiles of the 8-wave tail kernel from row 384 * tiles[0] on.  tail > 0 only for
+//   unsplit launches (launch_decode merges key ranges after the one-kernel launches only).
 struct DecodeLayout {
   int waves;
   int32_t tiles[3];
