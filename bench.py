@@ -510,7 +510,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path "
-              "is built and measured on a single MI355X; see the sharding notes in DESIGN.md)",
+              "is built and measured on a single MI355X; sharding across GPUs is not built)",
               file=sys.stderr)
         sys.exit(2)
 
