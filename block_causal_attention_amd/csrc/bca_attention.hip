@@ -1080,9 +1080,9 @@ DecodeLayout decode_layout(int64_t n_q, int64_t groups, int n_split, int cus, in
       decode_mix((int)n_q, (int)(groups / 8), cus / 8, l.tiles, &span);
       l.mixed = true;
       // a bf16 cache may instead finish with the 8-wave tail launch, taken when the replay
-      // predicts it at least 3% shorter and each XCD holds at least 8 (batch, head) entries
-      // (with 4, at B = 1 and 32 heads, two launches measured no faster for N = 4,096 to 8,192)
-      if (cache_fmt == kCacheBf16 && groups / 8 >= 8) {
+      // predicts it at least 3% shorter and each XCD holds at least 4 (batch, head) entries
+      // (measured from 4 to 16; the replay overstates the gain, which is 0-9%)
+      if (cache_fmt == kCacheBf16 && groups / 8 >= 4) {
         int n3 = -1;
         double two = 0.0;
         decode_two_launch((int)n_q, (int)(groups / 8), cus / 8, &n3, &two);

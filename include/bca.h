@@ -263,7 +263,7 @@ bca_status bca_decode_varlen(bca_plan_t plan, int32_t H, int32_t D, float scale,
  *   a tile at its busiest SIMD's step time, 1, 0.88 and 0.66 for 3, 2 and 1 waves with rows (the
  *   384-, 256- and 128-row tiles' ratios measured on an MI355X), plus 0.01; a tie keeps the
  *   candidate with fewer 256-row, then fewer 128-row tiles.
- *   With a bf16 cache and batch_heads >= 64 (8 entries per XCD) the step may instead take two
+ *   With a bf16 cache and batch_heads >= 32 (4 entries per XCD) the step may instead take two
  *   launches: n3 tiles of 384 rows in the 12-wave kernel, then the rest in 256-row tiles of
  *   8-wave workgroups (2 waves per SIMD, 64-key fills), priced in whole rounds of the XCD's CUs
  *   at 1.01 and 0.737 per tile plus 0.02 for the second launch; the best n3 is taken when it

@@ -104,7 +104,7 @@ def test_layout_covers_rows_and_follows_the_rules(n, bh, n_split, cus, fmt):
         return
     span, mix = replay(n, bh // 8, cus // 8)
     two = two_launch(n, bh // 8, cus // 8)
-    if fmt == 0 and bh // 8 >= 8 and two is not None and two[0] < 0.97 * span:
+    if fmt == 0 and bh // 8 >= 4 and two is not None and two[0] < 0.97 * span:
         assert (t3, t2, t1, tail) == (two[1], 0, 0, two[2])
         assert 384 * t3 < n <= 384 * t3 + 256 * tail and 384 * t3 + 256 * (tail - 1) < n
     else:

@@ -303,9 +303,8 @@ def test_decode_workgroup_widths_agree_bitwise():
     """A row's arithmetic and key order depend neither on the workgroup width nor on the height
     of the query tile or the launch that holds it.  At N = 4,096, H = 32 the B = 2 decode runs
     8 x 384-row tiles in 12-wave workgroups and the last 1,024 rows in the 8-wave tail launch,
-    the B = 1 decode runs one launch of 384-, 256- and 128-row tiles in 12-wave workgroups, and
-    an 8-head view of B = 1 runs 4-wave workgroups in 128-row tiles: batch item 0 of the first
-    equals the other two bit for bit
+    the B = 1 decode runs every row in the tail launch, and an 8-head view of B = 1 runs 4-wave
+    workgroups in 128-row tiles: batch item 0 of the first equals the other two bit for bit
     (sampled against the oracle too, through the CFG test)."""
     lay = W.EDIT_2REF
     ids = lay.block_ids()
@@ -323,7 +322,7 @@ def test_decode_workgroup_widths_agree_bitwise():
                        v[:1, :, :8])
     torch.cuda.synchronize()
     assert bca.decode_layout(N, 2 * H) == (12, 8, 0, 0, 4)
-    assert bca.decode_layout(N, H) == (12, 2, 12, 2, 0) and bca.decode_layout(N, 8)[0] == 4
+    assert bca.decode_layout(N, H) == (12, 0, 0, 0, 16) and bca.decode_layout(N, 8)[0] == 4
     assert torch.equal(both[:1], one)
     assert torch.equal(one[:, :, :8], eight)
 
@@ -336,7 +335,8 @@ MIX_CASES = [
     (3356, 2, 32),   # 4 x 384, tail 8 x 256
     (777, 4, 64),    # 1 x 384, tail 2 x 256
     (2048, 2, 32),   # tail only, 8 x 256
-    (4096, 1, 32),   # 2 x 384 + 12 x 256 + 2 x 128 in one launch (no CFG: 4 entries per XCD)
+    (4096, 1, 32),   # tail only, 16 x 256 (no CFG: 4 entries per XCD)
+    (8192, 1, 16),   # 16 x 384 + 7 x 256 + 2 x 128 in one launch (2 entries per XCD)
     (3072, 1, 32),   # 8 x 384 in one launch: one round
     (16384, 2, 32),  # 40 x 384 + 4 x 256 in one launch
     (2048, 1, 32),   # under one round: every row in the tail launch, 8 x 256
@@ -349,7 +349,7 @@ MIX_CASES = [
 def test_decode_tile_mix(N, B, H):
     """Decode grids large enough for 12-wave workgroups, whose query tiles then come in several
     heights and, past the 384-row ones, from the 8-wave tail launch: every output is bitwise the
-    4-wave decode's (run on 8-head slices, whose grids are small), and two heads are checked
+    4-wave decode's (run on 2-head slices, whose grids are small), and two heads are checked
     against the oracle on sampled rows, including every tile's first and last row."""
     P = 300
     ids = np.r_[np.full(40, -1), np.zeros(P - 40), np.ones(N)].astype(np.int32)
@@ -362,11 +362,13 @@ def test_decode_tile_mix(N, B, H):
     kc, vc, q, k, v = (to_dev(x) for x in (kcb, vcb, qt, kt, vt))
     o = bca.decode(plan, q, kc, vc, k, v)
     torch.cuda.synchronize()
-    for h0 in range(0, H, 8):
-        sl = slice(h0, h0 + 8)
-        o8 = bca.decode(plan, q[:, :, sl], kc[:, :, sl], vc[:, :, sl], k[:, :, sl], v[:, :, sl])
+    # two heads at a time: grids small enough for the 4-wave decode
+    assert bca.decode_layout(N, B * 2)[0] == 4
+    for h0 in range(0, H, 2):
+        sl = slice(h0, h0 + 2)
+        o2 = bca.decode(plan, q[:, :, sl], kc[:, :, sl], vc[:, :, sl], k[:, :, sl], v[:, :, sl])
         torch.cuda.synchronize()
-        assert torch.equal(o8, o[:, :, sl]), f"heads {h0}..{h0 + 7}"
+        assert torch.equal(o2, o[:, :, sl]), f"heads {h0}, {h0 + 1}"
     edges = [r for t in range(0, N, 128) for r in (t, t + 127)]
     rows = np.unique(np.clip(np.r_[np.arange(0, N, 7), edges, N - 1], 0, N - 1))
     heads = [0, H - 1]
